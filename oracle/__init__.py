@@ -1,0 +1,133 @@
+"""fp64 CPU oracle for exact attention.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg are the only users.  The product path never imports it.
+
+``attention_oracle.cpp`` holds the definition (standard attention written
+out in double precision, see its header for the readings taken); this module
+builds it with g++ and calls it through ctypes on float64 numpy arrays.
+Entries the caller did not select are returned as NaN.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attention_oracle.cpp")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle (g++, no fast-math: IEEE double throughout)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["g++", "-std=c++17", "-O2", "-fPIC", "-shared",
+                               "-pthread", "-o", tmp, _SRC])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        lib.oracle_attention_fwd.argtypes = [P] * 7 + [I] * 9 + \
+            [ctypes.c_double, P, I, P, I, I]
+        lib.oracle_attention_fwd.restype = I
+        lib.oracle_attention_bwd.argtypes = [P] * 11 + [I] * 9 + \
+            [ctypes.c_double, P, I, P, I, P, I, I]
+        lib.oracle_attention_bwd.restype = I
+        _lib = lib
+    return _lib
+
+
+def _f64(x):
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor -> exact float64
+        x = x.detach().cpu().double().numpy()
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _i32(x):
+    if x is None:
+        return None
+    if hasattr(x, "detach"):
+        x = x.detach().cpu().numpy()
+    return np.ascontiguousarray(x, dtype=np.int32)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _geometry(q, k, heads_hint, cu):
+    if cu is None:
+        b, nq, h, d = q.shape
+        _, nk, hk, _ = k.shape
+        return b, h, hk, nq, nk, d
+    _, h, d = q.shape
+    _, hk, _ = k.shape
+    lens = np.diff(cu)
+    m = int(lens.max()) if len(lens) else 0
+    return len(cu) - 1, h, hk, m, m, d
+
+
+def attention_fwd(q, k, v, *, scale, causal=False, window=(-1, -1),
+                  cu_seqlens=None, rows=None, heads=None, threads=0):
+    """O and LSE of exact attention.  q: (B, Nq, H, d) or packed (T, H, d);
+    k, v: (B, Nk, Hkv, d) or (T, Hkv, d).  ``cu_seqlens`` (B+1 prefix sums)
+    marks a packed batch, used for both queries and keys.  ``rows`` /
+    ``heads`` restrict the computed query rows (positions within each
+    sequence) / query heads; the rest stays NaN."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    cu = _i32(cu_seqlens)
+    B, H, HK, NQ, NK, D = _geometry(q, k, None, cu)
+    o = np.full(q.shape, np.nan)
+    lse = np.full((B, H, NQ) if cu is None else (H, q.shape[0]), np.nan)
+    rs, hs = _i32(rows), _i32(heads)
+    rc = _load().oracle_attention_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu), _ptr(cu),
+        B, H, HK, NQ, NK, D, int(bool(causal)), int(window[0]), int(window[1]),
+        float(scale), _ptr(rs), 0 if rs is None else len(rs),
+        _ptr(hs), 0 if hs is None else len(hs), int(threads))
+    if rc:
+        raise ValueError("oracle_attention_fwd: bad arguments")
+    return o, lse
+
+
+def attention_bwd(q, k, v, dout, *, scale, causal=False, window=(-1, -1),
+                  cu_seqlens=None, q_rows=None, k_rows=None, kv_heads=None,
+                  threads=0):
+    """dQ, dK, dV (and the oracle's own O, LSE on the rows it needed) of exact
+    attention for upstream gradient ``dout``.  ``q_rows`` restricts dQ rows,
+    ``k_rows`` the dK/dV rows, ``kv_heads`` the kv heads (with all query
+    heads of their groups); unselected entries stay NaN."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    cu = _i32(cu_seqlens)
+    B, H, HK, NQ, NK, D = _geometry(q, k, None, cu)
+    dq = np.full(q.shape, np.nan)
+    dk = np.full(k.shape, np.nan)
+    dv = np.full(k.shape, np.nan)
+    o = np.full(q.shape, np.nan)
+    lse = np.full((B, H, NQ) if cu is None else (H, q.shape[0]), np.nan)
+    qr, kr, kh = _i32(q_rows), _i32(k_rows), _i32(kv_heads)
+    rc = _load().oracle_attention_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(o), _ptr(lse), _ptr(cu), _ptr(cu),
+        B, H, HK, NQ, NK, D, int(bool(causal)), int(window[0]), int(window[1]),
+        float(scale), _ptr(qr), 0 if qr is None else len(qr),
+        _ptr(kr), 0 if kr is None else len(kr),
+        _ptr(kh), 0 if kh is None else len(kh), int(threads))
+    if rc:
+        raise ValueError("oracle_attention_bwd: bad arguments")
+    return dq, dk, dv, o, lse
