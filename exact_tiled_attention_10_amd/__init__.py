@@ -1,0 +1,246 @@
+"""Exact tiled attention for AMD MI355X (gfx950): a thin Python binding over
+the C-ABI library ``libfa.so`` (declared in ``include/fa.h``).
+
+Every step of the computation runs in the library's HIP kernels; this module
+only checks tensor metadata, passes ``data_ptr()`` values and the current
+HIP stream, and maps status codes to exceptions.  PyTorch supplies device
+memory and streams.  There is no fallback: if ``libfa.so`` is missing or the
+device is not a gfx950, calls raise.
+
+The call shapes follow flash_attn_func(q, k, v, dropout_p, softmax_scale,
+causal) on (batch, seqlen, nheads, headdim) tensors from the FlashAttention-2
+overview page (lshu.cn/news/55956, section 3.3), with window_size and packed
+variable-length batches as named on the pages.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch  # first: libfa.so then binds to the HIP runtime torch already loaded
+
+__all__ = [
+    "FaError", "lib", "forward", "backward", "flash_attn_func",
+    "flash_attn_varlen_func", "workspace_size", "FA_DTYPE_F16", "FA_DTYPE_BF16",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+FA_DTYPE_F16, FA_DTYPE_BF16 = 0, 1
+_STATUS = {0: "FA_OK", 1: "FA_ERR_INVALID_ARG", 2: "FA_ERR_UNSUPPORTED",
+           3: "FA_ERR_ARCH", 4: "FA_ERR_WORKSPACE", 5: "FA_ERR_LAUNCH"}
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        msg = _lib.fa_strerror(code).decode() if _lib is not None else ""
+        super().__init__(f"{where}: {_STATUS.get(code, code)} ({msg})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C-ABI library with argument types set."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m exact_tiled_attention_10_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.fa_fwd.argtypes = [P] * 7 + [I] * 9 + [F, I, P]
+    L.fa_fwd.restype = I
+    L.fa_bwd_workspace_size.argtypes = [I] * 5
+    L.fa_bwd_workspace_size.restype = S
+    L.fa_bwd.argtypes = [P] * 10 + [S] + [P] * 2 + [I] * 9 + [F, I, P]
+    L.fa_bwd.restype = I
+    L.fa_strerror.argtypes = [I]
+    L.fa_strerror.restype = ctypes.c_char_p
+    L.fa_version.argtypes = []
+    L.fa_version.restype = I
+    _lib = L
+    return L
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float16:
+        return FA_DTYPE_F16
+    if t.dtype == torch.bfloat16:
+        return FA_DTYPE_BF16
+    raise TypeError(f"attention inputs must be float16 or bfloat16, got {t.dtype}")
+
+
+def _check(t: torch.Tensor, name: str, dtype=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (call .contiguous())")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+class _Geom:
+    """Sizes of one call, from the tensors (fixed length or packed)."""
+
+    def __init__(self, q, k, cu_q, cu_k, max_q, max_k):
+        self.varlen = cu_q is not None
+        if self.varlen:
+            if q.dim() != 3 or k.dim() != 3:
+                raise ValueError("packed batches take q as (total_q, heads, d) and k/v as (total_k, kv_heads, d)")
+            if cu_k is None:
+                raise ValueError("cu_seqlens_q and cu_seqlens_k go together")
+            if cu_q.dtype != torch.int32 or cu_k.dtype != torch.int32:
+                raise TypeError("cu_seqlens must be int32")
+            if cu_q.numel() != cu_k.numel() or cu_q.numel() < 1:
+                raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold batch+1 entries")
+            self.batch = cu_q.numel() - 1
+            _, self.heads, self.d = q.shape
+            _, self.kv_heads, dk = k.shape
+            if max_q is None:
+                max_q = int((cu_q[1:] - cu_q[:-1]).max().item()) if self.batch else 0
+            if max_k is None:
+                max_k = int((cu_k[1:] - cu_k[:-1]).max().item()) if self.batch else 0
+            self.seqlen_q, self.seqlen_k = int(max_q), int(max_k)
+            self.lse_shape = (self.heads, q.shape[0])
+        else:
+            if q.dim() != 4 or k.dim() != 4:
+                raise ValueError("q, k, v must be (batch, seqlen, heads, head_dim)")
+            self.batch, self.seqlen_q, self.heads, self.d = q.shape
+            bk, self.seqlen_k, self.kv_heads, dk = k.shape
+            if bk != self.batch:
+                raise ValueError("q and k batch sizes differ")
+            self.lse_shape = (self.batch, self.heads, self.seqlen_q)
+        if dk != self.d:
+            raise ValueError("q and k head_dim differ")
+
+
+def _default_scale(d: int, softmax_scale):
+    return 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+
+
+def forward(q, k, v, *, causal=False, window_size=(-1, -1), softmax_scale=None,
+            cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
+            out=None, lse=None):
+    """O and LSE of exact attention (see include/fa.h for the definition).
+    Returns (out, lse); lse is float32 (batch, heads, seqlen_q) or
+    (heads, total_q) for packed batches."""
+    L = lib()
+    dt = q.dtype
+    _check(q, "q"); _check(k, "k", dt, q.device); _check(v, "v", dt, q.device)
+    if k.shape != v.shape:
+        raise ValueError("k and v shapes differ")
+    if cu_seqlens_q is not None:
+        _check(cu_seqlens_q, "cu_seqlens_q", torch.int32, q.device)
+        _check(cu_seqlens_k, "cu_seqlens_k", torch.int32, q.device)
+    g = _Geom(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", dt, q.device)
+    if lse is None:
+        lse = torch.empty(g.lse_shape, dtype=torch.float32, device=q.device)
+    else:
+        _check(lse, "lse", torch.float32, q.device)
+    rc = L.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                  _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                  g.batch, g.heads, g.kv_heads, g.seqlen_q, g.seqlen_k, g.d,
+                  int(bool(causal)), int(window_size[0]), int(window_size[1]),
+                  _default_scale(g.d, softmax_scale), _dtype_code(q), _stream(q.device))
+    if rc != 0:
+        raise FaError(rc, "fa_fwd")
+    return out, lse
+
+
+def workspace_size(batch, heads, seqlen_q, head_dim, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else (FA_DTYPE_BF16 if dtype == torch.bfloat16 else FA_DTYPE_F16)
+    return int(lib().fa_bwd_workspace_size(batch, heads, seqlen_q, head_dim, code))
+
+
+def backward(dout, q, k, v, out, lse, *, causal=False, window_size=(-1, -1),
+             softmax_scale=None, cu_seqlens_q=None, cu_seqlens_k=None,
+             max_seqlen_q=None, max_seqlen_k=None, dq=None, dk=None, dv=None,
+             workspace=None):
+    """dQ, dK, dV of exact attention for upstream gradient ``dout``, from the
+    forward's ``out`` and ``lse`` (recomputing the scores)."""
+    L = lib()
+    dt = q.dtype
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _check(t, name, dt, q.device)
+    _check(lse, "lse", torch.float32, q.device)
+    if cu_seqlens_q is not None:
+        _check(cu_seqlens_q, "cu_seqlens_q", torch.int32, q.device)
+        _check(cu_seqlens_k, "cu_seqlens_k", torch.int32, q.device)
+    g = _Geom(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check(t, name, dt, q.device)
+        if t.shape != like.shape:
+            raise ValueError(f"{name} must have the shape of its input")
+    need = int(L.fa_bwd_workspace_size(g.batch, g.heads, g.seqlen_q, g.d, _dtype_code(q)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+    rc = L.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
+                  _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                  _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                  g.batch, g.heads, g.kv_heads, g.seqlen_q, g.seqlen_k, g.d,
+                  int(bool(causal)), int(window_size[0]), int(window_size[1]),
+                  _default_scale(g.d, softmax_scale), _dtype_code(q), _stream(q.device))
+    if rc != 0:
+        raise FaError(rc, "fa_bwd")
+    return dq, dk, dv
+
+
+class _FlashAttn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, softmax_scale, causal, window_size, cu_q, cu_k, max_q, max_k):
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        out, lse = forward(q, k, v, causal=causal, window_size=window_size,
+                           softmax_scale=softmax_scale, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k,
+                           max_seqlen_q=max_q, max_seqlen_k=max_k)
+        ctx.save_for_backward(q, k, v, out, lse, cu_q, cu_k)
+        ctx.args = (softmax_scale, causal, window_size, max_q, max_k)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, out, lse, cu_q, cu_k = ctx.saved_tensors
+        softmax_scale, causal, window_size, max_q, max_k = ctx.args
+        dq, dk, dv = backward(dout.contiguous(), q, k, v, out, lse, causal=causal,
+                              window_size=window_size, softmax_scale=softmax_scale,
+                              cu_seqlens_q=cu_q, cu_seqlens_k=cu_k,
+                              max_seqlen_q=max_q, max_seqlen_k=max_k)
+        return dq, dk, dv, None, None, None, None, None, None, None
+
+
+def flash_attn_func(q, k, v, dropout_p=0.0, softmax_scale=None, causal=False,
+                    window_size=(-1, -1)):
+    """Autograd entry with the call shape the pages use; dropout is not
+    implemented (every call on the pages passes 0.0)."""
+    if dropout_p != 0.0:
+        raise NotImplementedError("dropout_p > 0 is not implemented")
+    return _FlashAttn.apply(q, k, v, softmax_scale, causal, tuple(window_size), None, None, None, None)
+
+
+def flash_attn_varlen_func(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                           dropout_p=0.0, softmax_scale=None, causal=False, window_size=(-1, -1)):
+    """Packed variable-length batches: q (total_q, heads, d), k/v (total_k,
+    kv_heads, d), int32 prefix sums cu_seqlens_*."""
+    if dropout_p != 0.0:
+        raise NotImplementedError("dropout_p > 0 is not implemented")
+    return _FlashAttn.apply(q, k, v, softmax_scale, causal, tuple(window_size),
+                            cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)

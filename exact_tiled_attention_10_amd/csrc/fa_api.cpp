@@ -1,0 +1,149 @@
+// C-ABI front end of the attention library: argument validation, the device
+// check and dispatch to the kernel launchers.  Declared in include/fa.h.
+//
+// Every argument check runs before the first HIP call, so misuse is reported
+// the same way on a host without a GPU.  The device check is cached per
+// device ordinal.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "../../include/fa.h"
+#include "fa_launch.hpp"
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+int check_common(int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k, int head_dim,
+                 int causal, int window_left, int window_right, float softmax_scale, int dtype,
+                 const int32_t* cu_q, const int32_t* cu_k) {
+    if (batch < 0 || heads < 1 || kv_heads < 1 || seqlen_q < 0 || seqlen_k < 0) return FA_ERR_INVALID_ARG;
+    if (heads % kv_heads != 0) return FA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    if (window_left < -1 || window_right < -1) return FA_ERR_INVALID_ARG;
+    if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return FA_ERR_INVALID_ARG;
+    if ((cu_q == nullptr) != (cu_k == nullptr)) return FA_ERR_INVALID_ARG;
+    if (cu_q && (!aligned(cu_q, 4) || !aligned(cu_k, 4))) return FA_ERR_INVALID_ARG;
+    // indices are 32-bit inside a sequence, 64-bit across the batch
+    if ((long long)batch * heads > (1LL << 31) - 1) return FA_ERR_INVALID_ARG;
+    if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
+
+int check_arch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return FA_ERR_ARCH;
+    }
+    if (dev < kMaxDevices) {
+        const int st = g_arch_state[dev].load(std::memory_order_relaxed);
+        if (st == 1) return FA_OK;
+        if (st == 2) return FA_ERR_ARCH;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return FA_ERR_ARCH;
+    }
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 &&
+                    (prop.gcnArchName[6] == '\0' || prop.gcnArchName[6] == ':');
+    if (dev < kMaxDevices) g_arch_state[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    return ok ? FA_OK : FA_ERR_ARCH;
+}
+
+float log2e_scaled(float s) { return (float)((double)s * 1.4426950408889634074); }
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+           int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
+           int head_dim, int causal, int window_left, int window_right,
+           float softmax_scale, int dtype, void* stream) {
+    int rc = check_common(batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim, causal, window_left,
+                          window_right, softmax_scale, dtype, cu_seqlens_q, cu_seqlens_k);
+    if (rc != FA_OK) return rc;
+    const bool has_q = (long long)batch * seqlen_q > 0, has_k = (long long)batch * seqlen_k > 0;
+    if ((has_q && (!q || !o || !lse)) || (has_k && (!k || !v))) return FA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+        return FA_ERR_INVALID_ARG;
+    rc = check_arch();
+    if (rc != FA_OK) return rc;
+    fa::FwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
+    a.batch = batch; a.heads = heads; a.kv_heads = kv_heads;
+    a.seqlen_q = seqlen_q; a.seqlen_k = seqlen_k; a.head_dim = head_dim;
+    a.causal = causal; a.left = window_left; a.right = window_right;
+    a.scale = softmax_scale; a.scale_log2 = log2e_scaled(softmax_scale);
+    a.bf16 = dtype == FA_DTYPE_BF16;
+    return fa::launch_fwd(a, (hipStream_t)stream) == 0 ? FA_OK : FA_ERR_LAUNCH;
+}
+
+size_t fa_bwd_workspace_size(int batch, int heads, int seqlen_q, int head_dim, int dtype) {
+    if (batch < 0 || heads < 1 || seqlen_q < 0) return 0;
+    if (head_dim != 64 && head_dim != 128) return 0;
+    if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return 0;
+    const size_t n = (size_t)batch * (size_t)heads * (size_t)seqlen_q * sizeof(float);
+    return n > 0 ? n : 4;  // never zero for valid sizes, so a null workspace is an error
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+           void* workspace, size_t workspace_bytes,
+           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+           int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
+           int head_dim, int causal, int window_left, int window_right,
+           float softmax_scale, int dtype, void* stream) {
+    int rc = check_common(batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim, causal, window_left,
+                          window_right, softmax_scale, dtype, cu_seqlens_q, cu_seqlens_k);
+    if (rc != FA_OK) return rc;
+    const bool has_q = (long long)batch * seqlen_q > 0, has_k = (long long)batch * seqlen_k > 0;
+    if ((has_q && (!q || !o || !lse || !dout || !dq)) || (has_k && (!k || !v || !dk || !dv)) || !workspace)
+        return FA_ERR_INVALID_ARG;
+    const void* p16[] = {q, k, v, o, dout, dq, dk, dv};
+    for (const void* p : p16)
+        if (!aligned(p, 16)) return FA_ERR_INVALID_ARG;
+    if (!aligned(lse, 4) || !aligned(workspace, 4)) return FA_ERR_INVALID_ARG;
+    if (workspace_bytes < fa_bwd_workspace_size(batch, heads, seqlen_q, head_dim, dtype))
+        return FA_ERR_WORKSPACE;
+    rc = check_arch();
+    if (rc != FA_OK) return rc;
+    fa::BwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dsum = (float*)workspace;
+    a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
+    a.batch = batch; a.heads = heads; a.kv_heads = kv_heads;
+    a.seqlen_q = seqlen_q; a.seqlen_k = seqlen_k; a.head_dim = head_dim;
+    a.causal = causal; a.left = window_left; a.right = window_right;
+    a.scale = softmax_scale; a.scale_log2 = log2e_scaled(softmax_scale);
+    a.bf16 = dtype == FA_DTYPE_BF16;
+    return fa::launch_bwd(a, (hipStream_t)stream) == 0 ? FA_OK : FA_ERR_LAUNCH;
+}
+
+const char* fa_strerror(int status) {
+    switch (status) {
+        case FA_OK: return "ok";
+        case FA_ERR_INVALID_ARG: return "invalid argument";
+        case FA_ERR_UNSUPPORTED: return "unsupported head_dim or dtype";
+        case FA_ERR_ARCH: return "no gfx950 (MI355X) device is current";
+        case FA_ERR_WORKSPACE: return "workspace too small";
+        case FA_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int fa_version(void) { return kVersion; }
+
+}  // extern "C"

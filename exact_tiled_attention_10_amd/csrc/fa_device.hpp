@@ -1,0 +1,144 @@
+// Device building blocks for the gfx950 (CDNA4) attention kernels.
+//
+// Matrix products use the 32x32x16 16-bit MFMA with fp32 accumulation.  Lane
+// layout of v_mfma_f32_32x32x16_{bf16,f16} (checked on the device against a
+// host matmul): with lane l, r = l % 32 and half = l / 32,
+//   A (32 x 16, M x K): lane l holds A[r][8*half .. 8*half+7]
+//   B (16 x 32, K x N): lane l holds B[8*half .. 8*half+7][r]
+//   C (32 x 32)       : lane l, register i holds C[8*(i/4) + 4*half + i%4][r]
+// So a C tile gives every lane one column and 16 of its rows, in four runs of
+// four consecutive rows.  Feeding such a tile back as the B operand of the
+// next product (the "P" of P.V and the "dS" of dS.K) is legal if the
+// contraction index is renumbered consistently in both operands: for the
+// k-step that covers rows 16*s .. 16*s+15 of the C tile, operand element j of
+// lane half h stands for row 16*s + ROWPERM(h, j) with
+//   ROWPERM(h, j) = 8*(j/4) + 4*h + j%4,
+// i.e. the row order 0-3, 8-11 | 4-7, 12-15 inside each group of 16.  The
+// other operand is stored in LDS with the same order (rows 4-7 and 8-11 of
+// every 16 swapped), so each lane reads its eight values in one 16-byte load.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kNegInf = -__builtin_inff();
+
+// C += A * B on one 32x32x16 MFMA; A and B are eight 16-bit values per lane.
+template <bool BF16>
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+    if constexpr (BF16) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            __builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+}
+
+// Two fp32 values rounded to nearest even into one packed 16-bit pair
+// (first value in the low half).
+template <bool BF16>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    if constexpr (BF16) {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    } else {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+    }
+}
+
+// One 16-bit value to fp32 (exact).
+template <bool BF16>
+__device__ __forceinline__ float to_f32(uint32_t bits16) {
+    if constexpr (BF16) {
+        return __uint_as_float(bits16 << 16);
+    } else {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+    }
+}
+
+// Combine a per-lane value with the lane 32 positions away (the other half
+// of a wave that holds the same C-tile column).
+__device__ __forceinline__ float max_halves(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Position, inside a row of the permuted LDS layout, of the 4-element chunk
+// holding rows 4*c .. 4*c+3 of a tile: chunks 1 and 2 of every 4 swap places.
+__device__ __forceinline__ int perm_chunk_pos(int c) {
+    const int cc = c & 3;
+    const int pc = (cc == 1) ? 2 : (cc == 2) ? 1 : cc;
+    return ((c >> 2) << 4) + (pc << 2);
+}
+
+// Transpose four rows of eight 16-bit values (r0..r3, element e of row k in
+// half (e & 1) of word e / 2) into eight columns of four: out[e] holds
+// element e of rows 0..3 in order.
+__device__ __forceinline__ void transpose4x8(const u32x4& r0, const u32x4& r1, const u32x4& r2,
+                                             const u32x4& r3, u32x2 out[8]) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        // v_perm_b32 selector bytes: 0-3 pick from the second operand, 4-7 from the first
+        out[2 * w].x = __builtin_amdgcn_perm(r1[w], r0[w], 0x05040100u);
+        out[2 * w].y = __builtin_amdgcn_perm(r3[w], r2[w], 0x05040100u);
+        out[2 * w + 1].x = __builtin_amdgcn_perm(r1[w], r0[w], 0x07060302u);
+        out[2 * w + 1].y = __builtin_amdgcn_perm(r3[w], r2[w], 0x07060302u);
+    }
+}
+
+// Geometry of one (batch, head) problem slice, resolved from cu_seqlens.
+struct Seq {
+    int64_t q_start, k_start;  // first packed row of the sequence
+    int len_q, len_k;
+    int off;                   // len_k - len_q: bottom-right alignment
+};
+
+__device__ __forceinline__ Seq seq_of(int b, const int32_t* cu_q, const int32_t* cu_k,
+                                      int seqlen_q, int seqlen_k) {
+    Seq s;
+    if (cu_q) {
+        const int q0 = cu_q[b], q1 = cu_q[b + 1], k0 = cu_k[b], k1 = cu_k[b + 1];
+        s.q_start = q0; s.k_start = k0; s.len_q = q1 - q0; s.len_k = k1 - k0;
+    } else {
+        s.q_start = (int64_t)b * seqlen_q; s.k_start = (int64_t)b * seqlen_k;
+        s.len_q = seqlen_q; s.len_k = seqlen_k;
+    }
+    s.off = s.len_k - s.len_q;
+    return s;
+}
+
+// Mask parameters: key j visible for query i iff j < len_k and
+// lo(i) <= j <= hi(i), lo(i) = i + off - left (left >= 0), hi(i) = i + off
+// (causal) or i + off + right (right >= 0).
+struct Mask {
+    int causal, left, right;
+    __device__ __forceinline__ int hi_of(int i, const Seq& s) const {
+        int hi = s.len_k - 1;
+        if (causal) hi = min(hi, i + s.off);
+        if (right >= 0) hi = min(hi, i + s.off + right);
+        return hi;
+    }
+    __device__ __forceinline__ int lo_of(int i, const Seq& s) const {
+        return left >= 0 ? max(0, i + s.off - left) : 0;
+    }
+};
+
+}  // namespace fa

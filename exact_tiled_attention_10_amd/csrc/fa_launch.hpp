@@ -1,0 +1,49 @@
+// Host-side argument blocks and launchers shared by the C-ABI front end and
+// the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    const int32_t* cu_q;
+    const int32_t* cu_k;
+    int batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim;
+    int causal, left, right;
+    float scale;       // softmax scale
+    float scale_log2;  // softmax scale * log2(e)
+    int bf16;
+};
+
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const float* lse;
+    const void* dout;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dsum;  // workspace: D_i = dO_i . O_i, laid out like lse
+    const int32_t* cu_q;
+    const int32_t* cu_k;
+    int batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim;
+    int causal, left, right;
+    float scale;
+    float scale_log2;
+    int bf16;
+};
+
+// Each returns 0 when every launch was accepted, 1 otherwise.
+int launch_fwd(const FwdArgs& a, hipStream_t stream);
+int launch_bwd(const BwdArgs& a, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,147 @@
+/*
+ * fa.h - exact tiled attention (forward and backward) for AMD MI355X (gfx950).
+ *
+ * The operation is exact scaled-dot-product attention as defined on the
+ * FlashAttention-2 overview page (lshu.cn/news/55956): section 2.1 gives the
+ * standard definition (score matrix Q K^T, softmax of each row, weighted sum
+ * of V), section 2.2 the tiled, IO-aware way of computing it (Q/K/V tiles
+ * streamed from HBM, online softmax with a running row max and row sum, no
+ * N x N matrix in HBM, double-buffered on-chip tiles), section 3.3 the call
+ * flash_attn_func(q, k, v, dropout_p, softmax_scale, causal) on tensors laid
+ * out (batch, seqlen, nheads, headdim) with num_kv_heads for K and V, and
+ * section 4.2 (question 4) the causal upper-triangular mask.  The install
+ * guide page (yfxerp.com/news/195771, section 1) names the sliding window
+ * (window_size) and the backward that recomputes the scores instead of
+ * storing them; its section 3.3 gives the head_dim contract.  The same
+ * overview page's section 3.2 names packed variable-length batches.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout (row-major, head dimension contiguous, no other strides):
+ *   q, o, dout, dq : [batch, seqlen_q, heads,    head_dim]
+ *   k, v, dk, dv   : [batch, seqlen_k, kv_heads, head_dim]
+ *   lse            : [batch, heads, seqlen_q] float32
+ * Packed variable-length batches (cu_seqlens_q and cu_seqlens_k both
+ * non-null): sequence b holds rows cu_seqlens[b] .. cu_seqlens[b+1]-1 of
+ *   q, o, dout, dq : [total_q, heads,    head_dim]
+ *   k, v, dk, dv   : [total_k, kv_heads, head_dim]
+ *   lse            : [heads, total_q] float32
+ * and seqlen_q / seqlen_k give the longest sequence of each.  cu_seqlens_*
+ * are device arrays of batch+1 non-decreasing int32 prefix sums starting at
+ * 0 (not checked on the device).
+ *
+ * Visible keys of query row i in a sequence of Lq queries and Lk keys, with
+ * p = i + Lk - Lq (bottom-right alignment; p = i when Lq = Lk):
+ *   key j is visible iff 0 <= j < Lk, (causal == 0 or j <= p),
+ *   (window_left < 0 or j >= p - window_left) and
+ *   (window_right < 0 or j <= p + window_right).
+ * A row with no visible key gets O = 0 and LSE = -inf (and zero gradient).
+ * GQA / MQA: query head h reads kv head h / (heads / kv_heads).
+ *
+ * LSE[i] = ln(sum over visible j of exp(softmax_scale * q_i . k_j)).
+ *
+ * Arithmetic: 16-bit inputs (fp16 or bf16, same type for every tensor),
+ * products on the matrix cores with fp32 accumulation, softmax statistics
+ * in fp32, P rounded to the input type before P.V, outputs rounded to
+ * nearest even.  Results are deterministic (no atomics): the same call on
+ * the same inputs gives the same bytes.
+ *
+ * Pointers: device pointers, 16-byte aligned (lse and the workspace 4-byte
+ * aligned).  A tensor with no elements may be passed as NULL: the query-side
+ * tensors (q, o, lse, dout, dq) when batch * seqlen_q == 0, the key-side ones
+ * (k, v, dk, dv) when batch * seqlen_k == 0.  The caller owns every buffer; the library allocates nothing,
+ * frees nothing and keeps no pointer after returning.  Inputs are never
+ * written, outputs are fully overwritten (no zeroing needed) and must not
+ * alias inputs or each other.
+ *
+ * Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL is the null
+ * stream) and the call returns without waiting.  Execution errors surface at
+ * the caller's next synchronisation.
+ *
+ * Errors: every argument check runs before any HIP call, so a bad call
+ * returns its code on any host.  The device check (FA_ERR_ARCH) is the
+ * first HIP call; on a host without a gfx950 device it returns that code.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fa_status {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, bad scale   */
+    FA_ERR_UNSUPPORTED = 2, /* head_dim not 64/128, or dtype not fp16/bf16        */
+    FA_ERR_ARCH = 3,        /* no HIP device, or the current device is not gfx950 */
+    FA_ERR_WORKSPACE = 4,   /* workspace smaller than fa_bwd_workspace_size()     */
+    FA_ERR_LAUNCH = 5       /* a kernel launch was rejected by the runtime        */
+};
+
+enum fa_dtype { FA_DTYPE_F16 = 0, FA_DTYPE_BF16 = 1 };
+
+/*
+ * Forward: O = softmax(softmax_scale * Q K^T restricted to visible keys) V,
+ * and LSE, in one fused pass per query tile (overview page, sections 2.2
+ * "tiled fusion" and "online softmax").
+ *   q, k, v        in : see layout above
+ *   o              out: like q
+ *   lse            out: float32, see layout above
+ *   cu_seqlens_q/k in : both NULL (fixed length) or both device int32[batch+1]
+ *   batch >= 0, heads >= 1, kv_heads >= 1 with heads % kv_heads == 0,
+ *   seqlen_q >= 0, seqlen_k >= 0, head_dim in {64, 128},
+ *   causal in {0, 1}, window_left >= -1, window_right >= -1 (-1 = unbounded),
+ *   softmax_scale finite and >= 0 (callers wanting the default pass
+ *   1/sqrt(head_dim)), dtype one of fa_dtype.
+ * Returns FA_OK or an fa_status code; nothing is enqueued on error.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+           int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
+           int head_dim, int causal, int window_left, int window_right,
+           float softmax_scale, int dtype, void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for these sizes (the per-row term
+ * D_i = dO_i . O_i, float32, one per query row and head).  For packed
+ * batches pass the same batch and seqlen_q as to fa_bwd.  Returns 0 for
+ * invalid sizes.
+ */
+size_t fa_bwd_workspace_size(int batch, int heads, int seqlen_q, int head_dim, int dtype);
+
+/*
+ * Backward: given the forward's inputs, its O and LSE, and dout = dL/dO,
+ * writes dq, dk, dv (same dtype and layout as q, k, v).  The scores are
+ * recomputed from Q, K and the saved LSE (install guide page, section 1);
+ * the N x N matrices are never stored.  Three kernels run in order on
+ * `stream`: the row term D_i = dO_i . O_i, a pass over key tiles that
+ * accumulates dK and dV (summing the query heads of a GQA group inside the
+ * workgroup), and a separate pass over query tiles that accumulates dQ.
+ *   workspace / workspace_bytes: device memory of at least
+ *   fa_bwd_workspace_size(batch, heads, seqlen_q, head_dim, dtype) bytes,
+ *   owned by the caller; its contents on entry do not matter.
+ * All other arguments as for fa_fwd, which must have produced o and lse
+ * with the same arguments.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+           void* workspace, size_t workspace_bytes,
+           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+           int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
+           int head_dim, int causal, int window_left, int window_right,
+           float softmax_scale, int dtype, void* stream);
+
+/* Static text for a status code ("unknown status" for others). */
+const char* fa_strerror(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -18,13 +18,15 @@ Streams for one seed: Q = 16*seed + 0, K = +1, V = +2, dO = +3, lengths = +4.
 Tensors are laid out (batch, seqlen, heads, head_dim) with the last dimension
 contiguous; variable-length batches are packed to (total, heads, head_dim).
 
-The workload shapes are those of the exact-attention pages: the parity check
-on the Blackwell page (lshu/pptc pages: fp16, causal, head_dim 64/128), the
-7B-layer shape at 8K and the long-context / sliding-window cases.
+The named workloads stand in for the pages' own (model-level runs that need
+trained weights): a small non-causal fp16 case, a causal d=64 batch, a
+7B-layer attention shape at 8K, a long-context GQA shape at 32K and a packed
+sliding-window batch.
 """
 from __future__ import annotations
 
 import math
+import os
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -62,7 +64,8 @@ def normals_f64(stream: int, count: int) -> np.ndarray:
     the raw pair (2*(n//2), 2*(n//2)+1)."""
     out = np.empty(count, dtype=np.float64)
     two53 = float(1 << 53)
-    for c0 in range(0, count, _CHUNK):
+
+    def fill(c0):
         c1 = min(count, c0 + _CHUNK)
         p0 = c0 // 2
         p1 = (c1 + 1) // 2
@@ -78,6 +81,16 @@ def normals_f64(stream: int, count: int) -> np.ndarray:
         pair[1::2] = r * np.sin(t)
         off = c0 - 2 * p0
         out[c0:c1] = pair[off:off + (c1 - c0)]
+
+    starts = range(0, count, _CHUNK)
+    if count > _CHUNK:
+        # chunks are independent (counter-based), so threads change nothing
+        import concurrent.futures as cf
+        with cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+            list(ex.map(fill, starts))
+    else:
+        for c0 in starts:
+            fill(c0)
     return out
 
 
@@ -153,6 +166,8 @@ def make_problem(*, dtype: str, batch: int, heads: int, kv_heads: int,
     sequence uniformly on [lo, hi] (stream 4) and packs the batch; ``seqlens``
     gives the lengths explicitly instead."""
     seqlen_k = seqlen if seqlen_k is None else seqlen_k
+    if seqlens is not None:
+        batch = len(seqlens)
     if scale is None:
         scale = 1.0 / math.sqrt(head_dim)
     lens = None

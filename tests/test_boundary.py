@@ -1,0 +1,142 @@
+"""The C-ABI boundary on a CPU host: the library loads, exports every entry
+point include/fa.h declares, and rejects bad arguments with the documented
+codes before any HIP call.  No kernel runs here."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+OK, INVALID, UNSUPPORTED, ARCH, WORKSPACE, LAUNCH = range(6)
+
+
+@pytest.fixture(scope="module")
+def L():
+    import exact_tiled_attention_10_amd as fa
+    if not os.path.exists(fa.LIB_PATH):
+        from exact_tiled_attention_10_amd import build
+        build.build()
+    return fa.lib()
+
+
+# Fake, 256-byte aligned addresses: only ever passed where validation must
+# reject the call before anything touches them, or on a host with no GPU.
+FAKE = [ctypes.c_void_p(0x10000 * (i + 1)) for i in range(12)]
+no_gpu = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                            reason="passes fake pointers; only safe where no GPU exists")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(fa_[a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_strerror", "fa_version"]
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_strerror_and_version(L):
+    assert L.fa_strerror(0) == b"ok"
+    for code in range(1, 6):
+        assert L.fa_strerror(code) not in (b"", b"unknown status")
+    assert L.fa_strerror(99) == b"unknown status"
+    assert L.fa_version() >= 10000
+
+
+def fwd(L, **over):
+    args = dict(q=FAKE[0], k=FAKE[1], v=FAKE[2], o=FAKE[3], lse=FAKE[4], cu_q=None, cu_k=None,
+                batch=1, heads=4, kv_heads=2, seqlen_q=128, seqlen_k=128, head_dim=128,
+                causal=1, left=-1, right=-1, scale=0.125, dtype=1, stream=None)
+    args.update(over)
+    return L.fa_fwd(args["q"], args["k"], args["v"], args["o"], args["lse"], args["cu_q"], args["cu_k"],
+                    args["batch"], args["heads"], args["kv_heads"], args["seqlen_q"], args["seqlen_k"],
+                    args["head_dim"], args["causal"], args["left"], args["right"], args["scale"],
+                    args["dtype"], args["stream"])
+
+
+def bwd(L, **over):
+    args = dict(q=FAKE[0], k=FAKE[1], v=FAKE[2], o=FAKE[3], lse=FAKE[4], do=FAKE[5], dq=FAKE[6],
+                dk=FAKE[7], dv=FAKE[8], ws=FAKE[9], wsb=1 << 20, cu_q=None, cu_k=None,
+                batch=1, heads=4, kv_heads=2, seqlen_q=128, seqlen_k=128, head_dim=128,
+                causal=1, left=-1, right=-1, scale=0.125, dtype=1, stream=None)
+    args.update(over)
+    return L.fa_bwd(args["q"], args["k"], args["v"], args["o"], args["lse"], args["do"], args["dq"],
+                    args["dk"], args["dv"], args["ws"], args["wsb"], args["cu_q"], args["cu_k"],
+                    args["batch"], args["heads"], args["kv_heads"], args["seqlen_q"], args["seqlen_k"],
+                    args["head_dim"], args["causal"], args["left"], args["right"], args["scale"],
+                    args["dtype"], args["stream"])
+
+
+BAD_FWD = [
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID),
+    (dict(o=None), INVALID), (dict(lse=None), INVALID),
+    (dict(q=ctypes.c_void_p(0x10008)), INVALID),        # misaligned
+    (dict(batch=-1), INVALID), (dict(heads=0), INVALID), (dict(kv_heads=0), INVALID),
+    (dict(heads=6, kv_heads=4), INVALID), (dict(seqlen_q=-1), INVALID), (dict(seqlen_k=-5), INVALID),
+    (dict(causal=2), INVALID), (dict(left=-2), INVALID), (dict(right=-3), INVALID),
+    (dict(scale=-0.5), INVALID), (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(cu_q=FAKE[10]), INVALID),                      # only one of the pair
+    (dict(head_dim=96), UNSUPPORTED), (dict(head_dim=256), UNSUPPORTED), (dict(head_dim=0), UNSUPPORTED),
+    (dict(dtype=2), UNSUPPORTED), (dict(dtype=-1), UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("over,code", BAD_FWD)
+def test_fwd_rejects_bad_arguments(L, over, code):
+    assert fwd(L, **over) == code
+
+
+BAD_BWD = [
+    (dict(do=None), INVALID), (dict(dq=None), INVALID), (dict(dk=None), INVALID),
+    (dict(dv=None), INVALID), (dict(ws=None), INVALID),
+    (dict(dv=ctypes.c_void_p(0x10004)), INVALID),
+    (dict(heads=3, kv_heads=2), INVALID), (dict(head_dim=32), UNSUPPORTED),
+    (dict(wsb=4 * 4 * 128 - 4), WORKSPACE), (dict(wsb=0), WORKSPACE),
+]
+
+
+@pytest.mark.parametrize("over,code", BAD_BWD)
+def test_bwd_rejects_bad_arguments(L, over, code):
+    assert bwd(L, **over) == code
+
+
+def test_workspace_size(L):
+    f = L.fa_bwd_workspace_size
+    assert f(2, 8, 1000, 128, 1) == 2 * 8 * 1000 * 4
+    assert f(1, 4, 128, 64, 0) == 4 * 128 * 4
+    assert f(0, 4, 128, 64, 0) == 4  # never zero for valid sizes
+    assert f(1, 4, 128, 96, 0) == 0 and f(1, 0, 128, 64, 0) == 0 and f(1, 4, 128, 64, 7) == 0
+
+
+@no_gpu
+def test_valid_call_without_gfx950_reports_arch(L):
+    assert fwd(L) == ARCH
+    assert bwd(L) == ARCH
+    # empty tensors may be NULL: no keys, no queries, empty batch
+    assert fwd(L, k=None, v=None, seqlen_k=0) == ARCH
+    assert fwd(L, q=None, o=None, lse=None, seqlen_q=0) == ARCH
+    assert bwd(L, k=None, v=None, dk=None, dv=None, seqlen_k=0) == ARCH
+
+
+def test_null_pointers_only_for_empty_tensors(L):
+    assert fwd(L, k=None, seqlen_k=1) == INVALID
+    assert fwd(L, q=None, seqlen_k=0) == INVALID
+    assert bwd(L, dq=None, seqlen_k=0) == INVALID
+    assert bwd(L, dk=None, seqlen_q=0) == INVALID
+
+
+def test_python_binding_fails_loudly_without_gpu_tensors():
+    import exact_tiled_attention_10_amd as fa
+    q = torch.zeros(1, 8, 2, 64, dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU"):
+        fa.forward(q, q, q)
