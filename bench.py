@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark of exact tiled attention (forward + backward) on one MI355X.
+
+One step = fa_fwd, then the three backward kernels (row term, dK/dV pass,
+dQ pass) on one batch of the 7B-layer attention shape at 8K: bf16, causal,
+batch 1, 32 heads, seqlen 8192, head_dim 128, Q/K/V ~ N(0,1)*0.5 and
+dO ~ N(0,1) from the seeded generator.  Inputs are resident in HBM before
+the timed region.  HIP events on the launch stream bracket every kernel of
+every timed step; the wall clock around the K steps gives ms_per_step.
+
+value = algorithmic FLOPs of the step / step time, with forward FLOPs
+4*d*P*H and backward 10*d*P*H (P = visible (query, key) pairs per head,
+N(N+1)/2 for causal), i.e. two and five d-long contractions per visible
+pair.  The roofline object describes the kernel with the largest share of
+the step.  The CPU baseline is the fp64 oracle timed on a bounded sample of
+the same workload (one head, all rows, forward + backward).
+
+Prints ONE JSON line.  Only one GPU: --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 4096 dense bf16 FLOP/clk/CU x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+WORKLOAD = "bf16_causal_b1_h32_n8192_d128"
+METRIC = "attention fwd+bwd TFLOP/s and % MFMA bf16 peak, seq 8192 d128 causal, 1 GPU"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "exact_tiled_attention_10_amd", "csrc")
+KERNEL_SOURCES = {
+    "fwd": ["fa_fwd.hip", "fa_device.hpp"],
+    "bwd_rowdot": ["fa_bwd.hip", "fa_device.hpp"],
+    "bwd_dkdv": ["fa_bwd.hip", "fa_device.hpp"],
+    "bwd_dq": ["fa_bwd.hip", "fa_device.hpp"],
+}
+
+
+def visible_pairs(p) -> int:
+    """Number of visible (query, key) pairs summed over sequences (one head)."""
+    lens = p.seqlens if p.seqlens is not None else [p.seqlen_q] * p.batch
+    lens_k = p.seqlens if p.seqlens is not None else [p.seqlen_k] * p.batch
+    total = 0
+    for lq, lk in zip(lens, lens_k):
+        i = np.arange(lq, dtype=np.int64)
+        pos = i + (lk - lq)
+        hi = np.full(lq, lk - 1, dtype=np.int64)
+        if p.causal:
+            hi = np.minimum(hi, pos)
+        if p.window_right >= 0:
+            hi = np.minimum(hi, pos + p.window_right)
+        lo = np.maximum(0, pos - p.window_left) if p.window_left >= 0 else np.zeros(lq, dtype=np.int64)
+        total += int(np.clip(hi - lo + 1, 0, None).sum())
+    return total
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+    when there are none for this kernel/workload or the source changed."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            data = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    ent = data.get("kernels", {}).get(kernel)
+    if not ent or ent.get("workload") != workload or ent.get("source_hash") != source_hash(kernel):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+CPU_SAMPLE_HEADS = 4
+
+
+def cpu_baseline(p, threads: int):
+    """fp64 oracle, forward + backward for the first CPU_SAMPLE_HEADS kv heads
+    (with their query heads) of batch 0 of the workload."""
+    import oracle
+    oracle.build(force=False)
+    pairs = visible_pairs(p)
+    d = p.head_dim
+    nh = CPU_SAMPLE_HEADS * (p.heads // p.kv_heads)
+    flops = (4 + 10) * d * pairs * nh / p.batch
+    q, k, v, do = (t[:1].double().numpy() for t in (p.q, p.k, p.v, p.do))
+    t0 = time.perf_counter()
+    oracle.attention_bwd(q, k, v, do, scale=p.scale, causal=p.causal,
+                         window=(p.window_left, p.window_right),
+                         kv_heads=list(range(CPU_SAMPLE_HEADS)), threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"{WORKLOAD}: {nh} of {p.heads} heads of batch 0, all {p.seqlen_q} rows, "
+                      f"forward + backward in fp64 ({flops / 1e9:.1f} GFLOP)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (default min(16, cores))")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import exact_tiled_attention_10_amd as fa
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    p = synth.workload(WORKLOAD)
+    q, k, v, do = (t.to(dev) for t in (p.q, p.k, p.v, p.do))
+    plan = fa.Plan(q, k, v, do, causal=p.causal, window_size=(p.window_left, p.window_right),
+                   softmax_scale=p.scale)
+    stream = plan.stream
+    names = ["fwd", "bwd_rowdot", "bwd_dkdv", "bwd_dq"]
+    calls = [plan.fwd, lambda: plan.bwd_stage(0), lambda: plan.bwd_stage(1), lambda: plan.bwd_stage(2)]
+
+    for _ in range(args.warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        ev = events[s]
+        ev[0].record(stream)
+        for i, c in enumerate(calls):
+            c()
+            ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / K
+    kern_ms = {n: float(np.mean([events[s][i].elapsed_time(events[s][i + 1]) for s in range(K)]))
+               for i, n in enumerate(names)}
+    ev_step_ms = float(np.mean([events[s][0].elapsed_time(events[s][-1]) for s in range(K)]))
+
+    pairs = visible_pairs(p)
+    d, H = p.head_dim, p.heads
+    fwd_flops = 4.0 * d * pairs * H
+    bwd_flops = 10.0 * d * pairs * H
+    nrow = p.batch * p.seqlen_q * H
+    algo = {  # algorithmic work per launch
+        "fwd": ("mfma", fwd_flops),
+        "bwd_rowdot": ("hbm", 2.0 * nrow * d * 2 + 4.0 * nrow),
+        "bwd_dkdv": ("mfma", 8.0 * d * pairs * H),
+        "bwd_dq": ("mfma", 2.0 * d * pairs * H),
+    }
+    kernels = {}
+    for n in names:
+        bound, work = algo[n]
+        t = kern_ms[n] / 1e3
+        if bound == "mfma":
+            ach = work / t / 1e12
+            kernels[n] = {"ms": round(kern_ms[n], 4), "bound": "mfma", "achieved": round(ach, 2),
+                          "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+        else:
+            ach = work / t / 1e9
+            kernels[n] = {"ms": round(kern_ms[n], 4), "bound": "hbm", "achieved": round(ach, 1),
+                          "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4)}
+    dom = max(names, key=lambda n: kern_ms[n])
+    kd = kernels[dom]
+    roofline = {"bound": kd["bound"], "kernel": dom, "achieved": kd["achieved"],
+                "peak": PEAK_BF16_TFLOPS if kd["bound"] == "mfma" else PEAK_HBM_GBS,
+                "unit": kd["unit"], "frac": kd["frac"], "traffic": measured_traffic(dom, WORKLOAD)}
+
+    fwd_ms = kern_ms["fwd"]
+    bwd_ms = kern_ms["bwd_rowdot"] + kern_ms["bwd_dkdv"] + kern_ms["bwd_dq"]
+    value = (fwd_flops + bwd_flops) / (ms_step / 1e3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded SplitMix64 + Box-Muller normals)",
+        "config": {"workload": WORKLOAD, "batch": p.batch, "heads": H, "kv_heads": p.kv_heads,
+                   "seq_len": p.seqlen_q, "head_dim": d, "causal": bool(p.causal),
+                   "parallelism": "single GPU"},
+        "pct_peak": {"fwd": round(100 * fwd_flops / (fwd_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                     "bwd": round(100 * bwd_flops / (bwd_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                     "step": round(100 * value / PEAK_BF16_TFLOPS, 2)},
+        "fwd_tflops": round(fwd_flops / (fwd_ms / 1e3) / 1e12, 2),
+        "bwd_tflops": round(bwd_flops / (bwd_ms / 1e3) / 1e12, 2),
+        "fwd_ms": round(fwd_ms, 4),
+        "bwd_ms": round(bwd_ms, 4),
+        "event_ms_per_step": round(ev_step_ms, 4),
+        "tokens_per_s": round(p.batch * p.seqlen_q / (ms_step / 1e3), 1),
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+        out["cpu_baseline"] = cpu_baseline(p, threads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

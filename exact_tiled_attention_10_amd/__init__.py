@@ -21,7 +21,7 @@ import os
 import torch  # first: libfa.so then binds to the HIP runtime torch already loaded
 
 __all__ = [
-    "FaError", "lib", "forward", "backward", "flash_attn_func",
+    "FaError", "lib", "forward", "backward", "Plan", "flash_attn_func",
     "flash_attn_varlen_func", "workspace_size", "FA_DTYPE_F16", "FA_DTYPE_BF16",
 ]
 
@@ -55,6 +55,8 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd_workspace_size.restype = S
     L.fa_bwd.argtypes = [P] * 10 + [S] + [P] * 2 + [I] * 9 + [F, I, P]
     L.fa_bwd.restype = I
+    L.fa_bwd_stage.argtypes = [I] + [P] * 10 + [S] + [P] * 2 + [I] * 9 + [F, I, P]
+    L.fa_bwd_stage.restype = I
     L.fa_strerror.argtypes = [I]
     L.fa_strerror.restype = ctypes.c_char_p
     L.fa_version.argtypes = []
@@ -203,6 +205,57 @@ def backward(dout, q, k, v, out, lse, *, causal=False, window_size=(-1, -1),
     if rc != 0:
         raise FaError(rc, "fa_bwd")
     return dq, dk, dv
+
+
+class Plan:
+    """Pre-resolved C-ABI arguments for repeated calls on fixed buffers (the
+    benchmark loop): ``fwd()`` runs fa_fwd, ``bwd_stage(s)`` one backward
+    kernel, ``bwd()`` all three, each enqueued on ``stream`` (default: the
+    current torch stream of q's device).  Buffers are allocated once here."""
+
+    def __init__(self, q, k, v, dout=None, *, causal=False, window_size=(-1, -1), softmax_scale=None,
+                 cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, stream=None):
+        L = lib()
+        dt = q.dtype
+        _check(q, "q"); _check(k, "k", dt, q.device); _check(v, "v", dt, q.device)
+        g = _Geom(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+        self.geom = g
+        self.q, self.k, self.v, self.dout = q, k, v, dout
+        self.out = torch.empty_like(q)
+        self.lse = torch.empty(g.lse_shape, dtype=torch.float32, device=q.device)
+        self.cu_q, self.cu_k = cu_seqlens_q, cu_seqlens_k
+        st = stream if stream is not None else torch.cuda.current_stream(q.device)
+        self.stream = st
+        sp = ctypes.c_void_p(st.cuda_stream)
+        common = [g.batch, g.heads, g.kv_heads, g.seqlen_q, g.seqlen_k, g.d,
+                  int(bool(causal)), int(window_size[0]), int(window_size[1]),
+                  _default_scale(g.d, softmax_scale), _dtype_code(q), sp]
+        self._fwd = [_ptr(q), _ptr(k), _ptr(v), _ptr(self.out), _ptr(self.lse),
+                     _ptr(cu_seqlens_q), _ptr(cu_seqlens_k)] + common
+        if dout is not None:
+            _check(dout, "dout", dt, q.device)
+            self.dq, self.dk, self.dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+            need = int(L.fa_bwd_workspace_size(g.batch, g.heads, g.seqlen_q, g.d, _dtype_code(q)))
+            self.workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+            self._bwd = [_ptr(q), _ptr(k), _ptr(v), _ptr(self.out), _ptr(self.lse), _ptr(dout),
+                         _ptr(self.dq), _ptr(self.dk), _ptr(self.dv), _ptr(self.workspace),
+                         self.workspace.numel(), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k)] + common
+        self._L = L
+
+    def fwd(self):
+        rc = self._L.fa_fwd(*self._fwd)
+        if rc != 0:
+            raise FaError(rc, "fa_fwd")
+
+    def bwd_stage(self, stage: int):
+        rc = self._L.fa_bwd_stage(stage, *self._bwd)
+        if rc != 0:
+            raise FaError(rc, f"fa_bwd_stage({stage})")
+
+    def bwd(self):
+        rc = self._L.fa_bwd(*self._bwd)
+        if rc != 0:
+            raise FaError(rc, "fa_bwd")
 
 
 class _FlashAttn(torch.autograd.Function):

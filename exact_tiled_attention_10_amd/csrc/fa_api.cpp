@@ -99,13 +99,18 @@ size_t fa_bwd_workspace_size(int batch, int heads, int seqlen_q, int head_dim, i
     return n > 0 ? n : 4;  // never zero for valid sizes, so a null workspace is an error
 }
 
-int fa_bwd(const void* q, const void* k, const void* v, const void* o,
-           const float* lse, const void* dout, void* dq, void* dk, void* dv,
-           void* workspace, size_t workspace_bytes,
-           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
-           int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
-           int head_dim, int causal, int window_left, int window_right,
-           float softmax_scale, int dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int bwd_common(int stage_lo, int stage_hi,
+               const void* q, const void* k, const void* v, const void* o,
+               const float* lse, const void* dout, void* dq, void* dk, void* dv,
+               void* workspace, size_t workspace_bytes,
+               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+               int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
+               int head_dim, int causal, int window_left, int window_right,
+               float softmax_scale, int dtype, void* stream) {
     int rc = check_common(batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim, causal, window_left,
                           window_right, softmax_scale, dtype, cu_seqlens_q, cu_seqlens_k);
     if (rc != FA_OK) return rc;
@@ -129,7 +134,38 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
     a.causal = causal; a.left = window_left; a.right = window_right;
     a.scale = softmax_scale; a.scale_log2 = log2e_scaled(softmax_scale);
     a.bf16 = dtype == FA_DTYPE_BF16;
-    return fa::launch_bwd(a, (hipStream_t)stream) == 0 ? FA_OK : FA_ERR_LAUNCH;
+    for (int st = stage_lo; st <= stage_hi; ++st)
+        if (fa::launch_bwd(a, st, (hipStream_t)stream) != 0) return FA_ERR_LAUNCH;
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+           void* workspace, size_t workspace_bytes,
+           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+           int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
+           int head_dim, int causal, int window_left, int window_right,
+           float softmax_scale, int dtype, void* stream) {
+    return bwd_common(0, 2, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes,
+                      cu_seqlens_q, cu_seqlens_k, batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim,
+                      causal, window_left, window_right, softmax_scale, dtype, stream);
+}
+
+int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                 const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                 void* workspace, size_t workspace_bytes,
+                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                 int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
+                 int head_dim, int causal, int window_left, int window_right,
+                 float softmax_scale, int dtype, void* stream) {
+    if (stage < 0 || stage > 2) return FA_ERR_INVALID_ARG;
+    return bwd_common(stage, stage, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes,
+                      cu_seqlens_q, cu_seqlens_k, batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim,
+                      causal, window_left, window_right, softmax_scale, dtype, stream);
 }
 
 const char* fa_strerror(int status) {

@@ -488,12 +488,8 @@ bool set_smem(K kernel, int bytes) {
 }
 
 template <bool BF16, int D>
-int launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
-    if (a.batch == 0 || a.seqlen_q == 0) {
-        // no query rows: dK, dV are zero, handled by the dK/dV pass below
-    }
-    // 1. D_i = dO_i . O_i
-    {
+int launch_bwd_t(const BwdArgs& a, int stage, hipStream_t stream) {
+    if (stage == 0) {  // D_i = dO_i . O_i
         constexpr int RPB = 256 / (D / 8);
         const int64_t items = (int64_t)a.batch * a.seqlen_q * a.heads;
         const int64_t blocks = (items + RPB - 1) / RPB;
@@ -501,37 +497,37 @@ int launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
             hipLaunchKernelGGL((bwd_rowdot_kernel<BF16, D>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
             if (hipGetLastError() != hipSuccess) return 1;
         }
+        return 0;
     }
-    // 2. dK, dV
-    {
+    if (stage == 1) {  // dK, dV
         const int ntiles = (a.seqlen_k + kKvBN - 1) / kKvBN;
         if (ntiles > 0 && a.batch > 0) {
-            static bool ok = set_smem(bwd_dkdv_kernel<BF16, D>, DkdvSmem<D>::bytes);
+            static const bool ok = set_smem(bwd_dkdv_kernel<BF16, D>, DkdvSmem<D>::bytes);
             if (!ok) return 1;
             hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D>), dim3(a.batch * a.kv_heads, ntiles), dim3(256),
                                DkdvSmem<D>::bytes, stream, a);
             if (hipGetLastError() != hipSuccess) return 1;
         }
+        return 0;
     }
-    // 3. dQ
-    {
-        const int ntiles = (a.seqlen_q + kQBM - 1) / kQBM;
-        if (ntiles > 0 && a.batch > 0) {
-            static bool ok = set_smem(bwd_dq_kernel<BF16, D>, DqSmem<D>::bytes);
-            if (!ok) return 1;
-            hipLaunchKernelGGL((bwd_dq_kernel<BF16, D>), dim3(a.batch * a.heads, ntiles), dim3(256),
-                               DqSmem<D>::bytes, stream, a);
-            if (hipGetLastError() != hipSuccess) return 1;
-        }
+    // stage 2: dQ
+    const int ntiles = (a.seqlen_q + kQBM - 1) / kQBM;
+    if (ntiles > 0 && a.batch > 0) {
+        static const bool ok = set_smem(bwd_dq_kernel<BF16, D>, DqSmem<D>::bytes);
+        if (!ok) return 1;
+        hipLaunchKernelGGL((bwd_dq_kernel<BF16, D>), dim3(a.batch * a.heads, ntiles), dim3(256),
+                           DqSmem<D>::bytes, stream, a);
+        if (hipGetLastError() != hipSuccess) return 1;
     }
     return 0;
 }
 
 }  // namespace
 
-int launch_bwd(const BwdArgs& a, hipStream_t stream) {
-    if (a.bf16) return a.head_dim == 128 ? launch_bwd_t<true, 128>(a, stream) : launch_bwd_t<true, 64>(a, stream);
-    return a.head_dim == 128 ? launch_bwd_t<false, 128>(a, stream) : launch_bwd_t<false, 64>(a, stream);
+int launch_bwd(const BwdArgs& a, int stage, hipStream_t stream) {
+    if (a.bf16)
+        return a.head_dim == 128 ? launch_bwd_t<true, 128>(a, stage, stream) : launch_bwd_t<true, 64>(a, stage, stream);
+    return a.head_dim == 128 ? launch_bwd_t<false, 128>(a, stage, stream) : launch_bwd_t<false, 64>(a, stage, stream);
 }
 
 }  // namespace fa

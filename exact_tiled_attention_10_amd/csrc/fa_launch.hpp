@@ -42,8 +42,9 @@ struct BwdArgs {
     int bf16;
 };
 
-// Each returns 0 when every launch was accepted, 1 otherwise.
+// Each returns 0 when every launch was accepted, 1 otherwise.  Backward
+// stages: 0 = D_i = dO_i . O_i, 1 = dK/dV pass, 2 = dQ pass.
 int launch_fwd(const FwdArgs& a, hipStream_t stream);
-int launch_bwd(const BwdArgs& a, hipStream_t stream);
+int launch_bwd(const BwdArgs& a, int stage, hipStream_t stream);
 
 }  // namespace fa

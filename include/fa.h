@@ -49,8 +49,9 @@
  * Pointers: device pointers, 16-byte aligned (lse and the workspace 4-byte
  * aligned).  A tensor with no elements may be passed as NULL: the query-side
  * tensors (q, o, lse, dout, dq) when batch * seqlen_q == 0, the key-side ones
- * (k, v, dk, dv) when batch * seqlen_k == 0.  The caller owns every buffer; the library allocates nothing,
- * frees nothing and keeps no pointer after returning.  Inputs are never
+ * (k, v, dk, dv) when batch * seqlen_k == 0.  The caller owns every
+ * buffer; the library allocates nothing, frees nothing and keeps no pointer
+ * after returning.  Inputs are never
  * written, outputs are fully overwritten (no zeroing needed) and must not
  * alias inputs or each other.
  *
@@ -133,6 +134,22 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
            int head_dim, int causal, int window_left, int window_right,
            float softmax_scale, int dtype, void* stream);
+
+/*
+ * One stage of fa_bwd, for callers that schedule or time the three kernels
+ * themselves: stage 0 writes D_i = dO_i . O_i into the workspace, stage 1
+ * writes dk and dv, stage 2 writes dq.  fa_bwd is exactly stages 0, 1, 2 in
+ * this order on one stream; stages 1 and 2 read the workspace stage 0 wrote
+ * and are independent of each other.  Arguments as for fa_bwd; a stage
+ * outside 0..2 returns FA_ERR_INVALID_ARG.
+ */
+int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                 const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                 void* workspace, size_t workspace_bytes,
+                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                 int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
+                 int head_dim, int causal, int window_left, int window_right,
+                 float softmax_scale, int dtype, void* stream);
 
 /* Static text for a status code ("unknown status" for others). */
 const char* fa_strerror(int status);

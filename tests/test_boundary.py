@@ -37,7 +37,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_strerror", "fa_version"]
+    assert declared_functions() == ["fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_fwd",
+                                    "fa_strerror", "fa_version"]
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -108,6 +109,18 @@ BAD_BWD = [
 @pytest.mark.parametrize("over,code", BAD_BWD)
 def test_bwd_rejects_bad_arguments(L, over, code):
     assert bwd(L, **over) == code
+
+
+@pytest.mark.parametrize("stage", [-1, 3, 100])
+def test_bwd_stage_rejects_unknown_stage(L, stage):
+    args = [FAKE[i] for i in range(10)] + [1 << 20, None, None, 1, 4, 2, 128, 128, 128, 1, -1, -1, 0.125, 1, None]
+    assert L.fa_bwd_stage(stage, *args) == INVALID
+
+
+def test_bwd_stage_validates_like_fa_bwd(L):
+    args = [FAKE[i] for i in range(10)] + [16, None, None, 1, 4, 2, 128, 128, 128, 1, -1, -1, 0.125, 1, None]
+    for stage in range(3):
+        assert L.fa_bwd_stage(stage, *args) == WORKSPACE
 
 
 def test_workspace_size(L):
