@@ -21,9 +21,16 @@ FLAGS = [
 ]
 
 
+# Kernel sources only: they never form a NaN (masked scores are -inf and every
+# -inf - -inf is guarded), so the max reductions need no NaN canonicalisation.
+# The C-ABI front end keeps full IEEE semantics (it rejects NaN scales).
+KERNEL_FLAGS = ["-fno-honor-nans"]
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    extra = KERNEL_FLAGS if src.endswith(".hip") else []
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

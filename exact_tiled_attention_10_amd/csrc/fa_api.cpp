@@ -60,7 +60,13 @@ int check_arch() {
     return ok ? FA_OK : FA_ERR_ARCH;
 }
 
-float log2e_scaled(float s) { return (float)((double)s * 1.4426950408889634074); }
+// softmax_scale * log2(e), at least the smallest normal float: keeps -inf
+// scores at -inf (exp2 -> exact 0) when softmax_scale == 0, where any finite
+// score still maps to exp2(~0) = 1.
+float log2e_scaled(float s) {
+    const float c = (float)((double)s * 1.4426950408889634074);
+    return c < 1.17549435e-38f ? 1.17549435e-38f : c;
+}
 
 }  // namespace
 

@@ -1,11 +1,11 @@
 // Forward of exact tiled attention on gfx950.
 //
-// One workgroup = one (batch, query head) and a tile of BM = 256 query rows;
-// four waves, each owning 64 rows as two 32-row column blocks.  The kernel
-// streams the visible K/V tiles (BN = 64 keys) through two LDS buffers: while
-// the waves compute on one buffer, the next tile's global loads are in flight
-// into registers and are written to the other buffer afterwards (the
-// asynchronous double buffering of the FlashAttention-2 overview page,
+// One workgroup = one (batch, query head) and a tile of BM = 32 * QB * NW
+// query rows; NW waves, each owning QB column blocks of 32 rows.  The kernel
+// streams the visible K/V tiles (BN keys each) through two LDS buffers: while
+// the waves compute on one buffer, the next tile is in flight to the other --
+// K by direct global -> LDS loads, V through registers, transposed on the way
+// (the asynchronous double buffering of the FlashAttention-2 overview page,
 // lshu.cn/news/55956, section 2.2, third innovation).  Per tile and wave:
 //
 //   S^T = K Q^T            (keys x queries; Q^T held in registers)
@@ -23,10 +23,12 @@
 // row max exceeds it by more than 2^kLazyLog2 in p (log2 units); below that
 // the factors exp(s - m) stay <= 2^kLazyLog2, far from fp32 / fp16 overflow,
 // and the final O = acc / l and LSE = m + ln l are the same numbers.  This
-// skips the rescale of the 64..128 accumulator registers on almost every
-// tile.
-#include <type_traits>
-
+// skips the rescale of the accumulator registers on almost every tile.
+//
+// Masked scores are set to -inf before the exponent; the host clamps
+// scale*log2(e) to at least the smallest normal float, so -inf * c stays -inf
+// and exp2 gives an exact 0 even for softmax_scale == 0 (where every finite
+// score then maps to exp2(0) = 1, the uniform weights that scale means).
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -34,106 +36,59 @@ namespace fa {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kQB = 2;                  // 32-row query blocks per wave
-constexpr int kBM = 32 * kQB * kWaves;  // query rows per workgroup
-constexpr int kBN = 64;                 // keys per tile
-constexpr int kKB = kBN / 32;           // 32-key blocks per tile
 constexpr float kLazyLog2 = 8.0f;
 
-template <int D>
-struct FwdSmem {
-    static constexpr int kStride = D + 8;      // K rows, 16-bit elements (16 B pad)
-    static constexpr int vStride = kBN + 8;    // V^T rows (one per d), 16-bit elements
-    static constexpr int kElems = kBN * kStride;
+template <int D, int NW, int BN>
+struct FwdCfg {
+    static constexpr int kThreads = 64 * NW;
+    // K tile: BN rows of D 16-bit values, no padding; the 16-byte chunk c of
+    // row r sits at slot c ^ (r % CPR), so the 32 rows one MFMA operand read
+    // touches fall in distinct bank groups.  It is filled by direct
+    // global -> LDS loads, each writing 1 KiB (64 lanes x 16 B) in lane order.
+    static constexpr int CPR = D / 8;
+    static constexpr int kElems = BN * D;
+    static constexpr int kDmaBlocks = BN * D * 2 / 1024;
+    static constexpr int kDmaPerWave = kDmaBlocks / NW;
+    static constexpr int kRowsPerBlock = 1024 / (D * 2);
+    // V^T tile: D rows (one per d) of BN keys in the permuted key order, padded
+    // by 16 bytes; written from registers as 2-key x 8-d pieces.
+    static constexpr int vStride = BN + 8;
     static constexpr int vElems = D * vStride;
+    static constexpr int vItems = (BN / 2) * (D / 8);
+    static constexpr int vPieces = vItems / kThreads;
     static constexpr int stageElems = kElems + vElems;
     static constexpr int bytes = 2 * stageElems * 2;
+    static_assert(kDmaBlocks % NW == 0, "K tile must split evenly into 1 KiB blocks per wave");
+    static_assert(vItems % kThreads == 0, "V tile must split evenly over the threads");
+    static_assert((BN / 16) * (D / 64) == NW * vPieces, "V piece blocks must cover the tile");
 };
 
-template <int D>
-struct KVStage {
-    // K: 64 rows x D, as (row, 16-byte chunk) pieces spread over the threads.
-    static constexpr int kChunksPerRow = D / 8;
-    static constexpr int kPieces = kBN * kChunksPerRow / kThreads;  // per thread
-    // V: 4-key x 8-d pieces, transposed on the way to LDS.
-    static constexpr int vItems = (kBN / 4) * (D / 8);
-    u32x4 k[kPieces];
-    u32x4 v[4];
-};
-
-template <int D>
-__device__ __forceinline__ void load_kv(KVStage<D>& st, const uint16_t* __restrict__ kbase,
-                                        const uint16_t* __restrict__ vbase, int64_t row_stride,
-                                        int key0, int len_k, int tid) {
-    constexpr int CPR = KVStage<D>::kChunksPerRow;
-#pragma unroll
-    for (int p = 0; p < KVStage<D>::kPieces; ++p) {
-        const int c = tid + p * kThreads;
-        const int row = c / CPR, ch = c % CPR;
-        const int key = key0 + row;
-        if (key < len_k)
-            st.k[p] = *(const u32x4*)(kbase + (int64_t)key * row_stride + ch * 8);
-        else
-            st.k[p] = u32x4{0, 0, 0, 0};
-    }
-    if (tid < KVStage<D>::vItems) {
-        const int kc = tid % (kBN / 4), dc = tid / (kBN / 4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int key = key0 + 4 * kc + r;
-            if (key < len_k)
-                st.v[r] = *(const u32x4*)(vbase + (int64_t)key * row_stride + dc * 8);
-            else
-                st.v[r] = u32x4{0, 0, 0, 0};
-        }
-    }
-}
-
-template <int D>
-__device__ __forceinline__ void store_kv(const KVStage<D>& st, uint16_t* ks, uint16_t* vts, int tid) {
-    using SM = FwdSmem<D>;
-    constexpr int CPR = KVStage<D>::kChunksPerRow;
-#pragma unroll
-    for (int p = 0; p < KVStage<D>::kPieces; ++p) {
-        const int c = tid + p * kThreads;
-        const int row = c / CPR, ch = c % CPR;
-        *(u32x4*)(ks + row * SM::kStride + ch * 8) = st.k[p];
-    }
-    if (tid < KVStage<D>::vItems) {
-        const int kc = tid % (kBN / 4), dc = tid / (kBN / 4);
-        u32x2 cols[8];
-        transpose4x8(st.v[0], st.v[1], st.v[2], st.v[3], cols);
-        const int pos = perm_chunk_pos(kc);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            *(u32x2*)(vts + (dc * 8 + e) * SM::vStride + pos) = cols[e];
-    }
-}
-
-template <bool BF16, int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+template <bool BF16, int D, int NW, int QB, int BN, int WPE>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(WPE, WPE)))
 void fwd_kernel(FwdArgs a) {
-    using SM = FwdSmem<D>;
+    using C = FwdCfg<D, NW, BN>;
     constexpr int KS = D / 16;  // k-steps of S over d
     constexpr int DB = D / 32;  // 32-row blocks of O^T over d
+    constexpr int KB = BN / 32; // 32-key blocks per tile
+    constexpr int BM = 32 * QB * NW;
+    constexpr int RW = 32 * QB;  // rows per wave
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches below
     const int r32 = lane & 31, half = lane >> 5;
     const int hb = blockIdx.x;
     const int b = hb / a.heads, h = hb % a.heads;
     const int ntiles = gridDim.y;
     const int qt = a.causal ? (ntiles - 1 - (int)blockIdx.y) : (int)blockIdx.y;
     const Seq s = seq_of(b, a.cu_q, a.cu_k, a.seqlen_q, a.seqlen_k);
-    const int i0 = qt * kBM;
+    const int i0 = qt * BM;
     if (i0 >= s.len_q) return;
     const Mask mk{a.causal, a.left, a.right};
     const int hk = h / (a.heads / a.kv_heads);
 
     const int64_t q_row_stride = (int64_t)a.heads * D;
-    const int64_t kv_row_stride = (int64_t)a.kv_heads * D;
+    const int kv_row_stride = a.kv_heads * D;
     const uint16_t* qbase = (const uint16_t*)a.q + (s.q_start * a.heads + h) * D;
     const uint16_t* kbase = (const uint16_t*)a.k + (s.k_start * a.kv_heads + hk) * D;
     const uint16_t* vbase = (const uint16_t*)a.v + (s.k_start * a.kv_heads + hk) * D;
@@ -142,15 +97,15 @@ void fwd_kernel(FwdArgs a) {
                             : a.lse + ((int64_t)b * a.heads + h) * a.seqlen_q;
 
     // Key range of the whole workgroup, as whole tiles.
-    const int i_last = min(i0 + kBM, s.len_q) - 1;
+    const int i_last = min(i0 + BM, s.len_q) - 1;
     const int key_lo = mk.lo_of(i0, s);
     const int key_hi = mk.hi_of(i_last, s);  // inclusive
-    const int t_lo = key_lo / kBN;
-    const int t_hi = key_hi >= key_lo ? key_hi / kBN + 1 : t_lo;
+    const int t_lo = key_lo / BN;
+    const int t_hi = key_hi >= key_lo ? key_hi / BN + 1 : t_lo;
 
-    // This wave's rows and the key range any of them can see.
-    const int wq0 = i0 + 64 * wave;
-    const int wq1 = min(wq0 + 64, s.len_q) - 1;
+    // This wave's rows and the key range any of them can see (all uniform).
+    const int wq0 = i0 + RW * wave;
+    const int wq1 = min(wq0 + RW, s.len_q) - 1;
     const bool wave_live = wq0 < s.len_q;
     const int w_key_lo = wave_live ? mk.lo_of(wq0, s) : 0;
     const int w_key_hi = wave_live ? mk.hi_of(wq1, s) : -1;
@@ -159,150 +114,225 @@ void fwd_kernel(FwdArgs a) {
     const int w_full_hi = wave_live ? mk.hi_of(wq0, s) : -1;
 
     // Q^T fragments (B operand of S^T = K Q^T), resident for the whole loop.
-    u32x4 qf[kQB][KS];
+    u32x4 qf[QB][KS];
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
         const int row = wq0 + 32 * qb + r32;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            if (row < s.len_q)
-                qf[qb][ks] = *(const u32x4*)(qbase + (int64_t)row * q_row_stride + ks * 16 + 8 * half);
-            else
-                qf[qb][ks] = u32x4{0, 0, 0, 0};
-        }
+        for (int ks = 0; ks < KS; ++ks)
+            qf[qb][ks] = row < s.len_q
+                             ? *(const u32x4*)(qbase + (int64_t)row * q_row_stride + ks * 16 + 8 * half)
+                             : u32x4{0, 0, 0, 0};
     }
 
-    f32x16 acc[DB][kQB];
+    // ---- per-thread constant offsets -----------------------------------------------
+    // K direct loads: block bi = wave * kDmaPerWave + i covers rows
+    // bi * kRowsPerBlock + lane / CPR; lane's slot lane % CPR holds chunk slot ^ (row % CPR).
+    int k_goff[C::kDmaPerWave];  // element offset inside the tile (row * stride + chunk * 8)
+    int k_row[C::kDmaPerWave];
+#pragma unroll
+    for (int i = 0; i < C::kDmaPerWave; ++i) {
+        const int bi = wave * C::kDmaPerWave + i;
+        const int row = bi * C::kRowsPerBlock + lane / C::CPR;
+        const int slot = lane % C::CPR;
+        k_row[i] = row;
+        k_goff[i] = row * kv_row_stride + ((slot ^ (row % C::CPR)) * 8);
+    }
+    // V pieces: 8 key pairs x 8 d-chunks per wave block; lane % 8 -> key pair, lane / 8 -> d-chunk.
+    int v_kp[C::vPieces], v_dc[C::vPieces];
+#pragma unroll
+    for (int p = 0; p < C::vPieces; ++p) {
+        const int blk = wave * C::vPieces + p;
+        const int nkpb = BN / 16;
+        v_kp[p] = (blk % nkpb) * 8 + (lane & 7);
+        v_dc[p] = (blk / nkpb) * 8 + (lane >> 3);
+    }
+    // MFMA operand reads
+    int k_rd[KB][KS];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int row = kb * 32 + r32, ch = 2 * ks + half;
+            k_rd[kb][ks] = row * D + ((ch ^ (row % C::CPR)) * 8);
+        }
+    const int v_rd = r32 * C::vStride + 8 * half;
+
+    f32x16 acc[DB][QB];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) acc[db][qb] = f32x16{0};
-    float m_run[kQB], l_part[kQB];
+        for (int qb = 0; qb < QB; ++qb) acc[db][qb] = f32x16{0};
+    float m_run[QB], l_part[QB];
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) { m_run[qb] = kNegInf; l_part[qb] = 0.f; }
+    for (int qb = 0; qb < QB; ++qb) { m_run[qb] = kNegInf; l_part[qb] = 0.f; }
     const float c = a.scale_log2;
 
-    // One K/V tile for this wave; `masked` selects the edge-tile variant.
-    auto tile = [&](auto masked, const int key0, const uint16_t* ks_lds, const uint16_t* vt_lds) {
-            // ---- S^T = K Q^T -------------------------------------------------
-            f32x16 sacc[kKB][kQB];
+    u32x4 vreg[C::vPieces][2];
+    // Issue the loads of tile t: K straight into LDS buffer `buf`, V into registers.
+    auto issue_tile = [&](int t, int buf) {
+        const int key0 = t * BN;
+        const uint16_t* kt = kbase + (int64_t)key0 * kv_row_stride;
+        uint16_t* kl = smem + buf * C::stageElems;
+        const bool tail = key0 + BN > s.len_k;  // uniform
+        const int last = s.len_k - 1 - key0;
 #pragma unroll
-            for (int kb = 0; kb < kKB; ++kb)
+        for (int i = 0; i < C::kDmaPerWave; ++i) {
+            int off = k_goff[i];
+            if (tail && k_row[i] > last) off += (last - k_row[i]) * kv_row_stride;  // clamp to the last key
+            __builtin_amdgcn_global_load_lds(
+                (const void*)(kt + off),
+                (__attribute__((address_space(3))) void*)(kl + (wave * C::kDmaPerWave + i) * 512), 16, 0, 0);
+        }
+        const uint16_t* vt = vbase + (int64_t)key0 * kv_row_stride;
 #pragma unroll
-                for (int qb = 0; qb < kQB; ++qb) sacc[kb][qb] = f32x16{0};
+        for (int p = 0; p < C::vPieces; ++p)
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                u32x4 kf[kKB];
-#pragma unroll
-                for (int kb = 0; kb < kKB; ++kb)
-                    kf[kb] = *(const u32x4*)(ks_lds + (kb * 32 + r32) * SM::kStride + ks * 16 + 8 * half);
-#pragma unroll
-                for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-                    for (int qb = 0; qb < kQB; ++qb)
-                        sacc[kb][qb] = mfma32<BF16>(kf[kb], qf[qb][ks], sacc[kb][qb]);
+            for (int r = 0; r < 2; ++r) {
+                int row = 2 * v_kp[p] + r;
+                if (tail) row = min(row, last);
+                vreg[p][r] = *(const u32x4*)(vt + row * kv_row_stride + v_dc[p] * 8);
             }
-            // ---- mask (edge tiles only) ---------------------------------------
-            if constexpr (decltype(masked)::value) {
+    };
+    // V registers -> transposed, permuted V^T tile of buffer `buf`.
+    auto store_v = [&](int buf) {
+        uint16_t* vl = smem + buf * C::stageElems + C::kElems;
 #pragma unroll
-                for (int qb = 0; qb < kQB; ++qb) {
-                    const int qi = wq0 + 32 * qb + r32;
-                    const int lo = mk.lo_of(qi, s), hi = mk.hi_of(qi, s);
+        for (int p = 0; p < C::vPieces; ++p) {
+            const int pos = perm_chunk_pos(v_kp[p] >> 1) + 2 * (v_kp[p] & 1);
 #pragma unroll
-                    for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            const int key = key0 + kb * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-                            if (key < lo || key > hi) sacc[kb][qb][i] = kNegInf;
-                        }
-                }
+            for (int w = 0; w < 4; ++w) {
+                // element 2w and 2w+1 of both keys
+                const uint32_t lo = __builtin_amdgcn_perm(vreg[p][1][w], vreg[p][0][w], 0x05040100u);
+                const uint32_t hi = __builtin_amdgcn_perm(vreg[p][1][w], vreg[p][0][w], 0x07060302u);
+                *(uint32_t*)(vl + (v_dc[p] * 8 + 2 * w) * C::vStride + pos) = lo;
+                *(uint32_t*)(vl + (v_dc[p] * 8 + 2 * w + 1) * C::vStride + pos) = hi;
             }
-            // ---- online softmax ------------------------------------------------
-            uint32_t pk[kKB][kQB][8];
+        }
+    };
+
+    // One K/V tile on LDS buffer `buf` for this wave.
+    auto compute_tile = [&](int t, int buf) {
+        const int key0 = t * BN;
+        if (!(wave_live && key0 <= w_key_hi && key0 + BN - 1 >= w_key_lo)) return;
+        const uint16_t* ks_lds = smem + buf * C::stageElems;
+        const uint16_t* vt_lds = ks_lds + C::kElems;
+        // ---- S^T = K Q^T -------------------------------------------------
+        f32x16 sacc[KB][QB];
 #pragma unroll
-            for (int qb = 0; qb < kQB; ++qb) {
-                float mx = kNegInf;
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int kb = 0; kb < kKB; ++kb)
+            for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = f32x16{0};
+        // K fragments are read one k-step ahead of the MFMAs that use them.
+        u32x4 kf[2][KB];
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][qb][i]);
-                mx = max_halves(mx);
-                const float m_old = m_run[qb];
-                const bool up = mx > m_old && (m_old == kNegInf || (mx - m_old) * c > kLazyLog2);
-                if (__builtin_amdgcn_ballot_w64(up)) {
-                    const float alpha = !up ? 1.f : (m_old == kNegInf ? 0.f : fast_exp2((m_old - mx) * c));
-                    if (up) m_run[qb] = mx;
-                    l_part[qb] *= alpha;
+        for (int kb = 0; kb < KB; ++kb) kf[0][kb] = *(const u32x4*)(ks_lds + k_rd[kb][0]);
 #pragma unroll
-                    for (int db = 0; db < DB; ++db) acc[db][qb] *= alpha;
-                }
-                const float mc = m_run[qb] == kNegInf ? 0.f : m_run[qb] * c;
-                float lsum = 0.f;
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 1 < KS) {
 #pragma unroll
-                for (int kb = 0; kb < kKB; ++kb)
+                for (int kb = 0; kb < KB; ++kb) kf[(ks + 1) & 1][kb] = *(const u32x4*)(ks_lds + k_rd[kb][ks + 1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of these MFMAs
 #pragma unroll
-                    for (int i = 0; i < 16; i += 2) {
-                        float p0 = fast_exp2(__builtin_fmaf(sacc[kb][qb][i], c, -mc));
-                        float p1 = fast_exp2(__builtin_fmaf(sacc[kb][qb][i + 1], c, -mc));
-                        if constexpr (decltype(masked)::value) {
-                            // exact zero for masked keys, also when scale == 0
-                            p0 = sacc[kb][qb][i] == kNegInf ? 0.f : p0;
-                            p1 = sacc[kb][qb][i + 1] == kNegInf ? 0.f : p1;
-                        }
-                        lsum += p0 + p1;
-                        pk[kb][qb][i / 2] = pack2<BF16>(p0, p1);
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = mfma32<BF16>(kf[ks & 1][kb], qf[qb][ks], sacc[kb][qb]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // ---- mask (edge tiles only; uniform branch) --------------------------
+        if (key0 < w_full_lo || key0 + BN - 1 > w_full_hi) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const int qi = wq0 + 32 * qb + r32;
+                const int lo = mk.lo_of(qi, s) - key0, hi = mk.hi_of(qi, s) - key0;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int kk = kb * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+                        sacc[kb][qb][i] = (kk < lo || kk > hi) ? kNegInf : sacc[kb][qb][i];
                     }
-                l_part[qb] += lsum;
             }
-            // ---- O^T += V^T P^T --------------------------------------------------
+        }
+        // V^T fragments of the first key step: read now, used after the softmax.
+        u32x4 vf0[DB];
 #pragma unroll
-            for (int kk = 0; kk < kBN / 16; ++kk) {
-                const int kb = kk / 2, hs = kk % 2;
-                u32x4 pb[kQB];
+        for (int db = 0; db < DB; ++db) vf0[db] = *(const u32x4*)(vt_lds + db * 32 * C::vStride + v_rd);
+        // ---- online softmax ------------------------------------------------
+        uint32_t pk[KB][QB][8];
 #pragma unroll
-                for (int qb = 0; qb < kQB; ++qb)
-                    pb[qb] = u32x4{pk[kb][qb][4 * hs], pk[kb][qb][4 * hs + 1],
-                                   pk[kb][qb][4 * hs + 2], pk[kb][qb][4 * hs + 3]};
+        for (int qb = 0; qb < QB; ++qb) {
+            float mx = kNegInf;
 #pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const u32x4 vf = *(const u32x4*)(vt_lds + (db * 32 + r32) * SM::vStride + kk * 16 + 8 * half);
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                    for (int qb = 0; qb < kQB; ++qb) acc[db][qb] = mfma32<BF16>(vf, pb[qb], acc[db][qb]);
+                for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[kb][qb][i], sacc[kb][qb][i + 1]));
+            mx = max_halves(mx);
+            const float m_old = m_run[qb];
+            const bool up = mx > m_old && (m_old == kNegInf || (mx - m_old) * c > kLazyLog2);
+            if (__builtin_amdgcn_ballot_w64(up)) {
+                const float alpha = !up ? 1.f : (m_old == kNegInf ? 0.f : fast_exp2((m_old - mx) * c));
+                m_run[qb] = up ? mx : m_old;
+                l_part[qb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) acc[db][qb] *= alpha;
+            }
+            const float mc = m_run[qb] == kNegInf ? 0.f : m_run[qb] * c;
+            float lsum = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; i += 2) {
+                    const float p0 = fast_exp2(__builtin_fmaf(sacc[kb][qb][i], c, -mc));
+                    const float p1 = fast_exp2(__builtin_fmaf(sacc[kb][qb][i + 1], c, -mc));
+                    lsum += p0 + p1;
+                    pk[kb][qb][i / 2] = pack2<BF16>(p0, p1);
+                }
+            l_part[qb] += lsum;
+        }
+        // ---- O^T += V^T P^T --------------------------------------------------
+#pragma unroll
+        for (int kk = 0; kk < BN / 16; ++kk) {
+            const int kb = kk / 2, hs = kk % 2;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const u32x4 vf = kk == 0 ? vf0[db] : *(const u32x4*)(vt_lds + db * 32 * C::vStride + v_rd + kk * 16);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    const u32x4 pb = u32x4{pk[kb][qb][4 * hs], pk[kb][qb][4 * hs + 1],
+                                           pk[kb][qb][4 * hs + 2], pk[kb][qb][4 * hs + 3]};
+                    acc[db][qb] = mfma32<BF16>(vf, pb, acc[db][qb]);
                 }
             }
+        }
+    };
+
+    // One pipeline step: prefetch tile t+1 into the other buffer, compute tile t.
+    auto step = [&](int t, int buf) {
+        const bool has_next = t + 1 < t_hi;
+        if (has_next) issue_tile(t + 1, buf ^ 1);
+        compute_tile(t, buf);
+        if (has_next) store_v(buf ^ 1);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): direct K loads have landed
+        __syncthreads();
     };
 
     if (t_lo < t_hi) {
-        KVStage<D> st;
-        load_kv<D>(st, kbase, vbase, kv_row_stride, t_lo * kBN, s.len_k, tid);
-        store_kv<D>(st, smem, smem + SM::kElems, tid);
+        issue_tile(t_lo, 0);
+        store_v(0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
-
-        for (int t = t_lo; t < t_hi; ++t) {
-            const int buf = (t - t_lo) & 1;
-            const uint16_t* ks_lds = smem + buf * SM::stageElems;
-            const uint16_t* vt_lds = ks_lds + SM::kElems;
-            const bool has_next = t + 1 < t_hi;
-            if (has_next) load_kv<D>(st, kbase, vbase, kv_row_stride, (t + 1) * kBN, s.len_k, tid);
-
-            const int key0 = t * kBN;
-            const bool wave_on = wave_live && key0 <= w_key_hi && key0 + kBN - 1 >= w_key_lo;
-            if (wave_on) {
-                if (key0 < w_full_lo || key0 + kBN - 1 > w_full_hi)
-                    tile(std::true_type{}, key0, ks_lds, vt_lds);
-                else
-                    tile(std::false_type{}, key0, ks_lds, vt_lds);
-            }
-            if (has_next) store_kv<D>(st, smem + (buf ^ 1) * SM::stageElems,
-                                      smem + (buf ^ 1) * SM::stageElems + SM::kElems, tid);
-            __syncthreads();
+        for (int t = t_lo; t < t_hi; t += 2) {
+            step(t, 0);
+            if (t + 1 < t_hi) step(t + 1, 1);
         }
     }
 
     // ---- epilogue: O = acc / l, LSE = scale * m + ln l ------------------------------
     if (!wave_live) return;
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
         const int row = wq0 + 32 * qb + r32;
         const float l = sum_halves(l_part[qb]);
         const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -323,24 +353,52 @@ void fwd_kernel(FwdArgs a) {
     }
 }
 
-template <bool BF16, int D>
+template <bool BF16, int D, int NW, int QB, int BN, int WPE>
 int launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
-    const int ntiles = (a.seqlen_q + kBM - 1) / kBM;
+    constexpr int BM = 32 * QB * NW;
+    using C = FwdCfg<D, NW, BN>;
+    const int ntiles = (a.seqlen_q + BM - 1) / BM;
     if (ntiles == 0 || a.batch == 0) return 0;
+    auto kern = fwd_kernel<BF16, D, NW, QB, BN, WPE>;
     static const bool smem_ok =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(fwd_kernel<BF16, D>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, FwdSmem<D>::bytes) == hipSuccess;
+        hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            C::bytes) == hipSuccess;
     if (!smem_ok) return 1;
     dim3 grid(a.batch * a.heads, ntiles);
-    hipLaunchKernelGGL((fwd_kernel<BF16, D>), grid, dim3(kThreads), FwdSmem<D>::bytes, stream, a);
+    hipLaunchKernelGGL(kern, grid, dim3(C::kThreads), C::bytes, stream, a);
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }
+
+// Launch shapes (measured on MI355X, bf16 causal): 8 waves of 32 query rows
+// (two waves per SIMD, all state in arch VGPRs) beat 4 waves of 64 rows, whose
+// accumulators spill into AGPR traffic; 64-key tiles suit d = 128, 128-key
+// tiles d = 64.  Overridable at build time for tuning.
+#ifndef FA_FWD_NW
+#define FA_FWD_NW 8
+#endif
+#ifndef FA_FWD_QB
+#define FA_FWD_QB 1
+#endif
+#ifndef FA_FWD_BN128
+#define FA_FWD_BN128 64
+#endif
+#ifndef FA_FWD_BN64
+#define FA_FWD_BN64 128
+#endif
+#ifndef FA_FWD_WPE
+#define FA_FWD_WPE 2
+#endif
 
 }  // namespace
 
 int launch_fwd(const FwdArgs& a, hipStream_t stream) {
-    if (a.bf16) return a.head_dim == 128 ? launch_fwd_t<true, 128>(a, stream) : launch_fwd_t<true, 64>(a, stream);
-    return a.head_dim == 128 ? launch_fwd_t<false, 128>(a, stream) : launch_fwd_t<false, 64>(a, stream);
+    constexpr int NW = FA_FWD_NW, QB = FA_FWD_QB, W = FA_FWD_WPE;
+    constexpr int B1 = FA_FWD_BN128, B2 = FA_FWD_BN64;
+    if (a.bf16)
+        return a.head_dim == 128 ? launch_fwd_t<true, 128, NW, QB, B1, W>(a, stream)
+                                 : launch_fwd_t<true, 64, NW, QB, B2, W>(a, stream);
+    return a.head_dim == 128 ? launch_fwd_t<false, 128, NW, QB, B1, W>(a, stream)
+                             : launch_fwd_t<false, 64, NW, QB, B2, W>(a, stream);
 }
 
 }  // namespace fa
