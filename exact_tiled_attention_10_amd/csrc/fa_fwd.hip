@@ -3,16 +3,17 @@
 // One workgroup = one (batch, query head) and a tile of BM = 32 * QB * NW
 // query rows; NW waves, each owning QB column blocks of 32 rows.  The kernel
 // streams the visible K/V tiles (BN keys each) through two LDS buffers: while
-// the waves compute on one buffer, the next tile is in flight to the other --
-// K by direct global -> LDS loads, V through registers, transposed on the way
-// (the asynchronous double buffering of the FlashAttention-2 overview page,
+// the waves compute on one buffer, the next tile is in flight to the other by
+// direct global -> LDS loads that bypass registers entirely (the
+// asynchronous double buffering of the FlashAttention-2 overview page,
 // lshu.cn/news/55956, section 2.2, third innovation).  Per tile and wave:
 //
 //   S^T = K Q^T            (keys x queries; Q^T held in registers)
 //   online softmax          per query column: running max m and sum l
 //                           (same page, section 2.2, second innovation)
 //   O^T += V^T P^T          (d x queries; P^T taken straight from the S^T
-//                           registers, V^T read from a transposed LDS copy)
+//                           registers, V^T gathered from the row-major V tile
+//                           by the transposing LDS reads of gfx950)
 //
 // The N x N score matrix never leaves registers (first innovation, tiled
 // fusion).  Working in the transposed orientation puts one query per lane
@@ -41,27 +42,29 @@ constexpr float kLazyLog2 = 8.0f;
 template <int D, int NW, int BN>
 struct FwdCfg {
     static constexpr int kThreads = 64 * NW;
-    // K tile: BN rows of D 16-bit values, no padding; the 16-byte chunk c of
-    // row r sits at slot c ^ (r % CPR), so the 32 rows one MFMA operand read
-    // touches fall in distinct bank groups.  It is filled by direct
-    // global -> LDS loads, each writing 1 KiB (64 lanes x 16 B) in lane order.
+    // K and V tiles: BN rows (keys) of D 16-bit values each, unpadded; the
+    // 16-byte chunk c of row r sits at slot c ^ swz(r).  Both are filled by
+    // direct global -> LDS loads, each writing 1 KiB (64 lanes x 16 B) in lane
+    // order, so a load instruction covers 1024 / (2 D) whole rows.
     static constexpr int CPR = D / 8;
-    static constexpr int kElems = BN * D;
+    static constexpr int tileElems = BN * D;
     static constexpr int kDmaBlocks = BN * D * 2 / 1024;
     static constexpr int kDmaPerWave = kDmaBlocks / NW;
     static constexpr int kRowsPerBlock = 1024 / (D * 2);
-    // V^T tile: D rows (one per d) of BN keys in the permuted key order, padded
-    // by 16 bytes; written from registers as 2-key x 8-d pieces.
-    static constexpr int vStride = BN + 8;
-    static constexpr int vElems = D * vStride;
-    static constexpr int vItems = (BN / 2) * (D / 8);
-    static constexpr int vPieces = vItems / kThreads;
-    static constexpr int stageElems = kElems + vElems;
+    static constexpr int stageElems = 2 * tileElems;  // K then V
     static constexpr int bytes = 2 * stageElems * 2;
-    static_assert(kDmaBlocks % NW == 0, "K tile must split evenly into 1 KiB blocks per wave");
-    static_assert(vItems % kThreads == 0, "V tile must split evenly over the threads");
-    static_assert((BN / 16) * (D / 64) == NW * vPieces, "V piece blocks must cover the tile");
+    static_assert(kDmaBlocks % NW == 0, "tiles must split evenly into 1 KiB blocks per wave");
 };
+
+// Chunk swizzle shared by the K and V tiles.  For 16 chunks per row it maps
+// row bits (r%4, (r/4)%4) to chunk bits (hi, lo): the 16 consecutive rows an
+// MFMA operand read touches land in 16 distinct chunk slots, and the 8 rows x
+// 4 chunks a transposed V read touches spread over all 16 slots.
+template <int CPR>
+__device__ __forceinline__ int swz(int row) {
+    if constexpr (CPR == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else return ((row & 3) << 1) | ((row >> 2) & 1);
+}
 
 template <bool BF16, int D, int NW, int QB, int BN, int WPE>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(WPE, WPE)))
@@ -126,37 +129,41 @@ void fwd_kernel(FwdArgs a) {
     }
 
     // ---- per-thread constant offsets -----------------------------------------------
-    // K direct loads: block bi = wave * kDmaPerWave + i covers rows
-    // bi * kRowsPerBlock + lane / CPR; lane's slot lane % CPR holds chunk slot ^ (row % CPR).
-    int k_goff[C::kDmaPerWave];  // element offset inside the tile (row * stride + chunk * 8)
-    int k_row[C::kDmaPerWave];
+    // Direct loads: block bi = wave * kDmaPerWave + i covers rows
+    // bi * kRowsPerBlock + lane / CPR; lane slot lane % CPR receives chunk slot ^ swz(row).
+    int dma_goff[C::kDmaPerWave];  // element offset inside the tile (row * stride + chunk * 8)
+    int dma_row[C::kDmaPerWave];
 #pragma unroll
     for (int i = 0; i < C::kDmaPerWave; ++i) {
         const int bi = wave * C::kDmaPerWave + i;
         const int row = bi * C::kRowsPerBlock + lane / C::CPR;
         const int slot = lane % C::CPR;
-        k_row[i] = row;
-        k_goff[i] = row * kv_row_stride + ((slot ^ (row % C::CPR)) * 8);
+        dma_row[i] = row;
+        dma_goff[i] = row * kv_row_stride + ((slot ^ swz<C::CPR>(row)) * 8);
     }
-    // V pieces: 8 key pairs x 8 d-chunks per wave block; lane % 8 -> key pair, lane / 8 -> d-chunk.
-    int v_kp[C::vPieces], v_dc[C::vPieces];
+    // S^T operand reads of K: lane (r32, half) reads row kb*32 + r32, chunk 2 ks + half.
+    int k_rd[KS];
 #pragma unroll
-    for (int p = 0; p < C::vPieces; ++p) {
-        const int blk = wave * C::vPieces + p;
-        const int nkpb = BN / 16;
-        v_kp[p] = (blk % nkpb) * 8 + (lane & 7);
-        v_dc[p] = (blk / nkpb) * 8 + (lane >> 3);
-    }
-    // MFMA operand reads
-    int k_rd[KB][KS];
+    for (int ks = 0; ks < KS; ++ks) k_rd[ks] = r32 * D + (((2 * ks + half) ^ swz<C::CPR>(r32)) * 8);
+    // V^T operand reads (transposing LDS reads, 4 x 16-bit per lane each): in
+    // every 16-lane group, lane 4r+c receives element c of the 8-byte rows
+    // addressed by lanes r, r+4, r+8, r+12.  Lane j of group g therefore points
+    // at key row 8*inst + 4*(g/2) + j/4 of the 16-key step and at d columns
+    // 32*db + 16*(g%2) + 4*(j%4) .. +3; the receiver's element 4*inst + j/4 is
+    // then key ROWPERM(g/2, 4*inst + j/4) of the step, as the P^T operand expects.
+    int v_rd[2][DB];
+    {
+        const int g = lane >> 4, j = lane & 15;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+        for (int inst = 0; inst < 2; ++inst) {
+            const int rr = 8 * inst + 4 * (g >> 1) + (j >> 2);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int row = kb * 32 + r32, ch = 2 * ks + half;
-            k_rd[kb][ks] = row * D + ((ch ^ (row % C::CPR)) * 8);
+            for (int db = 0; db < DB; ++db) {
+                const int col = 32 * db + 16 * (g & 1) + 4 * (j & 3);
+                v_rd[inst][db] = rr * D + (((col >> 3) ^ swz<C::CPR>(rr)) * 8) + (col & 7);
+            }
         }
-    const int v_rd = r32 * C::vStride + 8 * half;
+    }
 
     f32x16 acc[DB][QB];
 #pragma unroll
@@ -168,46 +175,22 @@ void fwd_kernel(FwdArgs a) {
     for (int qb = 0; qb < QB; ++qb) { m_run[qb] = kNegInf; l_part[qb] = 0.f; }
     const float c = a.scale_log2;
 
-    u32x4 vreg[C::vPieces][2];
-    // Issue the loads of tile t: K straight into LDS buffer `buf`, V into registers.
+    // Issue the loads of tile t straight into LDS buffer `buf` (K, then V).
     auto issue_tile = [&](int t, int buf) {
         const int key0 = t * BN;
-        const uint16_t* kt = kbase + (int64_t)key0 * kv_row_stride;
-        uint16_t* kl = smem + buf * C::stageElems;
         const bool tail = key0 + BN > s.len_k;  // uniform
         const int last = s.len_k - 1 - key0;
+        const int64_t tile_off = (int64_t)key0 * kv_row_stride;
+        uint16_t* kl = smem + buf * C::stageElems;
 #pragma unroll
         for (int i = 0; i < C::kDmaPerWave; ++i) {
-            int off = k_goff[i];
-            if (tail && k_row[i] > last) off += (last - k_row[i]) * kv_row_stride;  // clamp to the last key
-            __builtin_amdgcn_global_load_lds(
-                (const void*)(kt + off),
-                (__attribute__((address_space(3))) void*)(kl + (wave * C::kDmaPerWave + i) * 512), 16, 0, 0);
-        }
-        const uint16_t* vt = vbase + (int64_t)key0 * kv_row_stride;
-#pragma unroll
-        for (int p = 0; p < C::vPieces; ++p)
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                int row = 2 * v_kp[p] + r;
-                if (tail) row = min(row, last);
-                vreg[p][r] = *(const u32x4*)(vt + row * kv_row_stride + v_dc[p] * 8);
-            }
-    };
-    // V registers -> transposed, permuted V^T tile of buffer `buf`.
-    auto store_v = [&](int buf) {
-        uint16_t* vl = smem + buf * C::stageElems + C::kElems;
-#pragma unroll
-        for (int p = 0; p < C::vPieces; ++p) {
-            const int pos = perm_chunk_pos(v_kp[p] >> 1) + 2 * (v_kp[p] & 1);
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                // element 2w and 2w+1 of both keys
-                const uint32_t lo = __builtin_amdgcn_perm(vreg[p][1][w], vreg[p][0][w], 0x05040100u);
-                const uint32_t hi = __builtin_amdgcn_perm(vreg[p][1][w], vreg[p][0][w], 0x07060302u);
-                *(uint32_t*)(vl + (v_dc[p] * 8 + 2 * w) * C::vStride + pos) = lo;
-                *(uint32_t*)(vl + (v_dc[p] * 8 + 2 * w + 1) * C::vStride + pos) = hi;
-            }
+            int off = dma_goff[i];
+            if (tail && dma_row[i] > last) off += (last - dma_row[i]) * kv_row_stride;  // clamp to the last key
+            uint16_t* dst = kl + (wave * C::kDmaPerWave + i) * 512;
+            __builtin_amdgcn_global_load_lds((const void*)(kbase + tile_off + off),
+                                             (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(vbase + tile_off + off),
+                                             (__attribute__((address_space(3))) void*)(dst + C::tileElems), 16, 0, 0);
         }
     };
 
@@ -216,7 +199,7 @@ void fwd_kernel(FwdArgs a) {
         const int key0 = t * BN;
         if (!(wave_live && key0 <= w_key_hi && key0 + BN - 1 >= w_key_lo)) return;
         const uint16_t* ks_lds = smem + buf * C::stageElems;
-        const uint16_t* vt_lds = ks_lds + C::kElems;
+        const uint16_t* vs_lds = ks_lds + C::tileElems;
         // ---- S^T = K Q^T -------------------------------------------------
         f32x16 sacc[KB][QB];
 #pragma unroll
@@ -226,12 +209,12 @@ void fwd_kernel(FwdArgs a) {
         // K fragments are read one k-step ahead of the MFMAs that use them.
         u32x4 kf[2][KB];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) kf[0][kb] = *(const u32x4*)(ks_lds + k_rd[kb][0]);
+        for (int kb = 0; kb < KB; ++kb) kf[0][kb] = *(const u32x4*)(ks_lds + kb * 32 * D + k_rd[0]);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             if (ks + 1 < KS) {
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) kf[(ks + 1) & 1][kb] = *(const u32x4*)(ks_lds + k_rd[kb][ks + 1]);
+                for (int kb = 0; kb < KB; ++kb) kf[(ks + 1) & 1][kb] = *(const u32x4*)(ks_lds + kb * 32 * D + k_rd[ks + 1]);
             }
             __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of these MFMAs
 #pragma unroll
@@ -256,9 +239,17 @@ void fwd_kernel(FwdArgs a) {
             }
         }
         // V^T fragments of the first key step: read now, used after the softmax.
+        auto read_vt = [&](int kk, int db) {
+            typedef short s16x4 __attribute__((ext_vector_type(4)));
+            typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs_lds + kk * 16 * D + v_rd[0][db]));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs_lds + kk * 16 * D + v_rd[1][db]));
+            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+            return u32x4{l2.x, l2.y, h2.x, h2.y};
+        };
         u32x4 vf0[DB];
 #pragma unroll
-        for (int db = 0; db < DB; ++db) vf0[db] = *(const u32x4*)(vt_lds + db * 32 * C::vStride + v_rd);
+        for (int db = 0; db < DB; ++db) vf0[db] = read_vt(0, db);
         // ---- online softmax ------------------------------------------------
         uint32_t pk[KB][QB][8];
 #pragma unroll
@@ -297,7 +288,7 @@ void fwd_kernel(FwdArgs a) {
             const int kb = kk / 2, hs = kk % 2;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const u32x4 vf = kk == 0 ? vf0[db] : *(const u32x4*)(vt_lds + db * 32 * C::vStride + v_rd + kk * 16);
+                const u32x4 vf = kk == 0 ? vf0[db] : read_vt(kk, db);
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) {
                     const u32x4 pb = u32x4{pk[kb][qb][4 * hs], pk[kb][qb][4 * hs + 1],
@@ -313,14 +304,12 @@ void fwd_kernel(FwdArgs a) {
         const bool has_next = t + 1 < t_hi;
         if (has_next) issue_tile(t + 1, buf ^ 1);
         compute_tile(t, buf);
-        if (has_next) store_v(buf ^ 1);
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): direct K loads have landed
         __syncthreads();
     };
 
     if (t_lo < t_hi) {
         issue_tile(t_lo, 0);
-        store_v(0);
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
         for (int t = t_lo; t < t_hi; t += 2) {
