@@ -101,7 +101,8 @@ size_t fa_bwd_workspace_size(int batch, int heads, int seqlen_q, int head_dim, i
     if (batch < 0 || heads < 1 || seqlen_q < 0) return 0;
     if (head_dim != 64 && head_dim != 128) return 0;
     if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return 0;
-    const size_t n = (size_t)batch * (size_t)heads * (size_t)seqlen_q * sizeof(float);
+    // two float arrays (D and LSE * log2 e), each one entry per query row and head
+    const size_t n = 2 * (size_t)batch * (size_t)heads * (size_t)seqlen_q * sizeof(float);
     return n > 0 ? n : 4;  // never zero for valid sizes, so a null workspace is an error
 }
 
@@ -134,6 +135,7 @@ int bwd_common(int stage_lo, int stage_hi,
     fa::BwdArgs a;
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
     a.dq = dq; a.dk = dk; a.dv = dv; a.dsum = (float*)workspace;
+    a.lse2 = a.dsum + (size_t)batch * (size_t)heads * (size_t)seqlen_q;
     a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
     a.batch = batch; a.heads = heads; a.kv_heads = kv_heads;
     a.seqlen_q = seqlen_q; a.seqlen_k = seqlen_k; a.head_dim = head_dim;

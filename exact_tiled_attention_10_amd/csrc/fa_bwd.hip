@@ -10,19 +10,20 @@
 //   dQ = scale dS K.
 //
 // Three kernels on one stream:
-//   bwd_rowdot   D_i = dO_i . O_i                         (HBM-bound)
+//   bwd_rowdot   D_i = dO_i . O_i and LSE_i * log2(e) into the workspace
 //   bwd_dkdv     per key tile (outer) and every visible query tile of every
 //                query head of the GQA group (inner): dK, dV accumulated in
 //                registers, no atomics
 //   bwd_dq       per query tile (outer) over the visible key tiles (inner):
 //                the separate dQ accumulation pass, no atomics
-// Both main kernels double-buffer their streamed tiles in LDS like the
-// forward.  Operand orientation follows the MFMA C layout (fa_device.hpp):
-// the dK/dV pass computes S = Q K^T with one key per lane column, so P and dS
-// feed dV^T = dO^T P and dK^T = Q^T dS directly; the dQ pass computes
-// S^T = K Q^T with one query per lane column, so dS^T feeds dQ^T = K^T dS^T.
-#include <type_traits>
-
+// Both main kernels stream their tiles row-major into LDS with direct
+// global -> LDS loads (double-buffered) and build every transposed MFMA
+// operand (dO^T, Q^T, K^T) with the transposing LDS reads of gfx950, so no
+// tile is ever transposed through registers.  Operand orientation follows the
+// MFMA C layout (fa_device.hpp): the dK/dV pass computes S = Q K^T with one key
+// per lane column, so P and dS feed dV^T = dO^T P and dK^T = Q^T dS directly;
+// the dQ pass computes S^T = K Q^T with one query per lane column, so dS^T
+// feeds dQ^T = K^T dS^T.
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -33,7 +34,7 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
-// D_i = dO_i . O_i
+// D_i = dO_i . O_i  and  lse2_i = LSE_i * log2(e)
 // ---------------------------------------------------------------------------
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void bwd_rowdot_kernel(BwdArgs a) {
@@ -68,73 +69,244 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(BwdArgs a) {
             idx = (b * a.heads + h) * a.seqlen_q + i;
         }
         a.dsum[idx] = acc;
+        a.lse2[idx] = a.lse[idx] * kLog2e;  // -inf (a row without keys) stays -inf
     }
 }
 
-// Loads a 64-row x D tile of a row-major [rows, heads, D] tensor as
-// (4-row x 8-column) pieces: thread -> rows 4*rc .. 4*rc+3, columns 8*dc ..
-// 8*dc+7.  Rows outside [0, nrows) read as zero.
-template <int D, int ROWS>
-struct Piece {
-    static constexpr int kRowChunks = ROWS / 4;
-    static constexpr int kItems = kRowChunks * (D / 8);
-    static_assert(kItems <= 256, "one piece per thread");
-    u32x4 r[4];
-    __device__ __forceinline__ void load(const uint16_t* base, int64_t stride, int row0, int nrows, int tid) {
-        if (tid >= kItems) return;
-        const int rc = tid % kRowChunks, dc = tid / kRowChunks;
+// Direct loads of ROWS rows of a [rows, heads, D] tensor (row stride `stride`
+// elements, rows past `last` clamped to it) into a swizzled LDS tile, split
+// over NW waves: block bi = wave * PER + i covers 1024 bytes.
+template <int D, int ROWS, int NW>
+struct TileDma {
+    static constexpr int CPR = D / 8;
+    static constexpr int kBlocks = ROWS * D * 2 / 1024;
+    static constexpr int kPerWave = kBlocks / NW;
+    static constexpr int kRowsPerBlock = 1024 / (D * 2);
+    static_assert(kBlocks % NW == 0, "tile must split evenly into 1 KiB blocks per wave");
+    int goff[kPerWave];
+    int row[kPerWave];
+    __device__ __forceinline__ void init(int wave, int lane, int stride) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int row = row0 + 4 * rc + k;
-            r[k] = row < nrows ? *(const u32x4*)(base + (int64_t)row * stride + dc * 8) : u32x4{0, 0, 0, 0};
+        for (int i = 0; i < kPerWave; ++i) {
+            const int bi = wave * kPerWave + i;
+            const int r = bi * kRowsPerBlock + lane / CPR;
+            const int slot = lane % CPR;
+            row[i] = r;
+            goff[i] = r * stride + ((slot ^ swz<CPR>(r)) * 8);
         }
     }
-    // row-major copy: lds[row * stride + col]
-    __device__ __forceinline__ void store_rows(uint16_t* lds, int stride, int tid) const {
-        if (tid >= kItems) return;
-        const int rc = tid % kRowChunks, dc = tid / kRowChunks;
+    // g: first row of the tile in global memory; last: last valid row index
+    // relative to g (rows beyond are clamped); tail: whether clamping applies.
+    __device__ __forceinline__ void issue(const uint16_t* g, uint16_t* tile, int wave, int stride,
+                                          bool tail, int last) const {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) *(u32x4*)(lds + (4 * rc + k) * stride + dc * 8) = r[k];
-    }
-    // transposed copy in the permuted row order: lds[col * stride + perm(row)]
-    __device__ __forceinline__ void store_cols(uint16_t* lds, int stride, int tid) const {
-        if (tid >= kItems) return;
-        const int rc = tid % kRowChunks, dc = tid / kRowChunks;
-        u32x2 cols[8];
-        transpose4x8(r[0], r[1], r[2], r[3], cols);
-        const int pos = perm_chunk_pos(rc);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) *(u32x2*)(lds + (dc * 8 + e) * stride + pos) = cols[e];
+        for (int i = 0; i < kPerWave; ++i) {
+            int off = goff[i];
+            if (tail && row[i] > last) off += (last - row[i]) * stride;
+            dma16(g + off, tile + (wave * kPerWave + i) * 512);
+        }
     }
 };
 
 // ---------------------------------------------------------------------------
-// dK, dV: one workgroup per (batch, kv head, 128-key tile); 4 waves x 32 keys
+// dQ: one workgroup per (batch, query head, BM-row tile); NW waves x 32 rows,
+// two waves per SIMD.  Per key tile and wave:
+//   S^T = K Q^T, dP^T = V dO^T     (A from the K / V tiles, B resident)
+//   P^T = exp2(c S^T - lse2), dS^T = P^T o (dP^T - D)   (one query per lane)
+//   dQ^T += K^T dS^T              (K^T from transposing reads of the K tile)
+// ---------------------------------------------------------------------------
+template <int D, int NW, int BN>
+struct DqCfg {
+    static constexpr int tileElems = BN * D;
+    static constexpr int stageElems = 2 * tileElems;  // K then V
+    static constexpr int bytes = 2 * stageElems * 2;
+};
+
+template <bool BF16, int D, int NW, int BN>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel(BwdArgs a) {
+    using C = DqCfg<D, NW, BN>;
+    using Dma = TileDma<D, BN, NW>;
+    constexpr int KS = D / 16, DB = D / 32, KB = BN / 32, CPR = D / 8;
+    constexpr int BM = 32 * NW;
+    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r32 = lane & 31, half = lane >> 5;
+    const int b = blockIdx.x / a.heads, h = blockIdx.x % a.heads;
+    const int ntiles = gridDim.y;
+    const int qt = a.causal ? (ntiles - 1 - (int)blockIdx.y) : (int)blockIdx.y;
+    const Seq s = seq_of(b, a.cu_q, a.cu_k, a.seqlen_q, a.seqlen_k);
+    const int i0 = qt * BM;
+    if (i0 >= s.len_q) return;
+    const Mask mk{a.causal, a.left, a.right};
+    const int hk = h / (a.heads / a.kv_heads);
+    const int64_t q_stride = (int64_t)a.heads * D;
+    const int kv_stride = a.kv_heads * D;
+    const uint16_t* qbase = (const uint16_t*)a.q + (s.q_start * a.heads + h) * D;
+    const uint16_t* dobase = (const uint16_t*)a.dout + (s.q_start * a.heads + h) * D;
+    const uint16_t* kbase = (const uint16_t*)a.k + (s.k_start * a.kv_heads + hk) * D;
+    const uint16_t* vbase = (const uint16_t*)a.v + (s.k_start * a.kv_heads + hk) * D;
+    const int64_t rowidx0 = a.cu_q ? (int64_t)h * a.cu_q[a.batch] + s.q_start
+                                   : ((int64_t)b * a.heads + h) * a.seqlen_q;
+
+    const int i_last = min(i0 + BM, s.len_q) - 1;
+    const int key_lo = mk.lo_of(i0, s), key_hi = mk.hi_of(i_last, s);
+    const int t_lo = key_lo / BN;
+    const int t_hi = key_hi >= key_lo ? key_hi / BN + 1 : t_lo;
+
+    const int wq0 = i0 + 32 * wave;
+    const int wq1 = min(wq0 + 31, s.len_q - 1);
+    const bool wave_live = wq0 < s.len_q;
+    const int w_key_lo = wave_live ? mk.lo_of(wq0, s) : 0;
+    const int w_key_hi = wave_live ? mk.hi_of(wq1, s) : -1;
+    const int w_full_lo = wave_live ? mk.lo_of(wq1, s) : 0;
+    const int w_full_hi = wave_live ? mk.hi_of(wq0, s) : -1;
+
+    const int row = wq0 + r32;
+    const bool row_ok = row < s.len_q;
+    u32x4 qf[KS], dof[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        qf[ks] = row_ok ? *(const u32x4*)(qbase + (int64_t)row * q_stride + ks * 16 + 8 * half) : u32x4{0, 0, 0, 0};
+        dof[ks] = row_ok ? *(const u32x4*)(dobase + (int64_t)row * q_stride + ks * 16 + 8 * half) : u32x4{0, 0, 0, 0};
+    }
+    const float lse2 = row_ok ? a.lse2[rowidx0 + row] : __builtin_inff();  // +inf: P = 0 on padding rows
+    const float dsum = row_ok ? a.dsum[rowidx0 + row] : 0.f;
+    const int row_lo = mk.lo_of(row, s), row_hi = mk.hi_of(row, s);
+
+    Dma dma;
+    dma.init(wave, lane, kv_stride);
+    int k_rd[KS];  // A operand reads of the K / V tiles: row r32, chunk 2 ks + half
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) k_rd[ks] = r32 * D + (((2 * ks + half) ^ swz<CPR>(r32)) * 8);
+    int kt_rd[2][DB];  // K^T operand (transposing reads)
+    tr_offsets<D, DB>(lane, kt_rd);
+
+    f32x16 dq[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) dq[db] = f32x16{0};
+    const float c = a.scale_log2;
+
+    auto issue_tile = [&](int t, int buf) {
+        const int key0 = t * BN;
+        const bool tail = key0 + BN > s.len_k;
+        const int last = s.len_k - 1 - key0;
+        uint16_t* st = smem + buf * C::stageElems;
+        const int64_t toff = (int64_t)key0 * kv_stride;
+        dma.issue(kbase + toff, st, wave, kv_stride, tail, last);
+        dma.issue(vbase + toff, st + C::tileElems, wave, kv_stride, tail, last);
+    };
+
+    auto compute = [&](int t, int buf) {
+        const int key0 = t * BN;
+        if (!(wave_live && key0 <= w_key_hi && key0 + BN - 1 >= w_key_lo)) return;
+        const uint16_t* kt = smem + buf * C::stageElems;
+        const uint16_t* vt = kt + C::tileElems;
+        f32x16 sacc[KB], dpacc[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) { sacc[kb] = f32x16{0}; dpacc[kb] = f32x16{0}; }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4 ka[KB], va[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                ka[kb] = *(const u32x4*)(kt + kb * 32 * D + k_rd[ks]);
+                va[kb] = *(const u32x4*)(vt + kb * 32 * D + k_rd[ks]);
+            }
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                sacc[kb] = mfma32<BF16>(ka[kb], qf[ks], sacc[kb]);
+                dpacc[kb] = mfma32<BF16>(va[kb], dof[ks], dpacc[kb]);
+            }
+        }
+        // lane column = query row; register i = key key0 + kb*32 + 8(i/4) + 4 half + i%4
+        const bool masked = key0 < w_full_lo || key0 + BN - 1 > w_full_hi;  // uniform
+        const int lo = row_lo - key0, hi = row_hi - key0;
+        uint32_t dsp[KB][8];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) {
+                float p0 = fast_exp2(__builtin_fmaf(sacc[kb][i], c, -lse2));
+                float p1 = fast_exp2(__builtin_fmaf(sacc[kb][i + 1], c, -lse2));
+                if (masked) {
+                    const int k0 = kb * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+                    p0 = (k0 < lo || k0 > hi) ? 0.f : p0;
+                    p1 = (k0 + 1 < lo || k0 + 1 > hi) ? 0.f : p1;
+                }
+                dsp[kb][i / 2] = pack2<BF16>(p0 * (dpacc[kb][i] - dsum), p1 * (dpacc[kb][i + 1] - dsum));
+            }
+        // dQ^T += K^T dS^T over the BN keys (k-steps of 16)
+#pragma unroll
+        for (int kk = 0; kk < BN / 16; ++kk) {
+            const int kb = kk / 2, hs = kk % 2;
+            const u32x4 sb = u32x4{dsp[kb][4 * hs], dsp[kb][4 * hs + 1], dsp[kb][4 * hs + 2], dsp[kb][4 * hs + 3]};
+#pragma unroll
+            for (int db = 0; db < DB; ++db) dq[db] = mfma32<BF16>(read_tr<D, DB>(kt, kk, db, kt_rd), sb, dq[db]);
+        }
+    };
+
+    auto step = [&](int t, int buf) {
+        const bool has_next = t + 1 < t_hi;
+        if (has_next) issue_tile(t + 1, buf ^ 1);
+        compute(t, buf);
+        wait_vmcnt<0>();  // this wave's direct loads have landed
+        __syncthreads();
+    };
+    if (t_lo < t_hi) {
+        issue_tile(t_lo, 0);
+        wait_vmcnt<0>();
+        __syncthreads();
+        for (int t = t_lo; t < t_hi; t += 2) {
+            step(t, 0);
+            if (t + 1 < t_hi) step(t + 1, 1);
+        }
+    }
+    if (!row_ok) return;
+    uint16_t* dqrow = (uint16_t*)a.dq + ((s.q_start + row) * a.heads + h) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            u32x2 w;
+            w.x = pack2<BF16>(dq[db][4 * gq] * a.scale, dq[db][4 * gq + 1] * a.scale);
+            w.y = pack2<BF16>(dq[db][4 * gq + 2] * a.scale, dq[db][4 * gq + 3] * a.scale);
+            *(u32x2*)(dqrow + db * 32 + 8 * gq + 4 * half) = w;
+        }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one workgroup per (batch, kv head, 128-key tile); 4 waves x 32 keys,
+// one wave per SIMD (the dK/dV accumulators live beside resident K^T / V^T
+// operand fragments).  Per streamed 64-row query tile and wave:
+//   S = Q K^T, dP = dO V^T      (A from the Q / dO tiles, B resident)
+//   P = exp2(c S - lse2), dS = P o (dP - D)      (one key per lane column)
+//   dV^T += dO^T P, dK^T += Q^T dS   (A from transposing reads of the tiles)
 // ---------------------------------------------------------------------------
 constexpr int kKvWaves = 4;
 constexpr int kKvBN = 32 * kKvWaves;  // keys per workgroup
 constexpr int kKvBM = 64;             // query rows per streamed tile
 
 template <int D>
-struct DkdvSmem {
-    static constexpr int rStride = D + 8;        // row-major Q / dO
-    static constexpr int cStride = kKvBM + 8;    // transposed Q^T / dO^T (per d)
-    static constexpr int rElems = kKvBM * rStride;
-    static constexpr int cElems = D * cStride;
-    // per stage: Q, dO (row-major), Q^T, dO^T (permuted), LSE*log2e, D
-    static constexpr int stageBytes = (2 * rElems + 2 * cElems) * 2 + 2 * kKvBM * 4;
+struct DkdvCfg {
+    static constexpr int tileElems = kKvBM * D;
+    // per stage: Q tile, dO tile (16-bit), then lse2[64], D[64] (fp32)
+    static constexpr int stageBytes = 2 * tileElems * 2 + 2 * kKvBM * 4;
     static constexpr int bytes = 2 * stageBytes;
 };
 
 template <bool BF16, int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdArgs a) {
-    using SM = DkdvSmem<D>;
-    using P = Piece<D, kKvBM>;
-    constexpr int KS = D / 16, DB = D / 32;
+    using C = DkdvCfg<D>;
+    using Dma = TileDma<D, kKvBM, kKvWaves>;
+    constexpr int KS = D / 16, DB = D / 32, CPR = D / 8;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r32 = lane & 31, half = lane >> 5;
     const int g = a.heads / a.kv_heads;
     const int b = blockIdx.x / a.kv_heads, hk = blockIdx.x % a.kv_heads;
@@ -144,7 +316,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const Mask mk{a.causal, a.left, a.right};
     const int j1 = min(j0 + kKvBN, s.len_k) - 1;
 
-    const int64_t q_stride = (int64_t)a.heads * D, kv_stride = (int64_t)a.kv_heads * D;
+    const int q_stride = a.heads * D, kv_stride = a.kv_heads * D;
     const uint16_t* kbase = (const uint16_t*)a.k + (s.k_start * a.kv_heads + hk) * D;
     const uint16_t* vbase = (const uint16_t*)a.v + (s.k_start * a.kv_heads + hk) * D;
     const int64_t total_q = a.cu_q ? (int64_t)a.cu_q[a.batch] : 0;
@@ -158,88 +330,87 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const int it_hi = i_hi >= i_lo ? i_hi / kKvBM + 1 : it_lo;
     const int nt = it_hi - it_lo;  // tiles per head
 
-    // This wave's keys, resident as B operands (K^T and V^T fragments).
+    // This wave's keys and, per lane, the query rows that see its key.
     const int kw0 = j0 + 32 * wave;
     const int kw1 = min(kw0 + 31, s.len_k - 1);
     const bool wave_live = kw0 < s.len_k;
-    u32x4 kf[KS], vf[KS];
-    {
-        const int key = kw0 + r32;
+    const int key = kw0 + r32;
+    int q_lo = 0, q_hi = s.len_q - 1;  // visible iff q_lo <= query <= q_hi
+    if (a.causal) q_lo = max(q_lo, key - s.off);
+    if (a.right >= 0) q_lo = max(q_lo, key - s.off - a.right);
+    if (a.left >= 0) q_hi = min(q_hi, key - s.off + a.left);
+    if (key >= s.len_k) q_hi = -1;
+    u32x4 kf[KS], vf[KS];  // K^T, V^T B operands: lane column = key
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bool ok = key < s.len_k;
-            kf[ks] = ok ? *(const u32x4*)(kbase + (int64_t)key * kv_stride + ks * 16 + 8 * half) : u32x4{0, 0, 0, 0};
-            vf[ks] = ok ? *(const u32x4*)(vbase + (int64_t)key * kv_stride + ks * 16 + 8 * half) : u32x4{0, 0, 0, 0};
-        }
+    for (int ks = 0; ks < KS; ++ks) {
+        const bool ok = key < s.len_k;
+        kf[ks] = ok ? *(const u32x4*)(kbase + (int64_t)key * kv_stride + ks * 16 + 8 * half) : u32x4{0, 0, 0, 0};
+        vf[ks] = ok ? *(const u32x4*)(vbase + (int64_t)key * kv_stride + ks * 16 + 8 * half) : u32x4{0, 0, 0, 0};
     }
     f32x16 dk[DB], dv[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) { dk[db] = f32x16{0}; dv[db] = f32x16{0}; }
     const float c = a.scale_log2;
 
-    auto stage_ptr = [&](int buf) { return smem_raw + buf * SM::stageBytes; };
-    auto q_lds = [&](uint8_t* st) { return (uint16_t*)st; };
-    auto do_lds = [&](uint8_t* st) { return (uint16_t*)st + SM::rElems; };
-    auto qt_lds = [&](uint8_t* st) { return (uint16_t*)st + 2 * SM::rElems; };
-    auto dot_lds = [&](uint8_t* st) { return (uint16_t*)st + 2 * SM::rElems + SM::cElems; };
-    auto lse_lds = [&](uint8_t* st) { return (float*)((uint16_t*)st + 2 * SM::rElems + 2 * SM::cElems); };
-    auto ds_lds = [&](uint8_t* st) { return lse_lds(st) + kKvBM; };
+    Dma dma;
+    dma.init(wave, lane, q_stride);
+    int q_rd[KS];  // A operand reads of the Q / dO tiles: row r32 (+32 qb), chunk 2 ks + half
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) q_rd[ks] = r32 * D + (((2 * ks + half) ^ swz<CPR>(r32)) * 8);
+    int t_rd[2][DB];  // Q^T / dO^T operands (transposing reads)
+    tr_offsets<D, DB>(lane, t_rd);
 
-    P pq, pdo;
-    float st_lse = 0.f, st_d = 0.f;
-    // Flattened (head in group, query tile) sequence n = 0 .. g*nt-1.
-    auto load_stage = [&](int n) {
+    auto q_lds = [&](int buf) { return (uint16_t*)(smem_raw + buf * C::stageBytes); };
+    auto lse_lds = [&](int buf) { return (float*)(smem_raw + buf * C::stageBytes + 2 * C::tileElems * 2); };
+
+    // Flattened (query head in group, query tile) sequence n = 0 .. g*nt-1.
+    auto issue_step = [&](int n, int buf) {
         const int h = hk * g + n / nt;
         const int row0 = (it_lo + n % nt) * kKvBM;
-        const uint16_t* qb = (const uint16_t*)a.q + (s.q_start * a.heads + h) * D;
-        const uint16_t* dob = (const uint16_t*)a.dout + (s.q_start * a.heads + h) * D;
-        pq.load(qb, q_stride, row0, s.len_q, tid);
-        pdo.load(dob, q_stride, row0, s.len_q, tid);
-        if (tid < 2 * kKvBM) {
-            const int row = row0 + (tid % kKvBM);
-            const int64_t idx = a.cu_q ? (int64_t)h * total_q + s.q_start + row
-                                       : ((int64_t)b * a.heads + h) * a.seqlen_q + row;
-            if (tid < kKvBM)  // rows past the end get LSE = +inf, so P = 0 there
-                st_lse = row < s.len_q ? a.lse[idx] * kLog2e : __builtin_inff();
-            else
-                st_d = row < s.len_q ? a.dsum[idx] : 0.f;
+        const bool tail = row0 + kKvBM > s.len_q;
+        const int last = s.len_q - 1 - row0;
+        const int64_t hoff = (s.q_start * a.heads + h) * D + (int64_t)row0 * q_stride;
+        uint16_t* qt = q_lds(buf);
+        dma.issue((const uint16_t*)a.q + hoff, qt, wave, q_stride, tail, last);
+        dma.issue((const uint16_t*)a.dout + hoff, qt + C::tileElems, wave, q_stride, tail, last);
+        if (wave < 2) {  // one 4-byte direct load each: lse2 rows, D rows
+            const int64_t idx0 = a.cu_q ? (int64_t)h * total_q + s.q_start + row0
+                                        : ((int64_t)b * a.heads + h) * a.seqlen_q + row0;
+            const float* src = (wave == 0 ? a.lse2 : a.dsum) + idx0 + min(lane, last);
+            dma4(src, lse_lds(buf) + wave * kKvBM);
         }
     };
-    auto store_stage = [&](uint8_t* st) {
-        pq.store_rows(q_lds(st), SM::rStride, tid);
-        pdo.store_rows(do_lds(st), SM::rStride, tid);
-        pq.store_cols(qt_lds(st), SM::cStride, tid);
-        pdo.store_cols(dot_lds(st), SM::cStride, tid);
-        if (tid < kKvBM) lse_lds(st)[tid] = st_lse;
-        else if (tid < 2 * kKvBM) ds_lds(st)[tid - kKvBM] = st_d;
-    };
 
-    // One streamed query tile against this wave's 32 keys.
-    auto tile = [&](auto masked, int row0, uint8_t* st) {
-        const uint16_t* qs = q_lds(st);
-        const uint16_t* dos = do_lds(st);
-        const uint16_t* qts = qt_lds(st);
-        const uint16_t* dots = dot_lds(st);
-        const float* lses = lse_lds(st);
-        const float* dss = ds_lds(st);
+    auto compute = [&](int n, int buf) {
+        const int row0 = (it_lo + n % nt) * kKvBM;
+        const int row1 = min(row0 + kKvBM, s.len_q) - 1;
+        // any visible pair between rows [row0, row1] and keys [kw0, kw1]?  (uniform)
+        if (!(wave_live && mk.hi_of(row1, s) >= kw0 && mk.lo_of(row0, s) <= kw1)) return;
+        // all pairs visible: the first row sees the last key, the last row the first key
+        const bool full = row0 + kKvBM <= s.len_q && kw0 + 31 < s.len_k &&
+                          mk.hi_of(row0, s) >= kw0 + 31 && mk.lo_of(row0 + kKvBM - 1, s) <= kw0;
+        const uint16_t* qt = q_lds(buf);
+        const uint16_t* dot = qt + C::tileElems;
+        const float* lses = lse_lds(buf);
+        const float* dss = lses + kKvBM;
+        const int lo = q_lo - row0, hi = q_hi - row0;
         uint32_t pp[2][8], dsp[2][8];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             f32x16 sacc = f32x16{0}, dpacc = f32x16{0};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const u32x4 qa = *(const u32x4*)(qs + (qb * 32 + r32) * SM::rStride + ks * 16 + 8 * half);
-                const u32x4 da = *(const u32x4*)(dos + (qb * 32 + r32) * SM::rStride + ks * 16 + 8 * half);
+                const u32x4 qa = *(const u32x4*)(qt + qb * 32 * D + q_rd[ks]);
+                const u32x4 da = *(const u32x4*)(dot + qb * 32 * D + q_rd[ks]);
                 sacc = mfma32<BF16>(qa, kf[ks], sacc);
                 dpacc = mfma32<BF16>(da, vf[ks], dpacc);
             }
-            // lane column = key kw0 + r32; register i = query row qb*32 + 8(i/4) + 4 half + i%4
-            const int key = kw0 + r32;
+            // lane column = key; register i = query row0 + qb*32 + 8(i/4) + 4 half + i%4
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
-                const int rbase = qb * 32 + 8 * gq + 4 * half;
-                const float4 l4 = *(const float4*)(lses + rbase);
-                const float4 d4 = *(const float4*)(dss + rbase);
+                const int rb = qb * 32 + 8 * gq + 4 * half;
+                const float4 l4 = *(const float4*)(lses + rb);
+                const float4 d4 = *(const float4*)(dss + rb);
                 const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
                 const float dvv[4] = {d4.x, d4.y, d4.z, d4.w};
                 float pv[4], dsv[4];
@@ -247,10 +418,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
                 for (int e = 0; e < 4; ++e) {
                     const int i = 4 * gq + e;
                     float p = fast_exp2(__builtin_fmaf(sacc[i], c, -lv[e]));
-                    if constexpr (decltype(masked)::value) {
-                        const int qi = row0 + rbase + e;
-                        if (key < mk.lo_of(qi, s) || key > mk.hi_of(qi, s)) p = 0.f;
-                    }
+                    if (!full) p = (rb + e < lo || rb + e > hi) ? 0.f : p;
                     pv[e] = p;
                     dsv[e] = p * (dpacc[i] - dvv[e]);
                 }
@@ -260,7 +428,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
                 dsp[qb][2 * gq + 1] = pack2<BF16>(dsv[2], dsv[3]);
             }
         }
-        // dV^T += dO^T P, dK^T += Q^T dS over the 64 rows (4 k-steps of 16)
+        // dV^T += dO^T P, dK^T += Q^T dS over the 64 rows (k-steps of 16)
 #pragma unroll
         for (int kk = 0; kk < kKvBM / 16; ++kk) {
             const int qb = kk / 2, hs = kk % 2;
@@ -268,45 +436,31 @@ void bwd_dkdv_kernel(BwdArgs a) {
             const u32x4 sb = u32x4{dsp[qb][4 * hs], dsp[qb][4 * hs + 1], dsp[qb][4 * hs + 2], dsp[qb][4 * hs + 3]};
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const u32x4 doa = *(const u32x4*)(dots + (db * 32 + r32) * SM::cStride + kk * 16 + 8 * half);
-                const u32x4 qa = *(const u32x4*)(qts + (db * 32 + r32) * SM::cStride + kk * 16 + 8 * half);
-                dv[db] = mfma32<BF16>(doa, pb, dv[db]);
-                dk[db] = mfma32<BF16>(qa, sb, dk[db]);
+                dv[db] = mfma32<BF16>(read_tr<D, DB>(dot, kk, db, t_rd), pb, dv[db]);
+                dk[db] = mfma32<BF16>(read_tr<D, DB>(qt, kk, db, t_rd), sb, dk[db]);
             }
         }
     };
 
     const int total = g * nt;
-    if (total > 0) {
-        load_stage(0);
-        store_stage(stage_ptr(0));
+    auto step = [&](int n, int buf) {
+        const bool has_next = n + 1 < total;
+        if (has_next) issue_step(n + 1, buf ^ 1);
+        compute(n, buf);
+        wait_vmcnt<0>();
         __syncthreads();
-        for (int n = 0; n < total; ++n) {
-            const int buf = n & 1;
-            const bool has_next = n + 1 < total;
-            if (has_next) load_stage(n + 1);
-            const int row0 = (it_lo + n % nt) * kKvBM;
-            const int row1 = min(row0 + kKvBM, s.len_q) - 1;
-            // any visible pair between rows [row0, row1] and keys [kw0, kw1]?
-            const bool on = wave_live && mk.hi_of(row1, s) >= kw0 && mk.lo_of(row0, s) <= kw1 &&
-                            mk.hi_of(row1, s) >= mk.lo_of(row0, s);
-            if (on) {
-                // all pairs visible when the first row sees the last key and the
-                // last row sees the first key
-                const bool full = mk.hi_of(row0, s) >= kw1 && mk.lo_of(row1, s) <= kw0 &&
-                                  kw0 + 31 < s.len_k;
-                if (full)
-                    tile(std::false_type{}, row0, stage_ptr(buf));
-                else
-                    tile(std::true_type{}, row0, stage_ptr(buf));
-            }
-            if (has_next) store_stage(stage_ptr(buf ^ 1));
-            __syncthreads();
+    };
+    if (total > 0) {
+        issue_step(0, 0);
+        wait_vmcnt<0>();
+        __syncthreads();
+        for (int n = 0; n < total; n += 2) {
+            step(n, 0);
+            if (n + 1 < total) step(n + 1, 1);
         }
     }
 
     // store dK = scale * dK^T, dV = dV^T (lane column = key, registers = d)
-    const int key = kw0 + r32;
     if (!wave_live || key >= s.len_k) return;
     uint16_t* dkrow = (uint16_t*)a.dk + ((s.k_start + key) * a.kv_heads + hk) * D;
     uint16_t* dvrow = (uint16_t*)a.dv + ((s.k_start + key) * a.kv_heads + hk) * D;
@@ -325,171 +479,19 @@ void bwd_dkdv_kernel(BwdArgs a) {
         }
 }
 
-// ---------------------------------------------------------------------------
-// dQ: one workgroup per (batch, query head, 128-row tile); 4 waves x 32 rows
-// ---------------------------------------------------------------------------
-constexpr int kQWaves = 4;
-constexpr int kQBM = 32 * kQWaves;
-constexpr int kQBN = 64;
-
-template <int D>
-struct DqSmem {
-    static constexpr int rStride = D + 8;      // row-major K, V
-    static constexpr int cStride = kQBN + 8;   // K^T (permuted key order)
-    static constexpr int rElems = kQBN * rStride;
-    static constexpr int cElems = D * cStride;
-    static constexpr int stageElems = 2 * rElems + cElems;
-    static constexpr int bytes = 2 * stageElems * 2;
-};
-
-template <bool BF16, int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void bwd_dq_kernel(BwdArgs a) {
-    using SM = DqSmem<D>;
-    using P = Piece<D, kQBN>;
-    constexpr int KS = D / 16, DB = D / 32;
-    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int r32 = lane & 31, half = lane >> 5;
-    const int b = blockIdx.x / a.heads, h = blockIdx.x % a.heads;
-    const int ntiles = gridDim.y;
-    const int qt = a.causal ? (ntiles - 1 - (int)blockIdx.y) : (int)blockIdx.y;
-    const Seq s = seq_of(b, a.cu_q, a.cu_k, a.seqlen_q, a.seqlen_k);
-    const int i0 = qt * kQBM;
-    if (i0 >= s.len_q) return;
-    const Mask mk{a.causal, a.left, a.right};
-    const int hk = h / (a.heads / a.kv_heads);
-    const int64_t q_stride = (int64_t)a.heads * D, kv_stride = (int64_t)a.kv_heads * D;
-    const uint16_t* qbase = (const uint16_t*)a.q + (s.q_start * a.heads + h) * D;
-    const uint16_t* dobase = (const uint16_t*)a.dout + (s.q_start * a.heads + h) * D;
-    const uint16_t* kbase = (const uint16_t*)a.k + (s.k_start * a.kv_heads + hk) * D;
-    const uint16_t* vbase = (const uint16_t*)a.v + (s.k_start * a.kv_heads + hk) * D;
-    const int64_t rowidx0 = a.cu_q ? (int64_t)h * a.cu_q[a.batch] + s.q_start
-                                   : ((int64_t)b * a.heads + h) * a.seqlen_q;
-
-    const int i_last = min(i0 + kQBM, s.len_q) - 1;
-    const int key_lo = mk.lo_of(i0, s), key_hi = mk.hi_of(i_last, s);
-    const int t_lo = key_lo / kQBN;
-    const int t_hi = key_hi >= key_lo ? key_hi / kQBN + 1 : t_lo;
-
-    const int wq0 = i0 + 32 * wave;
-    const int wq1 = min(wq0 + 31, s.len_q - 1);
-    const bool wave_live = wq0 < s.len_q;
-    const int row = wq0 + r32;
-    const bool row_ok = row < s.len_q;
-    u32x4 qf[KS], dof[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        qf[ks] = row_ok ? *(const u32x4*)(qbase + (int64_t)row * q_stride + ks * 16 + 8 * half) : u32x4{0, 0, 0, 0};
-        dof[ks] = row_ok ? *(const u32x4*)(dobase + (int64_t)row * q_stride + ks * 16 + 8 * half) : u32x4{0, 0, 0, 0};
-    }
-    const float lse2 = row_ok ? a.lse[rowidx0 + row] * kLog2e : __builtin_inff();
-    const float dsum = row_ok ? a.dsum[rowidx0 + row] : 0.f;
-    const int row_lo = mk.lo_of(row, s), row_hi = mk.hi_of(row, s);
-    f32x16 dq[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db) dq[db] = f32x16{0};
-    const float c = a.scale_log2;
-
-    P pk, pv;
-    auto tile = [&](auto masked, int key0, const uint16_t* ks_lds) {
-        const uint16_t* vs_lds = ks_lds + SM::rElems;
-        const uint16_t* kts = ks_lds + 2 * SM::rElems;
-        uint32_t dsp[2][8];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            f32x16 sacc = f32x16{0}, dpacc = f32x16{0};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const u32x4 ka = *(const u32x4*)(ks_lds + (kb * 32 + r32) * SM::rStride + ks * 16 + 8 * half);
-                const u32x4 va = *(const u32x4*)(vs_lds + (kb * 32 + r32) * SM::rStride + ks * 16 + 8 * half);
-                sacc = mfma32<BF16>(ka, qf[ks], sacc);
-                dpacc = mfma32<BF16>(va, dof[ks], dpacc);
-            }
-            // lane column = query row; register i = key kb*32 + 8(i/4) + 4 half + i%4
-#pragma unroll
-            for (int i = 0; i < 16; i += 2) {
-                float p0 = fast_exp2(__builtin_fmaf(sacc[i], c, -lse2));
-                float p1 = fast_exp2(__builtin_fmaf(sacc[i + 1], c, -lse2));
-                if constexpr (decltype(masked)::value) {
-                    const int k0 = key0 + kb * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-                    if (k0 < row_lo || k0 > row_hi) p0 = 0.f;
-                    if (k0 + 1 < row_lo || k0 + 1 > row_hi) p1 = 0.f;
-                }
-                dsp[kb][i / 2] = pack2<BF16>(p0 * (dpacc[i] - dsum), p1 * (dpacc[i + 1] - dsum));
-            }
-        }
-        // dQ^T += K^T dS^T over the 64 keys (4 k-steps of 16)
-#pragma unroll
-        for (int kk = 0; kk < kQBN / 16; ++kk) {
-            const int kb = kk / 2, hs = kk % 2;
-            const u32x4 sb = u32x4{dsp[kb][4 * hs], dsp[kb][4 * hs + 1], dsp[kb][4 * hs + 2], dsp[kb][4 * hs + 3]};
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const u32x4 ka = *(const u32x4*)(kts + (db * 32 + r32) * SM::cStride + kk * 16 + 8 * half);
-                dq[db] = mfma32<BF16>(ka, sb, dq[db]);
-            }
-        }
-    };
-
-    const int w_key_lo = wave_live ? mk.lo_of(wq0, s) : 0;
-    const int w_key_hi = wave_live ? mk.hi_of(wq1, s) : -1;
-    const int w_full_lo = wave_live ? mk.lo_of(wq1, s) : 0;
-    const int w_full_hi = wave_live ? mk.hi_of(wq0, s) : -1;
-    if (t_lo < t_hi) {
-        pk.load(kbase, kv_stride, t_lo * kQBN, s.len_k, tid);
-        pv.load(vbase, kv_stride, t_lo * kQBN, s.len_k, tid);
-        pk.store_rows(smem, SM::rStride, tid);
-        pv.store_rows(smem + SM::rElems, SM::rStride, tid);
-        pk.store_cols(smem + 2 * SM::rElems, SM::cStride, tid);
-        __syncthreads();
-        for (int t = t_lo; t < t_hi; ++t) {
-            const int buf = (t - t_lo) & 1;
-            uint16_t* st = smem + buf * SM::stageElems;
-            const bool has_next = t + 1 < t_hi;
-            if (has_next) {
-                pk.load(kbase, kv_stride, (t + 1) * kQBN, s.len_k, tid);
-                pv.load(vbase, kv_stride, (t + 1) * kQBN, s.len_k, tid);
-            }
-            const int key0 = t * kQBN;
-            if (wave_live && key0 <= w_key_hi && key0 + kQBN - 1 >= w_key_lo) {
-                if (key0 < w_full_lo || key0 + kQBN - 1 > w_full_hi)
-                    tile(std::true_type{}, key0, st);
-                else
-                    tile(std::false_type{}, key0, st);
-            }
-            if (has_next) {
-                uint16_t* nx = smem + (buf ^ 1) * SM::stageElems;
-                pk.store_rows(nx, SM::rStride, tid);
-                pv.store_rows(nx + SM::rElems, SM::rStride, tid);
-                pk.store_cols(nx + 2 * SM::rElems, SM::cStride, tid);
-            }
-            __syncthreads();
-        }
-    }
-    if (!row_ok) return;
-    uint16_t* dqrow = (uint16_t*)a.dq + ((s.q_start + row) * a.heads + h) * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-            u32x2 w;
-            w.x = pack2<BF16>(dq[db][4 * gq] * a.scale, dq[db][4 * gq + 1] * a.scale);
-            w.y = pack2<BF16>(dq[db][4 * gq + 2] * a.scale, dq[db][4 * gq + 3] * a.scale);
-            *(u32x2*)(dqrow + db * 32 + 8 * gq + 4 * half) = w;
-        }
-}
-
 template <typename K>
 bool set_smem(K kernel, int bytes) {
     return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                                hipFuncAttributeMaxDynamicSharedMemorySize, bytes) == hipSuccess;
 }
 
+#ifndef FA_DQ_NW
+#define FA_DQ_NW 8
+#endif
+
 template <bool BF16, int D>
 int launch_bwd_t(const BwdArgs& a, int stage, hipStream_t stream) {
-    if (stage == 0) {  // D_i = dO_i . O_i
+    if (stage == 0) {  // D_i = dO_i . O_i, lse2_i
         constexpr int RPB = 256 / (D / 8);
         const int64_t items = (int64_t)a.batch * a.seqlen_q * a.heads;
         const int64_t blocks = (items + RPB - 1) / RPB;
@@ -502,21 +504,24 @@ int launch_bwd_t(const BwdArgs& a, int stage, hipStream_t stream) {
     if (stage == 1) {  // dK, dV
         const int ntiles = (a.seqlen_k + kKvBN - 1) / kKvBN;
         if (ntiles > 0 && a.batch > 0) {
-            static const bool ok = set_smem(bwd_dkdv_kernel<BF16, D>, DkdvSmem<D>::bytes);
+            static const bool ok = set_smem(bwd_dkdv_kernel<BF16, D>, DkdvCfg<D>::bytes);
             if (!ok) return 1;
             hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D>), dim3(a.batch * a.kv_heads, ntiles), dim3(256),
-                               DkdvSmem<D>::bytes, stream, a);
+                               DkdvCfg<D>::bytes, stream, a);
             if (hipGetLastError() != hipSuccess) return 1;
         }
         return 0;
     }
     // stage 2: dQ
-    const int ntiles = (a.seqlen_q + kQBM - 1) / kQBM;
+    constexpr int NW = FA_DQ_NW, BN = D == 128 ? 64 : 128;
+    constexpr int BM = 32 * NW;
+    const int ntiles = (a.seqlen_q + BM - 1) / BM;
     if (ntiles > 0 && a.batch > 0) {
-        static const bool ok = set_smem(bwd_dq_kernel<BF16, D>, DqSmem<D>::bytes);
+        auto kern = bwd_dq_kernel<BF16, D, NW, BN>;
+        constexpr int bytes = DqCfg<D, NW, BN>::bytes;
+        static const bool ok = set_smem(kern, bytes);
         if (!ok) return 1;
-        hipLaunchKernelGGL((bwd_dq_kernel<BF16, D>), dim3(a.batch * a.heads, ntiles), dim3(256),
-                           DqSmem<D>::bytes, stream, a);
+        hipLaunchKernelGGL(kern, dim3(a.batch * a.heads, ntiles), dim3(64 * NW), bytes, stream, a);
         if (hipGetLastError() != hipSuccess) return 1;
     }
     return 0;

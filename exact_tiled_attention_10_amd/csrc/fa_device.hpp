@@ -104,6 +104,76 @@ __device__ __forceinline__ void transpose4x8(const u32x4& r0, const u32x4& r1, c
     }
 }
 
+// ---------------------------------------------------------------------------
+// Row-major LDS tiles filled by direct global -> LDS loads.
+//
+// A tile holds ROWS rows of D 16-bit values, unpadded.  The 16-byte chunk c of
+// row r sits at slot c ^ swz(r): for 16 chunks per row the swizzle maps row
+// bits (r % 4, (r / 4) % 4) to chunk bits (hi, lo), so the 16 consecutive rows
+// an MFMA operand read (ds_read_b128, lane row r32, chunk 2 ks + half) touches
+// land in 16 distinct slots, and the 8 rows x 4 chunks of a transposing read
+// spread over all 16 slots (two lanes per bank word, the minimum for 512 B).
+// ---------------------------------------------------------------------------
+template <int CPR>
+__device__ __forceinline__ int swz(int row) {
+    if constexpr (CPR == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else return ((row & 3) << 1) | ((row >> 2) & 1);
+}
+
+// One direct load: each lane moves 16 bytes from `gsrc` to lds_dst + 16 * lane
+// (lds_dst must be the same for the whole wave).
+__device__ __forceinline__ void dma16(const void* gsrc, void* lds_dst) {
+    __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+}
+// Same with 4 bytes per lane (256 B per instruction).
+__device__ __forceinline__ void dma4(const void* gsrc, void* lds_dst) {
+    __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_dst, 4, 0, 0);
+}
+
+// s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt left at their
+// maxima): vector memory operations, direct LDS loads included, still in
+// flight <= N.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 16, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// Per-lane offsets (in 16-bit elements inside the tile) of the transposing
+// reads that build the A operand "X^T" of a 32x32x16 MFMA from a row-major
+// tile X (rows = contraction index, columns = M index).  In every 16-lane
+// group, lane 4r+c of ds_read_b64_tr_b16 receives element c of the 8-byte rows
+// addressed by lanes r, r+4, r+8, r+12.  Lane j of group g therefore points at
+// row 8*inst + 4*(g/2) + j/4 of the 16-row k-step and at columns
+// 32*mb + 16*(g%2) + 4*(j%4) .. +3; the receiver's element 4*inst + j/4 is row
+// ROWPERM(g/2, 4*inst + j/4) of the step, the order the B operand taken from an
+// MFMA C tile uses.  off[inst][mb] for M blocks mb of 32 columns.
+template <int D, int MB>
+__device__ __forceinline__ void tr_offsets(int lane, int off[2][MB]) {
+    constexpr int CPR = D / 8;
+    const int g = lane >> 4, j = lane & 15;
+#pragma unroll
+    for (int inst = 0; inst < 2; ++inst) {
+        const int rr = 8 * inst + 4 * (g >> 1) + (j >> 2);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int col = 32 * mb + 16 * (g & 1) + 4 * (j & 3);
+            off[inst][mb] = rr * D + (((col >> 3) ^ swz<CPR>(rr)) * 8) + (col & 7);
+        }
+    }
+}
+
+// The A operand X^T for k-step `ks` (rows 16 ks .. 16 ks + 15) and M block mb.
+template <int D, int MB>
+__device__ __forceinline__ u32x4 read_tr(const uint16_t* tile, int ks, int mb, const int off[2][MB]) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + ks * 16 * D + off[0][mb]));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + ks * 16 * D + off[1][mb]));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2.x, l2.y, h2.x, h2.y};
+}
+
 // Geometry of one (batch, head) problem slice, resolved from cu_seqlens.
 struct Seq {
     int64_t q_start, k_start;  // first packed row of the sequence

@@ -56,16 +56,6 @@ struct FwdCfg {
     static_assert(kDmaBlocks % NW == 0, "tiles must split evenly into 1 KiB blocks per wave");
 };
 
-// Chunk swizzle shared by the K and V tiles.  For 16 chunks per row it maps
-// row bits (r%4, (r/4)%4) to chunk bits (hi, lo): the 16 consecutive rows an
-// MFMA operand read touches land in 16 distinct chunk slots, and the 8 rows x
-// 4 chunks a transposed V read touches spread over all 16 slots.
-template <int CPR>
-__device__ __forceinline__ int swz(int row) {
-    if constexpr (CPR == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
-    else return ((row & 3) << 1) | ((row >> 2) & 1);
-}
-
 template <bool BF16, int D, int NW, int QB, int BN, int WPE>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(WPE, WPE)))
 void fwd_kernel(FwdArgs a) {
@@ -145,25 +135,9 @@ void fwd_kernel(FwdArgs a) {
     int k_rd[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) k_rd[ks] = r32 * D + (((2 * ks + half) ^ swz<C::CPR>(r32)) * 8);
-    // V^T operand reads (transposing LDS reads, 4 x 16-bit per lane each): in
-    // every 16-lane group, lane 4r+c receives element c of the 8-byte rows
-    // addressed by lanes r, r+4, r+8, r+12.  Lane j of group g therefore points
-    // at key row 8*inst + 4*(g/2) + j/4 of the 16-key step and at d columns
-    // 32*db + 16*(g%2) + 4*(j%4) .. +3; the receiver's element 4*inst + j/4 is
-    // then key ROWPERM(g/2, 4*inst + j/4) of the step, as the P^T operand expects.
+    // V^T operand reads: transposing LDS reads of the row-major V tile.
     int v_rd[2][DB];
-    {
-        const int g = lane >> 4, j = lane & 15;
-#pragma unroll
-        for (int inst = 0; inst < 2; ++inst) {
-            const int rr = 8 * inst + 4 * (g >> 1) + (j >> 2);
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const int col = 32 * db + 16 * (g & 1) + 4 * (j & 3);
-                v_rd[inst][db] = rr * D + (((col >> 3) ^ swz<C::CPR>(rr)) * 8) + (col & 7);
-            }
-        }
-    }
+    tr_offsets<D, DB>(lane, v_rd);
 
     f32x16 acc[DB][QB];
 #pragma unroll
@@ -239,14 +213,7 @@ void fwd_kernel(FwdArgs a) {
             }
         }
         // V^T fragments of the first key step: read now, used after the softmax.
-        auto read_vt = [&](int kk, int db) {
-            typedef short s16x4 __attribute__((ext_vector_type(4)));
-            typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs_lds + kk * 16 * D + v_rd[0][db]));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs_lds + kk * 16 * D + v_rd[1][db]));
-            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-            return u32x4{l2.x, l2.y, h2.x, h2.y};
-        };
+        auto read_vt = [&](int kk, int db) { return read_tr<D, DB>(vs_lds, kk, db, v_rd); };
         u32x4 vf0[DB];
 #pragma unroll
         for (int db = 0; db < DB; ++db) vf0[db] = read_vt(0, db);

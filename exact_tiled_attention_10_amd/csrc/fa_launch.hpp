@@ -33,6 +33,7 @@ struct BwdArgs {
     void* dk;
     void* dv;
     float* dsum;  // workspace: D_i = dO_i . O_i, laid out like lse
+    float* lse2;  // workspace: LSE_i * log2(e), laid out like lse
     const int32_t* cu_q;
     const int32_t* cu_k;
     int batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim;

@@ -106,10 +106,10 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            float softmax_scale, int dtype, void* stream);
 
 /*
- * Bytes of device workspace fa_bwd needs for these sizes (the per-row term
- * D_i = dO_i . O_i, float32, one per query row and head).  For packed
- * batches pass the same batch and seqlen_q as to fa_bwd.  Returns 0 for
- * invalid sizes.
+ * Bytes of device workspace fa_bwd needs for these sizes: two float32
+ * arrays of batch * heads * seqlen_q entries, the per-row term
+ * D_i = dO_i . O_i and LSE_i * log2(e).  For packed batches pass the same
+ * batch and seqlen_q as to fa_bwd.  Returns 0 for invalid sizes.
  */
 size_t fa_bwd_workspace_size(int batch, int heads, int seqlen_q, int head_dim, int dtype);
 

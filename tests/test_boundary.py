@@ -102,7 +102,7 @@ BAD_BWD = [
     (dict(dv=None), INVALID), (dict(ws=None), INVALID),
     (dict(dv=ctypes.c_void_p(0x10004)), INVALID),
     (dict(heads=3, kv_heads=2), INVALID), (dict(head_dim=32), UNSUPPORTED),
-    (dict(wsb=4 * 4 * 128 - 4), WORKSPACE), (dict(wsb=0), WORKSPACE),
+    (dict(wsb=2 * 4 * 4 * 128 - 4), WORKSPACE), (dict(wsb=0), WORKSPACE),
 ]
 
 
@@ -125,8 +125,8 @@ def test_bwd_stage_validates_like_fa_bwd(L):
 
 def test_workspace_size(L):
     f = L.fa_bwd_workspace_size
-    assert f(2, 8, 1000, 128, 1) == 2 * 8 * 1000 * 4
-    assert f(1, 4, 128, 64, 0) == 4 * 128 * 4
+    assert f(2, 8, 1000, 128, 1) == 2 * (2 * 8 * 1000 * 4)
+    assert f(1, 4, 128, 64, 0) == 2 * (4 * 128 * 4)
     assert f(0, 4, 128, 64, 0) == 4  # never zero for valid sizes
     assert f(1, 4, 128, 96, 0) == 0 and f(1, 0, 128, 64, 0) == 0 and f(1, 4, 128, 64, 7) == 0
 
