@@ -119,7 +119,6 @@ template <int D, int NW, int BN>
 struct DqCfg {
     static constexpr int tileElems = BN * D;
     static constexpr int stageElems = 2 * tileElems;  // K then V
-    static constexpr int bytes = 2 * stageElems * 2;
 };
 
 template <bool BF16, int D, int NW, int BN>
@@ -129,7 +128,10 @@ void bwd_dq_kernel(BwdArgs a) {
     using Dma = TileDma<D, BN, NW>;
     constexpr int KS = D / 16, DB = D / 32, KB = BN / 32, CPR = D / 8;
     constexpr int BM = 32 * NW;
-    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+    // separate objects per stage (no waits on the other stage's direct loads)
+    __shared__ __attribute__((aligned(16))) uint16_t lds0[C::stageElems];
+    __shared__ __attribute__((aligned(16))) uint16_t lds1[C::stageElems];
+    auto stage = [&](int buf) { return buf ? lds1 : lds0; };
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -193,7 +195,7 @@ void bwd_dq_kernel(BwdArgs a) {
         const int key0 = t * BN;
         const bool tail = key0 + BN > s.len_k;
         const int last = s.len_k - 1 - key0;
-        uint16_t* st = smem + buf * C::stageElems;
+        uint16_t* st = stage(buf);
         const int64_t toff = (int64_t)key0 * kv_stride;
         dma.issue(kbase + toff, st, wave, kv_stride, tail, last);
         dma.issue(vbase + toff, st + C::tileElems, wave, kv_stride, tail, last);
@@ -202,7 +204,7 @@ void bwd_dq_kernel(BwdArgs a) {
     auto compute = [&](int t, int buf) {
         const int key0 = t * BN;
         if (!(wave_live && key0 <= w_key_hi && key0 + BN - 1 >= w_key_lo)) return;
-        const uint16_t* kt = smem + buf * C::stageElems;
+        const uint16_t* kt = stage(buf);
         const uint16_t* vt = kt + C::tileElems;
         f32x16 sacc[KB], dpacc[KB];
 #pragma unroll
@@ -294,7 +296,6 @@ struct DkdvCfg {
     static constexpr int tileElems = kKvBM * D;
     // per stage: Q tile, dO tile (16-bit), then lse2[64], D[64] (fp32)
     static constexpr int stageBytes = 2 * tileElems * 2 + 2 * kKvBM * 4;
-    static constexpr int bytes = 2 * stageBytes;
 };
 
 template <bool BF16, int D>
@@ -303,7 +304,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
     using C = DkdvCfg<D>;
     using Dma = TileDma<D, kKvBM, kKvWaves>;
     constexpr int KS = D / 16, DB = D / 32, CPR = D / 8;
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
+    // separate objects per stage (no waits on the other stage's direct loads)
+    __shared__ __attribute__((aligned(16))) uint8_t lds0[C::stageBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t lds1[C::stageBytes];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -360,8 +363,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
     int t_rd[2][DB];  // Q^T / dO^T operands (transposing reads)
     tr_offsets<D, DB>(lane, t_rd);
 
-    auto q_lds = [&](int buf) { return (uint16_t*)(smem_raw + buf * C::stageBytes); };
-    auto lse_lds = [&](int buf) { return (float*)(smem_raw + buf * C::stageBytes + 2 * C::tileElems * 2); };
+    auto q_lds = [&](int buf) { return (uint16_t*)(buf ? lds1 : lds0); };
+    auto lse_lds = [&](int buf) { return (float*)((buf ? lds1 : lds0) + 2 * C::tileElems * 2); };
 
     // Flattened (query head in group, query tile) sequence n = 0 .. g*nt-1.
     auto issue_step = [&](int n, int buf) {
@@ -381,64 +384,131 @@ void bwd_dkdv_kernel(BwdArgs a) {
         }
     };
 
-    auto compute = [&](int n, int buf) {
+    // One step covers a 64-row query tile as two 32-row blocks, software-pipelined
+    // in four phases so that no MFMA waits on an LDS read issued just before it
+    // and the softmax arithmetic of one block runs beside the products of another:
+    //   1: S, dP of block 0                 (operands prefetched kPf reads ahead)
+    //   2: S, dP of block 1  | P, dS of block 0
+    //   3: dV, dK of block 0 | P, dS of block 1
+    //   4: dV, dK of block 1
+    // Scheduling fences keep this order.  P and dS are computed unmasked; on tiles
+    // where not every (row, key) pair is visible (full == false, uniform) the
+    // packed 16-bit words are ANDed with the visibility mask before their
+    // products, a branch that touches nothing but those words.  Masked entries
+    // of rows without any visible key give inf or NaN before the AND, never after.
+    auto compute = [&](int n, int buf, bool full) {
+        constexpr int kPf = 4;
         const int row0 = (it_lo + n % nt) * kKvBM;
-        const int row1 = min(row0 + kKvBM, s.len_q) - 1;
-        // any visible pair between rows [row0, row1] and keys [kw0, kw1]?  (uniform)
-        if (!(wave_live && mk.hi_of(row1, s) >= kw0 && mk.lo_of(row0, s) <= kw1)) return;
-        // all pairs visible: the first row sees the last key, the last row the first key
-        const bool full = row0 + kKvBM <= s.len_q && kw0 + 31 < s.len_k &&
-                          mk.hi_of(row0, s) >= kw0 + 31 && mk.lo_of(row0 + kKvBM - 1, s) <= kw0;
         const uint16_t* qt = q_lds(buf);
         const uint16_t* dot = qt + C::tileElems;
         const float* lses = lse_lds(buf);
         const float* dss = lses + kKvBM;
         const int lo = q_lo - row0, hi = q_hi - row0;
+
+        f32x16 sacc[2], dpacc[2];
+        u32x4 qa[2][KS], da[2][KS];  // A operands Q, dO of each block (row r32, k-step ks)
+        f32x4 l4[2][4], d4[2][4];    // lse2 and D of the rows of register group gq
         uint32_t pp[2][8], dsp[2][8];
+        u32x4 tra[2][4 * DB];        // X^T operands of the dV, dK products, in issue order
+
+        auto load_ops = [&](int qb, int ks) {
+            qa[qb][ks] = *(const u32x4*)(qt + qb * 32 * D + q_rd[ks]);
+            da[qb][ks] = *(const u32x4*)(dot + qb * 32 * D + q_rd[ks]);
+        };
+        auto load_rows = [&](int qb, int gq) {
+            const int rb = qb * 32 + 8 * gq + 4 * half;
+            l4[qb][gq] = *(const f32x4*)(lses + rb);
+            d4[qb][gq] = *(const f32x4*)(dss + rb);
+        };
+        // product j of a block: k-step kk = 2 qb + j / (2 DB), M block (j / 2) % DB,
+        // even j: dV^T += dO^T P, odd j: dK^T += Q^T dS
+        auto load_tr = [&](int qb, int j) {
+            const int kk = 2 * qb + j / (2 * DB), db = (j / 2) % DB;
+            tra[qb][j] = read_tr<D, DB>((j & 1) ? qt : dot, kk, db, t_rd);
+        };
+        auto prod = [&](int qb, int j) {
+            const int hs = j / (2 * DB), db = (j / 2) % DB;
+            const uint32_t* src = (j & 1) ? dsp[qb] : pp[qb];
+            const u32x4 bop = u32x4{src[4 * hs], src[4 * hs + 1], src[4 * hs + 2], src[4 * hs + 3]};
+            if (j & 1) dk[db] = mfma32<BF16>(tra[qb][j], bop, dk[db]);
+            else dv[db] = mfma32<BF16>(tra[qb][j], bop, dv[db]);
+        };
+        auto sdp = [&](int qb, int ks) {
+            sacc[qb] = mfma32<BF16>(qa[qb][ks], kf[ks], ks ? sacc[qb] : f32x16{0});
+            dpacc[qb] = mfma32<BF16>(da[qb][ks], vf[ks], ks ? dpacc[qb] : f32x16{0});
+        };
+        // P and dS of registers 2m, 2m + 1 (register i: query row
+        // 32 qb + 8 (i / 4) + 4 half + i % 4 of the tile, lane column = key)
+        auto softmax_pair = [&](int qb, int m) {
+            float pv[2], dv2[2];
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            f32x16 sacc = f32x16{0}, dpacc = f32x16{0};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const u32x4 qa = *(const u32x4*)(qt + qb * 32 * D + q_rd[ks]);
-                const u32x4 da = *(const u32x4*)(dot + qb * 32 * D + q_rd[ks]);
-                sacc = mfma32<BF16>(qa, kf[ks], sacc);
-                dpacc = mfma32<BF16>(da, vf[ks], dpacc);
+            for (int t = 0; t < 2; ++t) {
+                const int i = 2 * m + t;
+                const float pr = fast_exp2(__builtin_fmaf(sacc[qb][i], c, -l4[qb][i / 4][i % 4]));
+                pv[t] = pr;
+                dv2[t] = pr * (dpacc[qb][i] - d4[qb][i / 4][i % 4]);
             }
-            // lane column = key; register i = query row0 + qb*32 + 8(i/4) + 4 half + i%4
+            pp[qb][m] = pack2<BF16>(pv[0], pv[1]);
+            dsp[qb][m] = pack2<BF16>(dv2[0], dv2[1]);
+        };
+        auto mask_block = [&](int qb) {
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int rb = qb * 32 + 8 * gq + 4 * half;
-                const float4 l4 = *(const float4*)(lses + rb);
-                const float4 d4 = *(const float4*)(dss + rb);
-                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-                const float dvv[4] = {d4.x, d4.y, d4.z, d4.w};
-                float pv[4], dsv[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 4 * gq + e;
-                    float p = fast_exp2(__builtin_fmaf(sacc[i], c, -lv[e]));
-                    if (!full) p = (rb + e < lo || rb + e > hi) ? 0.f : p;
-                    pv[e] = p;
-                    dsv[e] = p * (dpacc[i] - dvv[e]);
-                }
-                pp[qb][2 * gq] = pack2<BF16>(pv[0], pv[1]);
-                pp[qb][2 * gq + 1] = pack2<BF16>(pv[2], pv[3]);
-                dsp[qb][2 * gq] = pack2<BF16>(dsv[0], dsv[1]);
-                dsp[qb][2 * gq + 1] = pack2<BF16>(dsv[2], dsv[3]);
+            for (int m = 0; m < 8; ++m) {
+                const int r0 = qb * 32 + 8 * (m / 2) + 4 * half + 2 * (m % 2);  // rows of registers 2m, 2m + 1
+                const uint32_t keep = ((r0 >= lo && r0 <= hi) ? 0x0000FFFFu : 0u) |
+                                      ((r0 + 1 >= lo && r0 + 1 <= hi) ? 0xFFFF0000u : 0u);
+                pp[qb][m] &= keep;
+                dsp[qb][m] &= keep;
             }
+        };
+        constexpr int NJ = 4 * DB;  // dV, dK products per block
+
+        // phase 1
+#pragma unroll
+        for (int ks = 0; ks < kPf; ++ks) load_ops(0, ks);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            sdp(0, ks);
+            if (ks + kPf < KS) load_ops(0, ks + kPf);
+            else load_ops(1, ks + kPf - KS);
+            if (ks >= KS - 2) load_rows(0, ks - (KS - 2));
+            __builtin_amdgcn_sched_barrier(0);
         }
-        // dV^T += dO^T P, dK^T += Q^T dS over the 64 rows (k-steps of 16)
+        // phase 2 (row terms of register group gq are loaded a few slots before use)
 #pragma unroll
-        for (int kk = 0; kk < kKvBM / 16; ++kk) {
-            const int qb = kk / 2, hs = kk % 2;
-            const u32x4 pb = u32x4{pp[qb][4 * hs], pp[qb][4 * hs + 1], pp[qb][4 * hs + 2], pp[qb][4 * hs + 3]};
-            const u32x4 sb = u32x4{dsp[qb][4 * hs], dsp[qb][4 * hs + 1], dsp[qb][4 * hs + 2], dsp[qb][4 * hs + 3]};
+        for (int ks = 0; ks < KS; ++ks) {
+            sdp(1, ks);
+            if (ks + kPf < KS) load_ops(1, ks + kPf);
+            if (ks == 0) load_rows(0, 2);
+            if (ks == KS / 4) load_rows(0, 3);
+            if (ks == KS / 2) load_rows(1, 0);
+            if (ks == 3 * KS / 4) load_rows(1, 1);
+            if (ks >= KS - kPf) load_tr(0, ks - (KS - kPf));
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                dv[db] = mfma32<BF16>(read_tr<D, DB>(dot, kk, db, t_rd), pb, dv[db]);
-                dk[db] = mfma32<BF16>(read_tr<D, DB>(qt, kk, db, t_rd), sb, dk[db]);
-            }
+            for (int m = ks * 8 / KS; m < (ks + 1) * 8 / KS; ++m) softmax_pair(0, m);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (!full) mask_block(0);
+        // phase 3
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            prod(0, j);
+            if (j + kPf < NJ) load_tr(0, j + kPf);
+            else load_tr(1, j + kPf - NJ);
+            if (j == 0) load_rows(1, 2);
+            if (j == NJ / 4) load_rows(1, 3);
+#pragma unroll
+            for (int m = j * 8 / NJ; m < (j + 1) * 8 / NJ; ++m) softmax_pair(1, m);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (!full) mask_block(1);
+        // phase 4
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            prod(1, j);
+            if (j + kPf < NJ) load_tr(1, j + kPf);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
@@ -446,7 +516,15 @@ void bwd_dkdv_kernel(BwdArgs a) {
     auto step = [&](int n, int buf) {
         const bool has_next = n + 1 < total;
         if (has_next) issue_step(n + 1, buf ^ 1);
-        compute(n, buf);
+        const int row0 = (it_lo + n % nt) * kKvBM;
+        const int row1 = min(row0 + kKvBM, s.len_q) - 1;
+        // any visible pair between rows [row0, row1] and keys [kw0, kw1]?  (uniform)
+        if (wave_live && mk.hi_of(row1, s) >= kw0 && mk.lo_of(row0, s) <= kw1) {
+            // all visible: the first row sees the last key and the last row the first key
+            const bool full = row0 + kKvBM <= s.len_q && kw0 + 31 < s.len_k &&
+                              mk.hi_of(row0, s) >= kw0 + 31 && mk.lo_of(row0 + kKvBM - 1, s) <= kw0;
+            compute(n, buf, full);
+        }
         wait_vmcnt<0>();
         __syncthreads();
     };
@@ -479,12 +557,6 @@ void bwd_dkdv_kernel(BwdArgs a) {
         }
 }
 
-template <typename K>
-bool set_smem(K kernel, int bytes) {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, bytes) == hipSuccess;
-}
-
 #ifndef FA_DQ_NW
 #define FA_DQ_NW 8
 #endif
@@ -504,10 +576,8 @@ int launch_bwd_t(const BwdArgs& a, int stage, hipStream_t stream) {
     if (stage == 1) {  // dK, dV
         const int ntiles = (a.seqlen_k + kKvBN - 1) / kKvBN;
         if (ntiles > 0 && a.batch > 0) {
-            static const bool ok = set_smem(bwd_dkdv_kernel<BF16, D>, DkdvCfg<D>::bytes);
-            if (!ok) return 1;
-            hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D>), dim3(a.batch * a.kv_heads, ntiles), dim3(256),
-                               DkdvCfg<D>::bytes, stream, a);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D>), dim3(a.batch * a.kv_heads, ntiles), dim3(256), 0,
+                               stream, a);
             if (hipGetLastError() != hipSuccess) return 1;
         }
         return 0;
@@ -518,10 +588,7 @@ int launch_bwd_t(const BwdArgs& a, int stage, hipStream_t stream) {
     const int ntiles = (a.seqlen_q + BM - 1) / BM;
     if (ntiles > 0 && a.batch > 0) {
         auto kern = bwd_dq_kernel<BF16, D, NW, BN>;
-        constexpr int bytes = DqCfg<D, NW, BN>::bytes;
-        static const bool ok = set_smem(kern, bytes);
-        if (!ok) return 1;
-        hipLaunchKernelGGL(kern, dim3(a.batch * a.heads, ntiles), dim3(64 * NW), bytes, stream, a);
+        hipLaunchKernelGGL(kern, dim3(a.batch * a.heads, ntiles), dim3(64 * NW), 0, stream, a);
         if (hipGetLastError() != hipSuccess) return 1;
     }
     return 0;

@@ -52,7 +52,6 @@ struct FwdCfg {
     static constexpr int kDmaPerWave = kDmaBlocks / NW;
     static constexpr int kRowsPerBlock = 1024 / (D * 2);
     static constexpr int stageElems = 2 * tileElems;  // K then V
-    static constexpr int bytes = 2 * stageElems * 2;
     static_assert(kDmaBlocks % NW == 0, "tiles must split evenly into 1 KiB blocks per wave");
 };
 
@@ -65,7 +64,12 @@ void fwd_kernel(FwdArgs a) {
     constexpr int KB = BN / 32; // 32-key blocks per tile
     constexpr int BM = 32 * QB * NW;
     constexpr int RW = 32 * QB;  // rows per wave
-    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+    // Two LDS stages as separate objects: the compiler can then tell that reads
+    // of one stage never touch the direct loads in flight into the other, and
+    // does not wait for those loads before the transposing reads.
+    __shared__ __attribute__((aligned(16))) uint16_t lds0[C::stageElems];
+    __shared__ __attribute__((aligned(16))) uint16_t lds1[C::stageElems];
+    auto stage = [&](int buf) { return buf ? lds1 : lds0; };
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches below
@@ -155,7 +159,7 @@ void fwd_kernel(FwdArgs a) {
         const bool tail = key0 + BN > s.len_k;  // uniform
         const int last = s.len_k - 1 - key0;
         const int64_t tile_off = (int64_t)key0 * kv_row_stride;
-        uint16_t* kl = smem + buf * C::stageElems;
+        uint16_t* kl = stage(buf);
 #pragma unroll
         for (int i = 0; i < C::kDmaPerWave; ++i) {
             int off = dma_goff[i];
@@ -172,7 +176,7 @@ void fwd_kernel(FwdArgs a) {
     auto compute_tile = [&](int t, int buf) {
         const int key0 = t * BN;
         if (!(wave_live && key0 <= w_key_hi && key0 + BN - 1 >= w_key_lo)) return;
-        const uint16_t* ks_lds = smem + buf * C::stageElems;
+        const uint16_t* ks_lds = stage(buf);
         const uint16_t* vs_lds = ks_lds + C::tileElems;
         // ---- S^T = K Q^T -------------------------------------------------
         f32x16 sacc[KB][QB];
@@ -316,12 +320,8 @@ int launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
     const int ntiles = (a.seqlen_q + BM - 1) / BM;
     if (ntiles == 0 || a.batch == 0) return 0;
     auto kern = fwd_kernel<BF16, D, NW, QB, BN, WPE>;
-    static const bool smem_ok =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            C::bytes) == hipSuccess;
-    if (!smem_ok) return 1;
     dim3 grid(a.batch * a.heads, ntiles);
-    hipLaunchKernelGGL(kern, grid, dim3(C::kThreads), C::bytes, stream, a);
+    hipLaunchKernelGGL(kern, grid, dim3(C::kThreads), 0, stream, a);
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
