@@ -20,7 +20,6 @@ Prints ONE JSON line.  Only one GPU: --gpus above 1 exits with a message.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import subprocess
@@ -36,16 +35,6 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 4096 dense bf16 FLOP/clk/CU x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 WORKLOAD = "bf16_causal_b1_h32_n8192_d128"
 METRIC = "attention fwd+bwd TFLOP/s and % MFMA bf16 peak, seq 8192 d128 causal, 1 GPU"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-CSRC = os.path.join(ROOT, "exact_tiled_attention_10_amd", "csrc")
-KERNEL_SOURCES = {
-    "fwd": ["fa_fwd.hip", "fa_device.hpp"],
-    "bwd_rowdot": ["fa_bwd.hip", "fa_device.hpp"],
-    "bwd_dkdv": ["fa_bwd.hip", "fa_device.hpp"],
-    "bwd_dq": ["fa_bwd.hip", "fa_device.hpp"],
-}
-
-
 def visible_pairs(p) -> int:
     """Number of visible (query, key) pairs summed over sequences (one head)."""
     lens = p.seqlens if p.seqlens is not None else [p.seqlen_q] * p.batch
@@ -62,28 +51,6 @@ def visible_pairs(p) -> int:
         lo = np.maximum(0, pos - p.window_left) if p.window_left >= 0 else np.zeros(lq, dtype=np.int64)
         total += int(np.clip(hi - lo + 1, 0, None).sum())
     return total
-
-
-def source_hash(kernel: str) -> str:
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
-def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
-    when there are none for this kernel/workload or the source changed."""
-    try:
-        with open(TRAFFIC_FILE) as fh:
-            data = json.load(fh)
-    except (OSError, ValueError):
-        return None
-    ent = data.get("kernels", {}).get(kernel)
-    if not ent or ent.get("workload") != workload or ent.get("source_hash") != source_hash(kernel):
-        return None
-    return ent.get("bytes_per_launch")
 
 
 CPU_SAMPLE_HEADS = 4
@@ -126,6 +93,7 @@ def main():
     import torch
     import synth
     import exact_tiled_attention_10_amd as fa
+    from exact_tiled_attention_10_amd.profile_run import measured_traffic
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -189,7 +157,7 @@ def main():
     kd = kernels[dom]
     roofline = {"bound": kd["bound"], "kernel": dom, "achieved": kd["achieved"],
                 "peak": PEAK_BF16_TFLOPS if kd["bound"] == "mfma" else PEAK_HBM_GBS,
-                "unit": kd["unit"], "frac": kd["frac"], "traffic": measured_traffic(dom, WORKLOAD)}
+                "unit": kd["unit"], "frac": kd["frac"], "traffic": measured_traffic(dom.replace("bwd_", ""), WORKLOAD)}
 
     fwd_ms = kern_ms["fwd"]
     bwd_ms = kern_ms["bwd_rowdot"] + kern_ms["bwd_dkdv"] + kern_ms["bwd_dq"]

@@ -25,12 +25,19 @@ FLAGS = [
 # -inf - -inf is guarded), so the max reductions need no NaN canonicalisation.
 # The C-ABI front end keeps full IEEE semantics (it rejects NaN scales).
 KERNEL_FLAGS = ["-fno-honor-nans"]
+# Per-source extras (none at present).
+SOURCE_FLAGS: dict = {}
+
+
+def compile_flags(src: str) -> list:
+    """hipcc flags for one source file (without -c / -o)."""
+    extra = KERNEL_FLAGS if src.endswith(".hip") else []
+    return [*FLAGS, *extra, *SOURCE_FLAGS.get(src, [])]
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    extra = KERNEL_FLAGS if src.endswith(".hip") else []
-    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *compile_flags(src), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

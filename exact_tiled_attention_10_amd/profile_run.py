@@ -1,0 +1,225 @@
+"""Profiling entry points for rocprofv3 runs, and the summaries taken from them.
+
+Subcommands (run from anywhere; the repository root is found from this file):
+
+  run     --workload W --kernel {fwd,rowdot,dkdv,dq} [--iters N]
+          Run one kernel of the library N times on a named synthetic workload
+          (after one untimed call of each earlier stage to produce its inputs).
+          Meant to sit under `rocprofv3 --pmc ...`.
+  copy    [--mib M] [--iters N]
+          Run a plain device copy of M MiB (read M MiB, write M MiB) N times:
+          the calibration for the HBM byte counters.
+  traffic --workload W --kernel K --fetch DIR --write DIR --copy-fetch DIR
+          --copy-write DIR [--mib M]
+          Read the counter CSVs of four `rocprofv3 --pmc` runs (FETCH_SIZE and
+          WRITE_SIZE, for the kernel and for the copy), scale the kernel's
+          counts by the copy's measured/known ratio, and record the bytes per
+          launch in profiles/traffic.json together with the hash of the
+          kernel's sources (bench.py reports the figure only while the hash
+          still matches).
+  trace   --db FILE --title T --command C
+          Print a markdown table of a rocprofv3 kernel-trace database.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sqlite3
+import sys
+from collections import defaultdict
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+# Sources each kernel is built from (the hash ties a counter reading to a build).
+KERNEL_SOURCES = {
+    "fwd": ["fa_fwd.hip", "fa_device.hpp"],
+    "rowdot": ["fa_bwd.hip", "fa_device.hpp"],
+    "dkdv": ["fa_bwd.hip", "fa_device.hpp"],
+    "dq": ["fa_bwd.hip", "fa_device.hpp"],
+}
+# Kernel-name substrings in rocprofv3 output.
+KERNEL_NAMES = {"fwd": "fwd_kernel", "rowdot": "bwd_rowdot_kernel", "dkdv": "bwd_dkdv_kernel",
+                "dq": "bwd_dq_kernel"}
+COPY_NAME = "elementwise"
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch recorded for this kernel and workload, or None when
+    there is no record or the kernel's sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            data = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    ent = data.get("kernels", {}).get(kernel)
+    if not ent or ent.get("workload") != workload or ent.get("source_hash") != source_hash(kernel):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def _run(args):
+    sys.path.insert(0, ROOT)
+    import torch
+    import synth
+    import exact_tiled_attention_10_amd as fa
+
+    p = synth.workload(args.workload)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (t.to(dev) for t in (p.q, p.k, p.v, p.do))
+    cu = p.cu_seqlens()
+    cu = cu.to(dev) if cu is not None else None
+    plan = fa.Plan(q, k, v, do, causal=p.causal, window_size=(p.window_left, p.window_right),
+                   softmax_scale=p.scale, cu_seqlens_q=cu, cu_seqlens_k=cu,
+                   max_seqlen_q=p.seqlen_q, max_seqlen_k=p.seqlen_k)
+    stages = {"fwd": plan.fwd, "rowdot": lambda: plan.bwd_stage(0),
+              "dkdv": lambda: plan.bwd_stage(1), "dq": lambda: plan.bwd_stage(2)}
+    order = ["fwd", "rowdot", "dkdv", "dq"]
+    for name in order[:order.index(args.kernel)]:  # inputs of the profiled stage
+        stages[name]()
+    torch.cuda.synchronize()
+    for _ in range(args.iters):
+        stages[args.kernel]()
+    torch.cuda.synchronize()
+    print(f"ran {args.kernel} x{args.iters} on {args.workload}", flush=True)
+
+
+def _copy(args):
+    import torch
+    n = args.mib * (1 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    for _ in range(args.iters):
+        torch.mul(x, 1.0, out=y)  # an elementwise kernel: reads x once, writes y once
+    torch.cuda.synchronize()
+    print(f"copied {args.mib} MiB x{args.iters}", flush=True)
+
+
+def _counter_per_dispatch(run_dir: str, name_sub: str, counter: str) -> list:
+    """Per-dispatch values (summed over the rows rocprofv3 reports for one
+    dispatch) of `counter` for kernels whose name contains name_sub."""
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
+    per = defaultdict(float)
+    for path in files:
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if name_sub in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                    per[r["Dispatch_Id"]] += float(r["Counter_Value"])
+    if not per:
+        raise ValueError(f"no {counter} rows for kernels matching {name_sub!r} in {run_dir}")
+    return [per[d] for d in sorted(per, key=int)]
+
+
+def _traffic(args):
+    kname = KERNEL_NAMES[args.kernel]
+    kf = _counter_per_dispatch(args.fetch, kname, "FETCH_SIZE")
+    kw = _counter_per_dispatch(args.write, kname, "WRITE_SIZE")
+    cf = _counter_per_dispatch(args.copy_fetch, COPY_NAME, "FETCH_SIZE")
+    cw = _counter_per_dispatch(args.copy_write, COPY_NAME, "WRITE_SIZE")
+    mean = lambda xs: sum(xs) / len(xs)
+    known_kib = args.mib * 1024.0
+    f_fac = known_kib / mean(cf)  # true bytes per counted byte, reads
+    w_fac = known_kib / mean(cw)  # and writes
+    fetch_b = mean(kf) * 1024.0 * f_fac
+    write_b = mean(kw) * 1024.0 * w_fac
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            data = json.load(fh)
+    except (OSError, ValueError):
+        data = {}
+    data.setdefault("kernels", {})[args.kernel] = {
+        "workload": args.workload,
+        "source_hash": source_hash(args.kernel),
+        "bytes_per_launch": round(fetch_b + write_b),
+        "fetch_bytes": round(fetch_b),
+        "write_bytes": round(write_b),
+        "fetch_kib_counted": mean(kf),
+        "write_kib_counted": mean(kw),
+        "calibration": {"copy_mib": args.mib, "fetch_kib_counted": mean(cf), "write_kib_counted": mean(cw),
+                        "fetch_factor": f_fac, "write_factor": w_fac},
+    }
+    data["method"] = ("rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE (separate runs), KiB per dispatch "
+                      "averaged over dispatches, each scaled by known/counted bytes of a plain copy kernel")
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(data, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(json.dumps(data["kernels"][args.kernel], indent=1))
+
+
+def _trace(args):
+    c = sqlite3.connect(args.db)
+    rows = list(c.execute("select name, total_calls, total_duration, average, percentage from top_kernels"))
+    durs = defaultdict(list)
+    info = {}
+    for r in c.execute("select name, duration, grid_x, grid_y, grid_z, workgroup_x, lds_size, scratch_size, "
+                       "vgpr_count, accum_vgpr_count from kernels order by start"):
+        durs[r[0]].append(r[1])
+        info[r[0]] = r[2:]
+    out = [f"# {args.title}", "", "Commands (from the repository root):", "", "```", args.command, "```", "",
+           f"Per kernel: all calls, and the mean of the last {args.last} (the timed steps).", "",
+           f"| kernel | calls | avg (us) | avg last {args.last} (us) | % | grid | WG | LDS (B) | scratch (B) |",
+           "|---|---|---|---|---|---|---|---|---|"]
+    for n, calls, tot, avg, pct in rows:
+        g = info.get(n)
+        short = n.replace("fa::(anonymous namespace)::", "").replace("void ", "")
+        last = durs[n][-args.last:]
+        lavg = sum(last) / len(last) / 1e3  # ns -> us
+        gs = f"{g[0]}x{g[1]}x{g[2]}" if g else ""
+        rest = " | ".join(str(x) for x in g[3:6]) if g else " | " * 2
+        out.append(f"| `{short}` | {calls} | {avg:.1f} | {lavg:.1f} | {pct:.1f} | {gs} | {rest} |")
+    if args.bench_log:
+        with open(args.bench_log) as fh:
+            line = next((l for l in fh if l.startswith('{"metric"')), None)
+        if line:
+            d = json.loads(line)
+            out += ["", "bench.py line of the same run (HIP-event kernel times, ms):", "", "```",
+                    json.dumps({"ms_per_step": d["ms_per_step"], "value": d["value"],
+                                "kernels_ms": {k: v["ms"] for k, v in d["kernels"].items()}}), "```"]
+    print("\n".join(out))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    r = sub.add_parser("run")
+    r.add_argument("--workload", required=True)
+    r.add_argument("--kernel", required=True, choices=list(KERNEL_NAMES))
+    r.add_argument("--iters", type=int, default=3)
+    cp = sub.add_parser("copy")
+    cp.add_argument("--mib", type=int, default=1024)
+    cp.add_argument("--iters", type=int, default=3)
+    t = sub.add_parser("traffic")
+    t.add_argument("--workload", required=True)
+    t.add_argument("--kernel", required=True, choices=list(KERNEL_NAMES))
+    for a in ("--fetch", "--write", "--copy-fetch", "--copy-write"):
+        t.add_argument(a, required=True)
+    t.add_argument("--mib", type=int, default=1024)
+    tr = sub.add_parser("trace")
+    tr.add_argument("--db", required=True)
+    tr.add_argument("--title", required=True)
+    tr.add_argument("--command", required=True)
+    tr.add_argument("--last", type=int, default=5)
+    tr.add_argument("--bench-log", default=None)
+    args = ap.parse_args(argv)
+    {"run": _run, "copy": _copy, "traffic": _traffic, "trace": _trace}[args.cmd](args)
+
+
+if __name__ == "__main__":
+    main()
