@@ -289,12 +289,13 @@ void bwd_dq_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kKvWaves = 4;
 constexpr int kKvBN = 32 * kKvWaves;  // keys per workgroup
-constexpr int kKvBM = 64;             // query rows per streamed tile
+constexpr int kKvBM = 128;            // query rows per streamed tile
+constexpr int kKvQB = kKvBM / 32;     // 32-row blocks per tile
 
 template <int D>
 struct DkdvCfg {
     static constexpr int tileElems = kKvBM * D;
-    // per stage: Q tile, dO tile (16-bit), then lse2[64], D[64] (fp32)
+    // per stage: Q tile, dO tile (16-bit), then lse2[kKvBM], D[kKvBM] (fp32)
     static constexpr int stageBytes = 2 * tileElems * 2 + 2 * kKvBM * 4;
 };
 
@@ -376,28 +377,35 @@ void bwd_dkdv_kernel(BwdArgs a) {
         uint16_t* qt = q_lds(buf);
         dma.issue((const uint16_t*)a.q + hoff, qt, wave, q_stride, tail, last);
         dma.issue((const uint16_t*)a.dout + hoff, qt + C::tileElems, wave, q_stride, tail, last);
-        if (wave < 2) {  // one 4-byte direct load each: lse2 rows, D rows
+        constexpr int kRowLoads = kKvBM / 64;  // 4-byte direct loads (64 rows each) per array
+        static_assert(2 * kRowLoads <= kKvWaves, "one row-term load per wave");
+        if (wave < 2 * kRowLoads) {  // lse2 rows, then D rows
+            const int arr = wave / kRowLoads, part = wave % kRowLoads;
             const int64_t idx0 = a.cu_q ? (int64_t)h * total_q + s.q_start + row0
                                         : ((int64_t)b * a.heads + h) * a.seqlen_q + row0;
-            const float* src = (wave == 0 ? a.lse2 : a.dsum) + idx0 + min(lane, last);
-            dma4(src, lse_lds(buf) + wave * kKvBM);
+            const float* src = (arr == 0 ? a.lse2 : a.dsum) + idx0 + min(64 * part + lane, last);
+            dma4(src, lse_lds(buf) + arr * kKvBM + 64 * part);
         }
     };
 
-    // One step covers a 64-row query tile as two 32-row blocks, software-pipelined
-    // in four phases so that no MFMA waits on an LDS read issued just before it
-    // and the softmax arithmetic of one block runs beside the products of another:
-    //   1: S, dP of block 0                 (operands prefetched kPf reads ahead)
-    //   2: S, dP of block 1  | P, dS of block 0
-    //   3: dV, dK of block 0 | P, dS of block 1
-    //   4: dV, dK of block 1
-    // Scheduling fences keep this order.  P and dS are computed unmasked; on tiles
-    // where not every (row, key) pair is visible (full == false, uniform) the
-    // packed 16-bit words are ANDed with the visibility mask before their
-    // products, a branch that touches nothing but those words.  Masked entries
-    // of rows without any visible key give inf or NaN before the AND, never after.
+    // One step covers a kKvBM-row query tile as kKvQB blocks of 32 rows,
+    // software-pipelined over the blocks: phase ph multiplies S, dP of block
+    // ph and dV, dK of block ph-2 beside the softmax arithmetic (P, dS) of
+    // block ph-1, so the matrix cores and the vector ALU work side by side and
+    // no MFMA waits on an LDS read issued just before it (operands are read
+    // kPf k-steps ahead; the next phase's first reads and the row terms of the
+    // next softmax block are issued during the current phase).  Scheduling
+    // fences keep this order.  P and dS are computed unmasked; on tiles where
+    // not every (row, key) pair is visible (full == false, uniform) the packed
+    // 16-bit words are ANDed with the visibility mask before their products, a
+    // branch that touches nothing but those words.  Masked entries of rows
+    // without any visible key give inf or NaN before the AND, never after.
     auto compute = [&](int n, int buf, bool full) {
-        constexpr int kPf = 4;
+        constexpr int QBS = kKvQB;
+        constexpr int kPf = 2;          // k-steps of operand reads ahead of their MFMAs
+        constexpr int NJ = 4 * DB;      // dV, dK products per block
+        constexpr int JPS = NJ / KS;    // dV, dK products per k-step
+        constexpr int MPS = 8 / KS;     // softmax register pairs per k-step
         const int row0 = (it_lo + n % nt) * kKvBM;
         const uint16_t* qt = q_lds(buf);
         const uint16_t* dot = qt + C::tileElems;
@@ -405,11 +413,11 @@ void bwd_dkdv_kernel(BwdArgs a) {
         const float* dss = lses + kKvBM;
         const int lo = q_lo - row0, hi = q_hi - row0;
 
-        f32x16 sacc[2], dpacc[2];
-        u32x4 qa[2][KS], da[2][KS];  // A operands Q, dO of each block (row r32, k-step ks)
-        f32x4 l4[2][4], d4[2][4];    // lse2 and D of the rows of register group gq
-        uint32_t pp[2][8], dsp[2][8];
-        u32x4 tra[2][4 * DB];        // X^T operands of the dV, dK products, in issue order
+        f32x16 sacc[QBS], dpacc[QBS];
+        u32x4 qa[QBS][KS], da[QBS][KS];  // A operands Q, dO of each block (row r32, k-step ks)
+        f32x4 l4[QBS][4], d4[QBS][4];    // lse2 and D of the rows of register group gq
+        uint32_t pp[QBS][8], dsp[QBS][8];
+        u32x4 tra[QBS][NJ];              // X^T operands of the dV, dK products, in issue order
 
         auto load_ops = [&](int qb, int ks) {
             qa[qb][ks] = *(const u32x4*)(qt + qb * 32 * D + q_rd[ks]);
@@ -452,6 +460,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
             dsp[qb][m] = pack2<BF16>(dv2[0], dv2[1]);
         };
         auto mask_block = [&](int qb) {
+            // Empty, emits nothing; its side effect keeps the compiler from
+            // speculating this edge-tile work out of its branch into every tile.
+            asm volatile("");
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
                 const int r0 = qb * 32 + 8 * (m / 2) + 4 * half + 2 * (m % 2);  // rows of registers 2m, 2m + 1
@@ -461,53 +472,46 @@ void bwd_dkdv_kernel(BwdArgs a) {
                 dsp[qb][m] &= keep;
             }
         };
-        constexpr int NJ = 4 * DB;  // dV, dK products per block
 
-        // phase 1
 #pragma unroll
         for (int ks = 0; ks < kPf; ++ks) load_ops(0, ks);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            sdp(0, ks);
-            if (ks + kPf < KS) load_ops(0, ks + kPf);
-            else load_ops(1, ks + kPf - KS);
-            if (ks >= KS - 2) load_rows(0, ks - (KS - 2));
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // phase 2 (row terms of register group gq are loaded a few slots before use)
+        for (int ph = 0; ph <= QBS + 1; ++ph) {
+            const int bs = ph, bv = ph - 1, bp = ph - 2;  // S/dP, softmax and dV/dK blocks
+            const bool hs = bs < QBS, hv = bv >= 0 && bv < QBS, hp = bp >= 0;
+            if (hp && !full) mask_block(bp);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            sdp(1, ks);
-            if (ks + kPf < KS) load_ops(1, ks + kPf);
-            if (ks == 0) load_rows(0, 2);
-            if (ks == KS / 4) load_rows(0, 3);
-            if (ks == KS / 2) load_rows(1, 0);
-            if (ks == 3 * KS / 4) load_rows(1, 1);
-            if (ks >= KS - kPf) load_tr(0, ks - (KS - kPf));
+            for (int ks = 0; ks < KS; ++ks) {
+                if (hs) sdp(bs, ks);
+                if (hp) {
 #pragma unroll
-            for (int m = ks * 8 / KS; m < (ks + 1) * 8 / KS; ++m) softmax_pair(0, m);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if (!full) mask_block(0);
-        // phase 3
+                    for (int jj = 0; jj < JPS; ++jj) prod(bp, ks * JPS + jj);
+                }
+                if (hs && ks + kPf < KS) load_ops(bs, ks + kPf);
+                if (hp && ks + kPf < KS) {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            prod(0, j);
-            if (j + kPf < NJ) load_tr(0, j + kPf);
-            else load_tr(1, j + kPf - NJ);
-            if (j == 0) load_rows(1, 2);
-            if (j == NJ / 4) load_rows(1, 3);
+                    for (int jj = 0; jj < JPS; ++jj) load_tr(bp, (ks + kPf) * JPS + jj);
+                }
+                // row terms of the softmax block: group gq serves pairs 2 gq, 2 gq + 1,
+                // read one group ahead of its first use
+                if (hv && (ks * MPS) % 2 == 0 && (ks * MPS) / 2 + 1 < 4) load_rows(bv, (ks * MPS) / 2 + 1);
+                if (hv) {
 #pragma unroll
-            for (int m = j * 8 / NJ; m < (j + 1) * 8 / NJ; ++m) softmax_pair(1, m);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if (!full) mask_block(1);
-        // phase 4
+                    for (int m = ks * MPS; m < (ks + 1) * MPS; ++m) softmax_pair(bv, m);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // first operand reads of the next phase: S/dP of block ph+1, dV/dK of block ph-1
+            if (ph + 1 < QBS) {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            prod(1, j);
-            if (j + kPf < NJ) load_tr(1, j + kPf);
+                for (int ks = 0; ks < kPf; ++ks) load_ops(ph + 1, ks);
+            }
+            if (ph - 1 >= 0 && ph - 1 < QBS) {
+#pragma unroll
+                for (int j = 0; j < kPf * JPS; ++j) load_tr(ph - 1, j);
+            }
+            if (ph < QBS) load_rows(ph, 0);  // first row group of the next softmax block
             __builtin_amdgcn_sched_barrier(0);
         }
     };
