@@ -136,11 +136,9 @@ void bwd_dq_kernel(BwdArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r32 = lane & 31, half = lane >> 5;
-    int hb, ty;
-    xcd_grid(hb, ty);
-    const int b = hb / a.heads, h = hb % a.heads;
+    const int b = blockIdx.x / a.heads, h = blockIdx.x % a.heads;
     const int ntiles = gridDim.y;
-    const int qt = a.causal ? (ntiles - 1 - ty) : ty;
+    const int qt = a.causal ? (ntiles - 1 - (int)blockIdx.y) : (int)blockIdx.y;
     const Seq s = seq_of(b, a.cu_q, a.cu_k, a.seqlen_q, a.seqlen_k);
     const int i0 = qt * BM;
     if (i0 >= s.len_q) return;
@@ -315,11 +313,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r32 = lane & 31, half = lane >> 5;
     const int g = a.heads / a.kv_heads;
-    int hb, ty;
-    xcd_grid(hb, ty);
-    const int b = hb / a.kv_heads, hk = hb % a.kv_heads;
+    const int b = blockIdx.x / a.kv_heads, hk = blockIdx.x % a.kv_heads;
     const Seq s = seq_of(b, a.cu_q, a.cu_k, a.seqlen_q, a.seqlen_k);
-    const int j0 = ty * kKvBN;
+    const int j0 = blockIdx.y * kKvBN;
     if (j0 >= s.len_k) return;
     const Mask mk{a.causal, a.left, a.right};
     const int j1 = min(j0 + kKvBN, s.len_k) - 1;

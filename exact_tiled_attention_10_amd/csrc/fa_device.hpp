@@ -175,23 +175,6 @@ __device__ __forceinline__ u32x4 read_tr(const uint16_t* tile, int ks, int mb, c
     return u32x4{l2.x, l2.y, h2.x, h2.y};
 }
 
-// Workgroup numbering.  The dispatcher hands workgroups to the 8 XCDs (each
-// with its own L2) round-robin by linear id.  Renumbering linear id i as
-// (i % 8) * (n / 8) + i / 8 makes the workgroups one XCD runs back to back
-// consecutive in the kernel's logical order, so that, with head-major logical
-// order, the workgroups resident on an XCD at one time share one head's K/V
-// (or Q/dO) tiles in that XCD's L2.  Left as is when n is not a multiple of 8.
-#ifndef FA_XCD
-#define FA_XCD 1
-#endif
-__device__ __forceinline__ void xcd_grid(int& major, int& minor) {
-    const int nx = gridDim.x, ny = gridDim.y, n = nx * ny;
-    int lin = blockIdx.x + blockIdx.y * nx;
-    if (FA_XCD && n % 8 == 0) lin = (lin % 8) * (n / 8) + lin / 8;
-    major = lin / ny;  // grid x extent: batch x heads
-    minor = lin % ny;  // grid y extent: tiles of one head
-}
-
 // Geometry of one (batch, head) problem slice, resolved from cu_seqlens.
 struct Seq {
     int64_t q_start, k_start;  // first packed row of the sequence

@@ -74,11 +74,10 @@ void fwd_kernel(FwdArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches below
     const int r32 = lane & 31, half = lane >> 5;
-    int hb, ty;
-    xcd_grid(hb, ty);
+    const int hb = blockIdx.x;
     const int b = hb / a.heads, h = hb % a.heads;
     const int ntiles = gridDim.y;
-    const int qt = a.causal ? (ntiles - 1 - ty) : ty;  // heavy tiles first
+    const int qt = a.causal ? (ntiles - 1 - (int)blockIdx.y) : (int)blockIdx.y;
     const Seq s = seq_of(b, a.cu_q, a.cu_k, a.seqlen_q, a.seqlen_k);
     const int i0 = qt * BM;
     if (i0 >= s.len_q) return;
