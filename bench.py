@@ -15,6 +15,11 @@ pair.  The roofline object describes the kernel with the largest share of
 the step.  The CPU baseline is the fp64 oracle timed on a bounded sample of
 the same workload (one head, all rows, forward + backward).
 
+A second object, "decode", times the KV-cache decode path on its own
+workload (one new token per sequence, GQA 32/8 heads, ragged caches of
+16K-32K tokens, d 128, bf16): bytes of the valid K/V cache rows read (plus
+q, o and lse) per call / call time, against the 8 TB/s HBM peak.
+
 Prints ONE JSON line.  Only one GPU: --gpus above 1 exits with a message.
 """
 from __future__ import annotations
@@ -54,6 +59,40 @@ def visible_pairs(p) -> int:
 
 
 CPU_SAMPLE_HEADS = 4
+DECODE_WORKLOAD = "bf16_decode_gqa_b8_h32kv8_q1_cache32768_d128"
+
+
+def decode_bytes(p) -> float:
+    """Algorithmic HBM bytes of one decode call: every valid K and V cache row
+    of every kv head read once, q read, o written (16-bit), lse written."""
+    d = p.head_dim
+    kv = 2.0 * sum(p.cache_lens) * p.kv_heads * d * 2
+    qo = 2.0 * p.batch * p.seqlen_q * p.heads * d * 2
+    return kv + qo + 4.0 * p.batch * p.heads * p.seqlen_q
+
+
+def bench_decode(fa, synth, torch, steps: int, warmup: int):
+    dev = torch.device("cuda:0")
+    p = synth.decode_workload(DECODE_WORKLOAD)
+    q, kc, vc = p.q.to(dev), p.k_cache.to(dev), p.v_cache.to(dev)
+    cs = p.cache_seqlens().to(dev)
+    plan = fa.DecodePlan(q, kc, vc, cs, causal=p.causal, softmax_scale=p.scale)
+    for _ in range(warmup):
+        plan.run()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(plan.stream)
+    for i in range(steps):
+        plan.run()
+        ev[i + 1].record(plan.stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]))
+    gbs = decode_bytes(p) / (ms / 1e3) / 1e9
+    return {"workload": DECODE_WORKLOAD, "ms_per_call": round(ms, 4), "bound": "hbm",
+            "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "splits": plan.nsplit,
+            "bytes_per_call": int(decode_bytes(p)),
+            "tokens_per_s": round(p.batch * p.seqlen_q / (ms / 1e3), 1)}
 
 
 def cpu_baseline(p, threads: int):
@@ -83,6 +122,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the KV-cache decode measurement")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (default min(16, cores))")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -190,7 +230,10 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": None,
+        "decode": None,
     }
+    if not args.no_decode:
+        out["decode"] = bench_decode(fa, synth, torch, max(K, 20), max(args.warmup, 3))
     if not args.no_cpu_baseline:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         out["cpu_baseline"] = cpu_baseline(p, threads)

@@ -23,6 +23,8 @@ import torch  # first: libfa.so then binds to the HIP runtime torch already load
 __all__ = [
     "FaError", "lib", "forward", "backward", "Plan", "flash_attn_func",
     "flash_attn_varlen_func", "workspace_size", "FA_DTYPE_F16", "FA_DTYPE_BF16",
+    "forward_kvcache", "kvcache_workspace_size", "kvcache_splits", "DecodePlan",
+    "flash_attn_with_kvcache",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -57,6 +59,12 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd.restype = I
     L.fa_bwd_stage.argtypes = [I] + [P] * 10 + [S] + [P] * 2 + [I] * 9 + [F, I, P]
     L.fa_bwd_stage.restype = I
+    L.fa_fwd_kvcache_workspace_size.argtypes = [I] * 7
+    L.fa_fwd_kvcache_workspace_size.restype = S
+    L.fa_fwd_kvcache.argtypes = [P] * 7 + [S] + [I] * 9 + [F, I, I, P]
+    L.fa_fwd_kvcache.restype = I
+    L.fa_fwd_kvcache_splits.argtypes = [I] * 6
+    L.fa_fwd_kvcache_splits.restype = I
     L.fa_strerror.argtypes = [I]
     L.fa_strerror.restype = ctypes.c_char_p
     L.fa_version.argtypes = []
@@ -297,3 +305,110 @@ def flash_attn_varlen_func(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, ma
         raise NotImplementedError("dropout_p > 0 is not implemented")
     return _FlashAttn.apply(q, k, v, softmax_scale, causal, tuple(window_size),
                             cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+
+
+# ---------------------------------------------------------------------------
+# Decode over a key/value cache
+# ---------------------------------------------------------------------------
+
+def kvcache_workspace_size(batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim, num_splits=0) -> int:
+    """Bytes of workspace fa_fwd_kvcache needs (partial O and LSE per split)."""
+    return int(lib().fa_fwd_kvcache_workspace_size(batch, heads, kv_heads, seqlen_q, seqlen_k,
+                                                   head_dim, num_splits))
+
+
+def kvcache_splits(batch, heads, kv_heads, seqlen_q, seqlen_k, num_splits=0) -> int:
+    """The number of key splits fa_fwd_kvcache uses for these sizes."""
+    return int(lib().fa_fwd_kvcache_splits(batch, heads, kv_heads, seqlen_q, seqlen_k, num_splits))
+
+
+class _DecGeom:
+    def __init__(self, q, k_cache, v_cache, cache_seqlens):
+        if q.dim() != 4 or k_cache.dim() != 4:
+            raise ValueError("q is (batch, seqlen_q, heads, d); caches are (batch, capacity, kv_heads, d)")
+        if k_cache.shape != v_cache.shape:
+            raise ValueError("k_cache and v_cache shapes differ")
+        self.batch, self.seqlen_q, self.heads, self.d = q.shape
+        bk, self.seqlen_k, self.kv_heads, dk = k_cache.shape
+        if bk != self.batch:
+            raise ValueError("q and cache batch sizes differ")
+        if dk != self.d:
+            raise ValueError("q and cache head_dim differ")
+        if cache_seqlens is not None:
+            _check(cache_seqlens, "cache_seqlens", torch.int32, q.device)
+            if cache_seqlens.shape != (self.batch,):
+                raise ValueError("cache_seqlens must hold one int32 per sequence")
+        self.lse_shape = (self.batch, self.heads, self.seqlen_q)
+
+
+def forward_kvcache(q, k_cache, v_cache, cache_seqlens=None, *, causal=False, window_size=(-1, -1),
+                    softmax_scale=None, num_splits=0, out=None, lse=None, workspace=None):
+    """Attention of the new tokens ``q`` over the first ``cache_seqlens[b]``
+    rows of the caches (which already hold the new tokens' keys and values);
+    see include/fa.h.  Returns (out, lse)."""
+    L = lib()
+    dt = q.dtype
+    _check(q, "q"); _check(k_cache, "k_cache", dt, q.device); _check(v_cache, "v_cache", dt, q.device)
+    g = _DecGeom(q, k_cache, v_cache, cache_seqlens)
+    out = torch.empty_like(q) if out is None else out
+    _check(out, "out", dt, q.device)
+    if out.shape != q.shape:
+        raise ValueError("out must have the shape of q")
+    lse = torch.empty(g.lse_shape, dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(lse, "lse", torch.float32, q.device)
+    need = int(L.fa_fwd_kvcache_workspace_size(g.batch, g.heads, g.kv_heads, g.seqlen_q, g.seqlen_k,
+                                               g.d, int(num_splits)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    rc = L.fa_fwd_kvcache(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), _ptr(cache_seqlens),
+                          _ptr(workspace), workspace.numel() * workspace.element_size(),
+                          g.batch, g.heads, g.kv_heads, g.seqlen_q, g.seqlen_k, g.d,
+                          int(bool(causal)), int(window_size[0]), int(window_size[1]),
+                          _default_scale(g.d, softmax_scale), _dtype_code(q), int(num_splits),
+                          _stream(q.device))
+    if rc != 0:
+        raise FaError(rc, "fa_fwd_kvcache")
+    return out, lse
+
+
+def flash_attn_with_kvcache(q, k_cache, v_cache, cache_seqlens=None, softmax_scale=None, causal=False,
+                            window_size=(-1, -1), num_splits=0):
+    """Inference entry with the KV-cache call shape: returns the output only.
+    The new tokens' keys and values must already be in the caches."""
+    return forward_kvcache(q, k_cache, v_cache, cache_seqlens, causal=causal, window_size=window_size,
+                           softmax_scale=softmax_scale, num_splits=num_splits)[0]
+
+
+class DecodePlan:
+    """Pre-resolved fa_fwd_kvcache arguments on fixed buffers (the benchmark
+    loop): ``run()`` enqueues one decode call on ``stream``."""
+
+    def __init__(self, q, k_cache, v_cache, cache_seqlens=None, *, causal=False, window_size=(-1, -1),
+                 softmax_scale=None, num_splits=0, stream=None):
+        L = lib()
+        dt = q.dtype
+        _check(q, "q"); _check(k_cache, "k_cache", dt, q.device); _check(v_cache, "v_cache", dt, q.device)
+        g = _DecGeom(q, k_cache, v_cache, cache_seqlens)
+        self.geom = g
+        self.out = torch.empty_like(q)
+        self.lse = torch.empty(g.lse_shape, dtype=torch.float32, device=q.device)
+        self.nsplit = int(L.fa_fwd_kvcache_splits(g.batch, g.heads, g.kv_heads, g.seqlen_q, g.seqlen_k,
+                                                  int(num_splits)))
+        need = int(L.fa_fwd_kvcache_workspace_size(g.batch, g.heads, g.kv_heads, g.seqlen_q, g.seqlen_k,
+                                                   g.d, int(num_splits)))
+        self.workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        st = stream if stream is not None else torch.cuda.current_stream(q.device)
+        self.stream = st
+        self._keep = (q, k_cache, v_cache, cache_seqlens)
+        self._args = [_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(self.out), _ptr(self.lse),
+                      _ptr(cache_seqlens), _ptr(self.workspace), self.workspace.numel(),
+                      g.batch, g.heads, g.kv_heads, g.seqlen_q, g.seqlen_k, g.d,
+                      int(bool(causal)), int(window_size[0]), int(window_size[1]),
+                      _default_scale(g.d, softmax_scale), _dtype_code(q), int(num_splits),
+                      ctypes.c_void_p(st.cuda_stream)]
+        self._L = L
+
+    def run(self):
+        rc = self._L.fa_fwd_kvcache(*self._args)
+        if rc != 0:
+            raise FaError(rc, "fa_fwd_kvcache")

@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libfa.so")
 BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 ALU forms stay off: plain fp32 code only
@@ -25,8 +25,10 @@ FLAGS = [
 # -inf - -inf is guarded), so the max reductions need no NaN canonicalisation.
 # The C-ABI front end keeps full IEEE semantics (it rejects NaN scales).
 KERNEL_FLAGS = ["-fno-honor-nans"]
-# Per-source extras (none at present).
-SOURCE_FLAGS: dict = {}
+# Per-source extras.  The decode kernel keeps its accumulators in VGPRs:
+# with AGPR accumulators the compiler copies all of them between the two
+# register files on every loop iteration.
+SOURCE_FLAGS: dict = {"fa_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def compile_flags(src: str) -> list:

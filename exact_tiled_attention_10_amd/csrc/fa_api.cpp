@@ -176,6 +176,98 @@ int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const v
                       causal, window_left, window_right, softmax_scale, dtype, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Split of the cache keys for a decode call: `row_blocks` blocks of 32
+// packed (query head, token) rows per kv head and `nsplit` key splits per
+// (batch, kv head), planned on the capacity seqlen_k (the kernel divides
+// each sequence's own length over the same count).  With num_splits <= 0
+// the split count fills about 2048 waves (8 per CU).
+struct DecPlan {
+    int nsplit, row_blocks;
+};
+
+DecPlan dec_plan(int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k, int num_splits) {
+    DecPlan p;
+    const long long rows = (long long)(heads / kv_heads) * seqlen_q;
+    p.row_blocks = (int)((rows + 31) / 32);
+    const int steps = (seqlen_k + 31) / 32;
+    long long ns = num_splits;
+    if (ns <= 0) {
+        const long long units = (long long)batch * kv_heads * (p.row_blocks > 0 ? p.row_blocks : 1);
+        ns = units > 0 ? (2048 + units - 1) / units : 1;
+    }
+    if (ns > 1024) ns = 1024;
+    if (ns > steps) ns = steps;
+    if (ns < 1) ns = 1;
+    const int steps_per = steps > 0 ? (int)((steps + ns - 1) / ns) : 1;
+    p.nsplit = steps > 0 ? (steps + steps_per - 1) / steps_per : 1;
+    return p;
+}
+
+// Partial O first (16-byte aligned rows of head_dim floats), then partial LSE.
+size_t dec_ws_o_elems(const DecPlan& p, int batch, int heads, int seqlen_q, int head_dim) {
+    return (size_t)p.nsplit * (size_t)batch * (size_t)heads * (size_t)seqlen_q * (size_t)head_dim;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fa_fwd_kvcache_workspace_size(int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
+                                     int head_dim, int num_splits) {
+    if (batch < 0 || heads < 1 || kv_heads < 1 || heads % kv_heads != 0 || seqlen_q < 0 || seqlen_k < 0)
+        return 0;
+    if (head_dim != 64 && head_dim != 128) return 0;
+    const DecPlan p = dec_plan(batch, heads, kv_heads, seqlen_q, seqlen_k, num_splits);
+    const size_t rows = (size_t)p.nsplit * (size_t)batch * (size_t)heads * (size_t)seqlen_q;
+    const size_t n = dec_ws_o_elems(p, batch, heads, seqlen_q, head_dim) * sizeof(float) + rows * sizeof(float);
+    return n > 0 ? n : 16;
+}
+
+int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                   const int32_t* cache_seqlens, void* workspace, size_t workspace_bytes,
+                   int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
+                   int head_dim, int causal, int window_left, int window_right,
+                   float softmax_scale, int dtype, int num_splits, void* stream) {
+    int rc = check_common(batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim, causal, window_left,
+                          window_right, softmax_scale, dtype, nullptr, nullptr);
+    if (rc != FA_OK) return rc;
+    const bool has_q = (long long)batch * seqlen_q > 0, has_k = (long long)batch * seqlen_k > 0;
+    if ((has_q && (!q || !o || !lse || !workspace)) || (has_k && (!k_cache || !v_cache)))
+        return FA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
+        !aligned(lse, 4) || !aligned(cache_seqlens, 4) || !aligned(workspace, 16))
+        return FA_ERR_INVALID_ARG;
+    if (has_q && workspace_bytes < fa_fwd_kvcache_workspace_size(batch, heads, kv_heads, seqlen_q, seqlen_k,
+                                                                 head_dim, num_splits))
+        return FA_ERR_WORKSPACE;
+    rc = check_arch();
+    if (rc != FA_OK) return rc;
+    if (!has_q) return FA_OK;
+    const DecPlan p = dec_plan(batch, heads, kv_heads, seqlen_q, seqlen_k, num_splits);
+    fa::DecArgs a;
+    a.q = q; a.kc = k_cache; a.vc = v_cache; a.o = o; a.lse = lse;
+    a.cache_lens = cache_seqlens;
+    a.ws_o = (float*)workspace;
+    a.ws_lse = a.ws_o + dec_ws_o_elems(p, batch, heads, seqlen_q, head_dim);
+    a.batch = batch; a.heads = heads; a.kv_heads = kv_heads;
+    a.seqlen_q = seqlen_q; a.seqlen_k = seqlen_k; a.head_dim = head_dim;
+    a.causal = causal; a.left = window_left; a.right = window_right;
+    a.scale = softmax_scale; a.scale_log2 = log2e_scaled(softmax_scale);
+    a.bf16 = dtype == FA_DTYPE_BF16;
+    a.nsplit = p.nsplit; a.row_blocks = p.row_blocks;
+    return fa::launch_decode(a, (hipStream_t)stream) == 0 ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_fwd_kvcache_splits(int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k, int num_splits) {
+    if (batch < 0 || heads < 1 || kv_heads < 1 || heads % kv_heads != 0 || seqlen_q < 0 || seqlen_k < 0)
+        return 0;
+    return dec_plan(batch, heads, kv_heads, seqlen_q, seqlen_k, num_splits).nsplit;
+}
+
 const char* fa_strerror(int status) {
     switch (status) {
         case FA_OK: return "ok";

@@ -133,11 +133,11 @@ __device__ __forceinline__ void dma4(const void* gsrc, void* lds_dst) {
 
 // s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt left at their
 // maxima): vector memory operations, direct LDS loads included, still in
-// flight <= N.
+// flight <= N.  The 6-bit count is split over bits 3:0 and 15:14.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 16, "vmcnt immediate");
-    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+    static_assert(N >= 0 && N < 64, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 // Per-lane offsets (in 16-bit elements inside the tile) of the transposing

@@ -43,9 +43,29 @@ struct BwdArgs {
     int bf16;
 };
 
+struct DecArgs {
+    const void* q;       // [batch, seqlen_q, heads, D]
+    const void* kc;      // [batch, seqlen_k, kv_heads, D] (seqlen_k = cache capacity)
+    const void* vc;
+    void* o;             // like q
+    float* lse;          // [batch, heads, seqlen_q]
+    const int32_t* cache_lens;  // [batch] valid cache rows, or null (all seqlen_k)
+    float* ws_o;         // [nsplit, batch, heads, seqlen_q, D] partial O, normalised
+    float* ws_lse;       // [nsplit, batch, heads, seqlen_q] partial LSE
+    int batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim;
+    int causal, left, right;
+    float scale;
+    float scale_log2;
+    int bf16;
+    int nsplit;          // key splits per (batch, kv head); each sequence's
+                         // valid keys are divided over them in 32-key steps
+    int row_blocks;      // ceil(heads / kv_heads * seqlen_q / 32)
+};
+
 // Each returns 0 when every launch was accepted, 1 otherwise.  Backward
 // stages: 0 = D_i = dO_i . O_i, 1 = dK/dV pass, 2 = dQ pass.
 int launch_fwd(const FwdArgs& a, hipStream_t stream);
 int launch_bwd(const BwdArgs& a, int stage, hipStream_t stream);
+int launch_decode(const DecArgs& a, hipStream_t stream);
 
 }  // namespace fa

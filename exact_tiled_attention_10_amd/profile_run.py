@@ -2,10 +2,11 @@
 
 Subcommands (run from anywhere; the repository root is found from this file):
 
-  run     --workload W --kernel {fwd,rowdot,dkdv,dq} [--iters N]
+  run     --workload W --kernel {fwd,rowdot,dkdv,dq,decode} [--iters N]
           Run one kernel of the library N times on a named synthetic workload
-          (after one untimed call of each earlier stage to produce its inputs).
-          Meant to sit under `rocprofv3 --pmc ...`.
+          (after one untimed call of each earlier stage to produce its inputs;
+          `decode` runs the KV-cache decode call, split pass and merge, on a
+          named decode workload).  Meant to sit under `rocprofv3 --pmc ...`.
   copy    [--mib M] [--iters N]
           Run a plain device copy of M MiB (read M MiB, write M MiB) N times:
           the calibration for the HBM byte counters.
@@ -43,10 +44,11 @@ KERNEL_SOURCES = {
     "rowdot": ["fa_bwd.hip", "fa_device.hpp"],
     "dkdv": ["fa_bwd.hip", "fa_device.hpp"],
     "dq": ["fa_bwd.hip", "fa_device.hpp"],
+    "decode": ["fa_decode.hip", "fa_device.hpp"],
 }
 # Kernel-name substrings in rocprofv3 output.
 KERNEL_NAMES = {"fwd": "fwd_kernel", "rowdot": "bwd_rowdot_kernel", "dkdv": "bwd_dkdv_kernel",
-                "dq": "bwd_dq_kernel"}
+                "dq": "bwd_dq_kernel", "decode": "decode_split_kernel"}
 COPY_NAME = "elementwise"
 
 
@@ -78,8 +80,19 @@ def _run(args):
     import synth
     import exact_tiled_attention_10_amd as fa
 
-    p = synth.workload(args.workload)
     dev = torch.device("cuda:0")
+    if args.kernel == "decode":
+        p = synth.decode_workload(args.workload)
+        cs = p.cache_seqlens().to(dev)
+        plan = fa.DecodePlan(p.q.to(dev), p.k_cache.to(dev), p.v_cache.to(dev), cs, causal=p.causal,
+                             softmax_scale=p.scale)
+        torch.cuda.synchronize()
+        for _ in range(args.iters):
+            plan.run()
+        torch.cuda.synchronize()
+        print(f"ran decode x{args.iters} on {args.workload}", flush=True)
+        return
+    p = synth.workload(args.workload)
     q, k, v, do = (t.to(dev) for t in (p.q, p.k, p.v, p.do))
     cu = p.cu_seqlens()
     cu = cu.to(dev) if cu is not None else None

@@ -78,7 +78,7 @@ enum fa_status {
     FA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, bad scale   */
     FA_ERR_UNSUPPORTED = 2, /* head_dim not 64/128, or dtype not fp16/bf16        */
     FA_ERR_ARCH = 3,        /* no HIP device, or the current device is not gfx950 */
-    FA_ERR_WORKSPACE = 4,   /* workspace smaller than fa_bwd_workspace_size()     */
+    FA_ERR_WORKSPACE = 4,   /* workspace smaller than the *_workspace_size() call */
     FA_ERR_LAUNCH = 5       /* a kernel launch was rejected by the runtime        */
 };
 
@@ -150,6 +150,53 @@ int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const v
                  int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
                  int head_dim, int causal, int window_left, int window_right,
                  float softmax_scale, int dtype, void* stream);
+
+/*
+ * Decode over a key/value cache (the KV-cache call named on the overview
+ * page, section 3.3, for incremental inference): the same exact attention
+ * as fa_fwd for a few new query tokens per sequence against a long cache,
+ * computed with the keys split over many workgroups and the partial results
+ * merged by their LSE (overview page, section 2.2, online softmax: partial
+ * results over disjoint key sets combine exactly through their row max and
+ * row sum).
+ *   q, o      : [batch, seqlen_q, heads, head_dim], the new tokens
+ *   k_cache,
+ *   v_cache   : [batch, seqlen_k, kv_heads, head_dim]; seqlen_k is the
+ *               cache capacity.  Rows 0 .. cache_seqlens[b]-1 of sequence b
+ *               are its keys; they already include the new tokens' own keys
+ *               (the caller appends them), so query token t of sequence b
+ *               sits at position cache_seqlens[b] - seqlen_q + t (bottom-right
+ *               alignment, as in fa_fwd).
+ *   lse       : [batch, heads, seqlen_q] float32
+ *   cache_seqlens: device int32[batch], or NULL for "every sequence holds
+ *               seqlen_k keys"; values are clamped to 0 .. seqlen_k on the
+ *               device.  Rows past a sequence's length are never used.
+ *   workspace : device memory of at least fa_fwd_kvcache_workspace_size()
+ *               bytes, 16-byte aligned, owned by the caller; contents on
+ *               entry do not matter.  It holds the per-split partial O
+ *               (float32) and LSE.
+ *   num_splits: key splits per (batch, kv head); 0 picks a count that fills
+ *               the device; larger counts are capped at the number of
+ *               32-key steps in seqlen_k and at 1024.
+ * All other arguments, the visibility rule, GQA, the empty-row convention
+ * and the arithmetic are those of fa_fwd, except that P is rounded to 16
+ * bits against each split's own running max and the splits are merged in
+ * float32, so O is not bit-identical to fa_fwd's (both are within rounding
+ * of the exact result).  Two kernels run on `stream`: the split pass and
+ * the merge.  Returns FA_OK or an fa_status code; nothing is enqueued on
+ * error.
+ */
+size_t fa_fwd_kvcache_workspace_size(int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
+                                     int head_dim, int num_splits);
+
+int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                   const int32_t* cache_seqlens, void* workspace, size_t workspace_bytes,
+                   int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
+                   int head_dim, int causal, int window_left, int window_right,
+                   float softmax_scale, int dtype, int num_splits, void* stream);
+
+/* The split count fa_fwd_kvcache uses for these sizes (0 for invalid sizes). */
+int fa_fwd_kvcache_splits(int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k, int num_splits);
 
 /* Static text for a status code ("unknown status" for others). */
 const char* fa_strerror(int status);

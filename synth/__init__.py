@@ -222,3 +222,72 @@ WORKLOADS = {
 
 def workload(name: str, seed: int = 0, with_do: bool = True) -> Problem:
     return make_problem(seed=seed, with_do=with_do, **WORKLOADS[name])
+
+
+@dataclass
+class DecodeProblem:
+    """New query tokens against a key/value cache (CPU tensors).  The caches
+    hold ``capacity`` rows per sequence, of which the first ``cache_lens[b]``
+    are valid and already include the new tokens' own keys and values."""
+    dtype: str
+    batch: int
+    heads: int
+    kv_heads: int
+    seqlen_q: int
+    capacity: int
+    head_dim: int
+    causal: bool
+    window_left: int = -1
+    window_right: int = -1
+    scale: float = 0.0
+    cache_lens: list | None = None
+    q: object = None
+    k_cache: object = None
+    v_cache: object = None
+
+    def cache_seqlens(self):
+        import torch
+        return torch.tensor(self.cache_lens, dtype=torch.int32)
+
+
+def make_decode(*, dtype: str, batch: int, heads: int, kv_heads: int, seqlen_q: int,
+                capacity: int, head_dim: int, causal: bool, window=(-1, -1),
+                scale: float | None = None, factor: float = 1.0, seed: int = 0,
+                len_range=None, cache_lens=None) -> DecodeProblem:
+    """Draw one decode problem.  ``len_range=(lo, hi)`` draws each sequence's
+    cache length uniformly on [lo, hi] (stream 4); ``cache_lens`` gives them
+    explicitly; by default every sequence fills the capacity."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    if cache_lens is not None:
+        lens = [int(x) for x in cache_lens]
+    elif len_range is not None:
+        lens = [int(x) for x in uniform_ints(16 * seed + STREAM_LEN, batch, len_range[0], len_range[1])]
+    else:
+        lens = [capacity] * batch
+    if len(lens) != batch or any(x < 0 or x > capacity for x in lens):
+        raise ValueError("cache lengths must be one per sequence, within the capacity")
+    p = DecodeProblem(dtype=dtype, batch=batch, heads=heads, kv_heads=kv_heads, seqlen_q=seqlen_q,
+                      capacity=capacity, head_dim=head_dim, causal=causal, window_left=window[0],
+                      window_right=window[1], scale=scale, cache_lens=lens)
+    p.q = tensor(seed, STREAM_Q, (batch, seqlen_q, heads, head_dim), dtype, factor)
+    p.k_cache = tensor(seed, STREAM_K, (batch, capacity, kv_heads, head_dim), dtype, factor)
+    p.v_cache = tensor(seed, STREAM_V, (batch, capacity, kv_heads, head_dim), dtype, factor)
+    return p
+
+
+# Decode workloads: one new token per sequence of a GQA model with a long,
+# ragged cache (the inference half of the long-context shape above), and a
+# block of 8 new tokens per sequence on the same caches.
+DECODE_WORKLOADS = {
+    "bf16_decode_gqa_b8_h32kv8_q1_cache32768_d128": dict(
+        dtype="bf16", batch=8, heads=32, kv_heads=8, seqlen_q=1, capacity=32768, head_dim=128,
+        causal=True, factor=0.5, len_range=(16384, 32768)),
+    "bf16_decode_gqa_b8_h32kv8_q8_cache32768_d128": dict(
+        dtype="bf16", batch=8, heads=32, kv_heads=8, seqlen_q=8, capacity=32768, head_dim=128,
+        causal=True, factor=0.5, len_range=(16384, 32768)),
+}
+
+
+def decode_workload(name: str, seed: int = 0) -> DecodeProblem:
+    return make_decode(seed=seed, **DECODE_WORKLOADS[name])

@@ -38,7 +38,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_fwd",
-                                    "fa_strerror", "fa_version"]
+                                    "fa_fwd_kvcache", "fa_fwd_kvcache_splits",
+                                    "fa_fwd_kvcache_workspace_size", "fa_strerror", "fa_version"]
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -153,3 +154,76 @@ def test_python_binding_fails_loudly_without_gpu_tensors():
     q = torch.zeros(1, 8, 2, 64, dtype=torch.float16)
     with pytest.raises(ValueError, match="GPU"):
         fa.forward(q, q, q)
+
+
+# ---------------------------------------------------------------------------
+# Decode over a key/value cache
+# ---------------------------------------------------------------------------
+
+def dec(L, **over):
+    args = dict(q=FAKE[0], kc=FAKE[1], vc=FAKE[2], o=FAKE[3], lse=FAKE[4], lens=FAKE[5], ws=FAKE[6],
+                wsb=1 << 24, batch=2, heads=8, kv_heads=2, seqlen_q=1, seqlen_k=4096, head_dim=128,
+                causal=1, left=-1, right=-1, scale=0.125, dtype=1, splits=0, stream=None)
+    args.update(over)
+    return L.fa_fwd_kvcache(args["q"], args["kc"], args["vc"], args["o"], args["lse"], args["lens"],
+                            args["ws"], args["wsb"], args["batch"], args["heads"], args["kv_heads"],
+                            args["seqlen_q"], args["seqlen_k"], args["head_dim"], args["causal"],
+                            args["left"], args["right"], args["scale"], args["dtype"], args["splits"],
+                            args["stream"])
+
+
+BAD_DEC = [
+    (dict(q=None), INVALID), (dict(kc=None), INVALID), (dict(vc=None), INVALID), (dict(o=None), INVALID),
+    (dict(lse=None), INVALID), (dict(ws=None), INVALID),
+    (dict(ws=ctypes.c_void_p(0x10008)), INVALID),        # workspace must be 16-byte aligned
+    (dict(lens=ctypes.c_void_p(0x10002)), INVALID),
+    (dict(kc=ctypes.c_void_p(0x10008)), INVALID),
+    (dict(heads=6, kv_heads=4), INVALID), (dict(seqlen_q=-1), INVALID), (dict(causal=3), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(left=-7), INVALID),
+    (dict(head_dim=80), UNSUPPORTED), (dict(dtype=5), UNSUPPORTED),
+    (dict(wsb=16), WORKSPACE),
+]
+
+
+@pytest.mark.parametrize("over,code", BAD_DEC)
+def test_kvcache_rejects_bad_arguments(L, over, code):
+    assert dec(L, **over) == code
+
+
+def test_kvcache_split_plan(L):
+    splits, size = L.fa_fwd_kvcache_splits, L.fa_fwd_kvcache_workspace_size
+    # auto: about 2048 waves over (batch, kv head, row block) units, at most one split per 32 keys
+    assert splits(8, 32, 8, 1, 32768, 0) == 32
+    assert splits(1, 2, 2, 1, 100, 0) == 4          # 100 keys = 4 steps of 32
+    assert splits(1, 32, 8, 1, 0, 0) == 1           # empty cache
+    assert splits(2, 8, 2, 1, 4096, 5) == 5
+    assert splits(2, 8, 2, 1, 4096, 5000) == 128    # capped at the step count
+    assert splits(1, 8, 2, 1, 1 << 20, 5000) == 1024  # and at 1024
+    assert splits(1, 3, 2, 1, 64, 0) == 0          # invalid sizes
+    # chunks are whole 32-key steps: 100 steps over 7 splits -> 15 steps each -> 7 splits
+    assert splits(1, 8, 2, 1, 3200, 7) == 7
+    assert splits(1, 8, 2, 1, 3200, 8) == 8         # 13 steps each, the last one 9
+    assert splits(1, 8, 2, 1, 3200, 9) == 9
+    assert splits(1, 8, 2, 1, 3200, 11) == 10       # 10 steps each -> only 10 splits needed
+    # workspace = splits x batch x heads x seqlen_q x (head_dim + 1) floats
+    for b, h, hk, nq, nk, d, ns in [(8, 32, 8, 1, 32768, 128, 0), (2, 16, 2, 8, 1000, 64, 3), (1, 4, 1, 16, 33, 128, 0)]:
+        n = splits(b, h, hk, nq, nk, ns)
+        assert size(b, h, hk, nq, nk, d, ns) == n * b * h * nq * (d + 1) * 4
+    assert size(0, 4, 2, 1, 100, 64, 0) == 16
+    assert size(1, 4, 2, 1, 100, 96, 0) == 0 and size(1, 4, 3, 1, 100, 64, 0) == 0
+
+
+@no_gpu
+def test_kvcache_valid_call_without_gfx950_reports_arch(L):
+    assert dec(L) == ARCH
+    assert dec(L, lens=None) == ARCH                    # every sequence fills the capacity
+    assert dec(L, kc=None, vc=None, seqlen_k=0) == ARCH  # empty caches may be NULL
+    assert dec(L, q=None, o=None, lse=None, ws=None, seqlen_q=0) == ARCH
+
+
+def test_kvcache_binding_fails_loudly_without_gpu_tensors():
+    import exact_tiled_attention_10_amd as fa
+    q = torch.zeros(1, 1, 2, 64, dtype=torch.float16)
+    kc = torch.zeros(1, 16, 2, 64, dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU"):
+        fa.forward_kvcache(q, kc, kc)
