@@ -63,7 +63,7 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd_kvcache_workspace_size.restype = S
     L.fa_fwd_kvcache.argtypes = [P] * 7 + [S] + [I] * 9 + [F, I, I, P]
     L.fa_fwd_kvcache.restype = I
-    L.fa_fwd_kvcache_splits.argtypes = [I] * 6
+    L.fa_fwd_kvcache_splits.argtypes = [I] * 7
     L.fa_fwd_kvcache_splits.restype = I
     L.fa_strerror.argtypes = [I]
     L.fa_strerror.restype = ctypes.c_char_p
@@ -317,9 +317,9 @@ def kvcache_workspace_size(batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim,
                                                    head_dim, num_splits))
 
 
-def kvcache_splits(batch, heads, kv_heads, seqlen_q, seqlen_k, num_splits=0) -> int:
-    """The number of key splits fa_fwd_kvcache uses for these sizes."""
-    return int(lib().fa_fwd_kvcache_splits(batch, heads, kv_heads, seqlen_q, seqlen_k, num_splits))
+def kvcache_splits(batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim, num_splits=0) -> int:
+    """The number of waves fa_fwd_kvcache's split pass uses for these sizes."""
+    return int(lib().fa_fwd_kvcache_splits(batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim, num_splits))
 
 
 class _DecGeom:
@@ -393,7 +393,7 @@ class DecodePlan:
         self.out = torch.empty_like(q)
         self.lse = torch.empty(g.lse_shape, dtype=torch.float32, device=q.device)
         self.nsplit = int(L.fa_fwd_kvcache_splits(g.batch, g.heads, g.kv_heads, g.seqlen_q, g.seqlen_k,
-                                                  int(num_splits)))
+                                                  g.d, int(num_splits)))
         need = int(L.fa_fwd_kvcache_workspace_size(g.batch, g.heads, g.kv_heads, g.seqlen_q, g.seqlen_k,
                                                    g.d, int(num_splits)))
         self.workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)

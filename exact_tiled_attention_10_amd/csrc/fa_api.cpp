@@ -180,37 +180,47 @@ int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const v
 
 namespace {
 
-// Split of the cache keys for a decode call: `row_blocks` blocks of 32
-// packed (query head, token) rows per kv head and `nsplit` key splits per
-// (batch, kv head), planned on the capacity seqlen_k (the kernel divides
-// each sequence's own length over the same count).  With num_splits <= 0
-// the split count fills about 2048 waves (8 per CU).
+// Work split of a decode call: `row_blocks` blocks of 32 packed (query head,
+// token) rows per kv head; a segment is one (sequence, row block), so there
+// are batch * row_blocks segments, and the visible steps of all of them are
+// divided evenly over `waves / kv_heads` groups of kv_heads waves (one per
+// kv head).  num_splits > 0 asks for num_splits waves per (sequence, kv
+// head, row block) on average; otherwise about kDecAutoWaves waves, two per
+// CU, which measured faster than filling every SIMD: the split pass is
+// bound by HBM, and fewer concurrent streams keep more DRAM pages open.
+// Never more groups than segment-steps at full capacity, and at most 65536
+// waves.
+constexpr long long kDecAutoWaves = 512;
 struct DecPlan {
-    int nsplit, row_blocks;
+    int waves, row_blocks;
+    long long segments;  // batch * row_blocks
 };
 
-DecPlan dec_plan(int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k, int num_splits) {
+DecPlan dec_plan(int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k, int head_dim, int num_splits) {
     DecPlan p;
     const long long rows = (long long)(heads / kv_heads) * seqlen_q;
     p.row_blocks = (int)((rows + 31) / 32);
-    const int steps = (seqlen_k + 31) / 32;
-    long long ns = num_splits;
-    if (ns <= 0) {
-        const long long units = (long long)batch * kv_heads * (p.row_blocks > 0 ? p.row_blocks : 1);
-        ns = units > 0 ? (2048 + units - 1) / units : 1;
-    }
-    if (ns > 1024) ns = 1024;
-    if (ns > steps) ns = steps;
-    if (ns < 1) ns = 1;
-    const int steps_per = steps > 0 ? (int)((steps + ns - 1) / ns) : 1;
-    p.nsplit = steps > 0 ? (steps + steps_per - 1) / steps_per : 1;
+    p.segments = (long long)batch * p.row_blocks;
+    long long groups = num_splits > 0 ? (long long)num_splits * p.segments
+                                      : kDecAutoWaves / kv_heads;
+    const long long max_useful = p.segments * ((seqlen_k + 31) / 32);
+    if (groups > max_useful) groups = max_useful;
+    if (groups > 65536 / kv_heads) groups = 65536 / kv_heads;
+    if (groups < 1) groups = 1;
+    p.waves = (int)(groups * kv_heads);
     return p;
 }
 
-// Partial O first (16-byte aligned rows of head_dim floats), then partial LSE.
-size_t dec_ws_o_elems(const DecPlan& p, int batch, int heads, int seqlen_q, int head_dim) {
-    return (size_t)p.nsplit * (size_t)batch * (size_t)heads * (size_t)seqlen_q * (size_t)head_dim;
+// Workspace layout: partial O [slots, 32, head_dim] floats, partial LSE
+// [slots, 32] floats, prefix sums [batch + 1] int64, with
+// slots = (groups + segments) * kv_heads.
+size_t dec_slots(const DecPlan& p, int kv_heads) {
+    return (size_t)(p.waves / kv_heads + p.segments) * (size_t)kv_heads;
 }
+size_t dec_ws_o_elems(const DecPlan& p, int kv_heads, int head_dim) {
+    return dec_slots(p, kv_heads) * 32 * (size_t)head_dim;
+}
+size_t dec_ws_lse_elems(const DecPlan& p, int kv_heads) { return dec_slots(p, kv_heads) * 32; }
 
 }  // namespace
 
@@ -221,10 +231,9 @@ size_t fa_fwd_kvcache_workspace_size(int batch, int heads, int kv_heads, int seq
     if (batch < 0 || heads < 1 || kv_heads < 1 || heads % kv_heads != 0 || seqlen_q < 0 || seqlen_k < 0)
         return 0;
     if (head_dim != 64 && head_dim != 128) return 0;
-    const DecPlan p = dec_plan(batch, heads, kv_heads, seqlen_q, seqlen_k, num_splits);
-    const size_t rows = (size_t)p.nsplit * (size_t)batch * (size_t)heads * (size_t)seqlen_q;
-    const size_t n = dec_ws_o_elems(p, batch, heads, seqlen_q, head_dim) * sizeof(float) + rows * sizeof(float);
-    return n > 0 ? n : 16;
+    const DecPlan p = dec_plan(batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim, num_splits);
+    return (dec_ws_o_elems(p, kv_heads, head_dim) + dec_ws_lse_elems(p, kv_heads)) * sizeof(float) +
+           ((size_t)batch + 1) * sizeof(int64_t);
 }
 
 int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
@@ -247,25 +256,28 @@ int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, void
     rc = check_arch();
     if (rc != FA_OK) return rc;
     if (!has_q) return FA_OK;
-    const DecPlan p = dec_plan(batch, heads, kv_heads, seqlen_q, seqlen_k, num_splits);
+    const DecPlan p = dec_plan(batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim, num_splits);
     fa::DecArgs a;
     a.q = q; a.kc = k_cache; a.vc = v_cache; a.o = o; a.lse = lse;
     a.cache_lens = cache_seqlens;
     a.ws_o = (float*)workspace;
-    a.ws_lse = a.ws_o + dec_ws_o_elems(p, batch, heads, seqlen_q, head_dim);
+    a.ws_lse = a.ws_o + dec_ws_o_elems(p, kv_heads, head_dim);
+    a.prefix = (int64_t*)(a.ws_lse + dec_ws_lse_elems(p, kv_heads));
     a.batch = batch; a.heads = heads; a.kv_heads = kv_heads;
     a.seqlen_q = seqlen_q; a.seqlen_k = seqlen_k; a.head_dim = head_dim;
     a.causal = causal; a.left = window_left; a.right = window_right;
     a.scale = softmax_scale; a.scale_log2 = log2e_scaled(softmax_scale);
     a.bf16 = dtype == FA_DTYPE_BF16;
-    a.nsplit = p.nsplit; a.row_blocks = p.row_blocks;
+    a.waves = p.waves; a.row_blocks = p.row_blocks;
     return fa::launch_decode(a, (hipStream_t)stream) == 0 ? FA_OK : FA_ERR_LAUNCH;
 }
 
-int fa_fwd_kvcache_splits(int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k, int num_splits) {
+int fa_fwd_kvcache_splits(int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k, int head_dim,
+                          int num_splits) {
     if (batch < 0 || heads < 1 || kv_heads < 1 || heads % kv_heads != 0 || seqlen_q < 0 || seqlen_k < 0)
         return 0;
-    return dec_plan(batch, heads, kv_heads, seqlen_q, seqlen_k, num_splits).nsplit;
+    if (head_dim != 64 && head_dim != 128) return 0;
+    return dec_plan(batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim, num_splits).waves;
 }
 
 const char* fa_strerror(int status) {

@@ -1,22 +1,34 @@
 // Decode: exact attention of a short block of new query tokens over a long
 // key/value cache (the KV-cache entry of the FlashAttention-2 overview page,
-// lshu.cn/news/55956, section 3.3), split over the keys.
+// lshu.cn/news/55956, section 3.3), split over the keys and merged through
+// the online-softmax statistics (same page, section 2.2).
 //
 // The work is bound by reading the cache once, so the kernel is organised for
 // memory-level parallelism rather than matrix-core rate:
-//   * one wave per (batch, kv head, key split, row block); the g query heads
-//     that share the kv head and the Nq new tokens are packed into blocks of
-//     32 rows (row r = (head r / Nq, token r % Nq)), so a cache byte is read
-//     once per kv head (per 32 such rows), not once per query head;
-//   * each wave streams its split in 32-key steps through its own two LDS
-//     stages with direct global -> LDS loads, waiting only on its own loads
-//     (no workgroup barriers);
+//   * the g query heads sharing a kv head and the Nq new tokens are packed
+//     into blocks of 32 rows (row r = (head r / Nq, token r % Nq)), so a
+//     cache byte is read once per kv head (per 32 such rows), not once per
+//     query head;
+//   * a segment is one (sequence b, row block).  The visible 32-key steps of
+//     all segments, laid end to end, are divided evenly over groups of
+//     kv_heads waves, whatever the sequence lengths; wave hk of a group
+//     takes kv head hk.  The waves of a group read neighbouring pieces of
+//     the same cache rows at the same time (kept in step by their equal
+//     work), which keeps DRAM pages open.  A group's range may span the end
+//     of one segment and the start of the next; each wave writes one partial
+//     result (O normalised, LSE) per piece.  Piece (group j, segment s) of
+//     kv head hk goes to slot (j + s) * kv_heads + hk: groups and segments
+//     both advance along the same axis, so no two pieces share a slot;
+//   * inside a piece the loads of K and V run kDecAhead steps ahead into
+//     registers (coalesced 16-byte loads; the register file is far larger
+//     than LDS, so many bytes are in flight per CU); at its turn a step is
+//     written to the wave's own LDS tiles, from which the matrix-core
+//     operands are read (V^T by transposing reads).  LDS operations of one
+//     wave execute in order, so no barrier is needed;
 //   * per step: S^T = K Q^T on the matrix cores, the online softmax per query
-//     column (lazy rescale, as in the forward kernel), O^T += V^T P^T with V^T
-//     from transposing LDS reads;
-//   * each split writes its normalised partial O (fp32) and LSE; a second
-//     kernel merges the splits by their LSE: LSE = log sum_s e^{LSE_s},
-//     O = sum_s e^{LSE_s - LSE} O_s.
+//     column (lazy rescale, as in the forward kernel), O^T += V^T P^T;
+//   * a second kernel merges, for every output row, the pieces of its
+//     segment: LSE = log sum_p e^{LSE_p}, O = sum_p e^{LSE_p - LSE} O_p.
 // Masking, alignment and empty-row conventions are those of the forward
 // (bottom-right causal alignment, inclusive windows, O = 0 and LSE = -inf
 // for a row without visible keys).
@@ -31,86 +43,130 @@ namespace fa {
 namespace {
 
 constexpr float kDecLazyLog2 = 8.0f;
-constexpr int kDecWaves = 4;  // splits per workgroup, one per wave
 constexpr int kDecBK = 32;    // keys per step
+constexpr int kDecAhead = 3;  // steps whose loads are in flight
 
 template <int D>
 struct DecCfg {
-    static constexpr int CPR = D / 8;
-    static constexpr int tileElems = kDecBK * D;          // one K or V tile
-    static constexpr int kDma = tileElems * 2 / 1024;     // 1 KiB direct loads per tile
-    static constexpr int kRowsPerBlock = 1024 / (2 * D);  // cache rows per direct load
+    static constexpr int CPR = D / 8;                  // 16-byte chunks per cache row
+    static constexpr int tileElems = kDecBK * D;       // one K or V tile
+    static constexpr int kLd = tileElems * 2 / 1024;   // 16-byte loads per lane per tile
+    static constexpr int kRowsPerLd = 1024 / (2 * D);  // cache rows per wave load
 };
 
+// Valid keys of sequence b.
+__device__ __forceinline__ int dec_len(const DecArgs& a, int b) {
+    const int len = a.cache_lens ? a.cache_lens[b] : a.seqlen_k;
+    return min(max(len, 0), a.seqlen_k);
+}
+
+__device__ __forceinline__ Seq dec_seq(const DecArgs& a, int b, int len) {
+    Seq s;
+    s.q_start = (int64_t)b * a.seqlen_q;
+    s.k_start = (int64_t)b * a.seqlen_k;
+    s.len_q = a.seqlen_q;
+    s.len_k = len;
+    s.off = len - a.seqlen_q;
+    return s;
+}
+
+// Steps a segment of sequence b walks: from the 32-key step holding the first
+// key any new token sees to the one holding the last (tokens 0 and Nq-1 bound
+// the range, the visible interval moving right with the token).
+__device__ __forceinline__ void dec_steps(const DecArgs& a, int b, int& st_lo, int& n) {
+    const Seq s = dec_seq(a, b, dec_len(a, b));
+    const Mask mk{a.causal, a.left, a.right};
+    const int lo = mk.lo_of(0, s), hi = mk.hi_of(a.seqlen_q - 1, s);
+    st_lo = lo / kDecBK;
+    n = lo <= hi ? hi / kDecBK + 1 - st_lo : 0;
+}
+
+// Group holding position pos of the step axis: group j of G covers
+// [floor(j T / G), floor((j + 1) T / G)).
+__device__ __forceinline__ int64_t dec_group_of(int64_t pos, int64_t T, int G) {
+    return ((pos + 1) * G - 1) / T;
+}
+
+// Inclusive prefix sum over the wave's lanes.
+__device__ __forceinline__ int64_t wave_scan(int64_t x, int lane) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int64_t y = __shfl_up(x, d, 64);
+        x += lane >= d ? y : 0;
+    }
+    return x;
+}
+
 template <bool BF16, int D>
-__global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(DecArgs a) {
+__global__ __launch_bounds__(64) void decode_split_kernel(DecArgs a) {
     using C = DecCfg<D>;
     constexpr int KS = D / 16, DB = D / 32;
-    // Two stages per tensor as separate objects (one slice per wave): reads of
-    // one stage are then known not to touch the loads in flight into the other.
-    __shared__ __attribute__((aligned(16))) uint16_t kst0[kDecWaves][C::tileElems];
-    __shared__ __attribute__((aligned(16))) uint16_t kst1[kDecWaves][C::tileElems];
-    __shared__ __attribute__((aligned(16))) uint16_t vst0[kDecWaves][C::tileElems];
-    __shared__ __attribute__((aligned(16))) uint16_t vst1[kDecWaves][C::tileElems];
+    __shared__ __attribute__((aligned(16))) uint16_t kt[C::tileElems];
+    __shared__ __attribute__((aligned(16))) uint16_t vt[C::tileElems];
 
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x;
     const int r32 = lane & 31, half = lane >> 5;
-    const int b = blockIdx.x / a.kv_heads, hk = blockIdx.x % a.kv_heads;
-    const int sp = blockIdx.y * kDecWaves + wave;
-    const int rb = blockIdx.z;
-    if (sp >= a.nsplit) return;  // whole wave; no barrier below
-    auto kst = [&](int p) { return p ? kst1[wave] : kst0[wave]; };
-    auto vst = [&](int p) { return p ? vst1[wave] : vst0[wave]; };
+    const int grp = blockIdx.x / a.kv_heads, hk = blockIdx.x % a.kv_heads;
+    const int G = a.waves / a.kv_heads;  // groups
+    const int HR = a.row_blocks;          // segments per sequence
 
+    // ---- this wave's range of the step axis -----------------------------------
+    // Sum of steps over the sequences, then (second pass) the sequence holding
+    // the range's first step.  The first wave also records the prefix sums of
+    // the per-sequence step counts for the merge kernel.
+    int n_first = 0;  // first 64 sequences: kept for the second pass
+    {
+        int st_lo;
+        if (lane < a.batch) dec_steps(a, lane, st_lo, n_first);
+    }
+    int64_t total = n_first;
+    for (int c0 = 64; c0 < a.batch; c0 += 64) {
+        int st_lo = 0, n = 0;
+        if (c0 + lane < a.batch) dec_steps(a, c0 + lane, st_lo, n);
+        total += n;
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) total += __shfl_xor(total, d, 64);
+    const int64_t T = total * HR;
+    const int64_t pos0 = T * grp / G, pos1 = T * (grp + 1) / G;
+    int b = -1;
+    int64_t seq_base = 0;  // step-axis position of sequence b's first segment
+    {
+        int64_t carry = 0;
+        for (int c0 = 0; c0 < a.batch; c0 += 64) {
+            const int bb = c0 + lane;
+            int st_lo = 0, n = n_first;
+            if (c0 > 0 && bb < a.batch) dec_steps(a, bb, st_lo, n);
+            const int64_t incl = carry + wave_scan(n, lane), excl = incl - n;
+            if (blockIdx.x == 0 && bb < a.batch) a.prefix[bb] = excl;
+            const bool here = bb < a.batch && n > 0 && excl * HR <= pos0 && pos0 < incl * HR;
+            const uint64_t m = __builtin_amdgcn_ballot_w64(here);
+            if (b < 0 && m) {
+                const int src = __builtin_ctzll(m);
+                b = c0 + src;
+                seq_base = __shfl(excl, src, 64) * HR;
+            }
+            carry = __shfl(incl, 63, 64);
+        }
+        if (blockIdx.x == 0 && lane == 0) a.prefix[a.batch] = carry;
+    }
+    if (pos0 >= pos1) return;  // empty range (more groups than steps)
+
+    // ---- per-lane constants ------------------------------------------------------
     const int g = a.heads / a.kv_heads;
     const int nq = a.seqlen_q;
     const int rows = g * nq;
-    int len_k = a.cache_lens ? a.cache_lens[b] : a.seqlen_k;
-    len_k = min(max(len_k, 0), a.seqlen_k);
-    Seq s;
-    s.q_start = (int64_t)b * nq;
-    s.k_start = (int64_t)b * a.seqlen_k;
-    s.len_q = nq;
-    s.len_k = len_k;
-    s.off = len_k - nq;
     const Mask mk{a.causal, a.left, a.right};
-
-    // this lane's row: query head hq, token t
-    const int rr = rb * 32 + r32;
-    const bool live = rr < rows;
-    const int t = live ? rr % nq : 0;
-    const int hq = hk * g + (live ? rr / nq : 0);
-    const int lo_q = mk.lo_of(t, s), hi_q = live ? mk.hi_of(t, s) : -1;
-    // This sequence's keys split in whole 32-key steps over the nsplit waves,
-    // so every split of a sequence does the same work whatever its length.
-    const int chunk = kDecBK * (((len_k + kDecBK - 1) / kDecBK + a.nsplit - 1) / a.nsplit);
-    const int k_begin = sp * chunk;
-    const int k_end = min(k_begin + chunk, len_k);  // exclusive
-    const int vis_lo = max(k_begin, mk.lo_of(0, s));
-    const int vis_hi = min(k_end - 1, mk.hi_of(nq - 1, s));
-    // no row of the block needs a mask inside [full_lo, full_hi] (uniform)
-    const int full_lo = max(k_begin, mk.lo_of(nq - 1, s));
-    const int full_hi = min(k_end - 1, mk.hi_of(0, s));
-
     const int kv_stride = a.kv_heads * D;
-    u32x4 qf[KS];
-    {
-        const uint16_t* qrow = (const uint16_t*)a.q + ((s.q_start + t) * a.heads + hq) * D;
+    const float c = a.scale_log2;
+    // load i of a tile: lane reads chunk lane % CPR of row i * kRowsPerLd + lane / CPR
+    // and later writes it to that row's swizzled slot in LDS
+    const int ld_r = lane / C::CPR, ld_c = lane % C::CPR;
+    int st_off[C::kLd];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            qf[ks] = live ? *(const u32x4*)(qrow + ks * 16 + 8 * half) : u32x4{0, 0, 0, 0};
-    }
-    const uint16_t* kbase = (const uint16_t*)a.kc + (s.k_start * a.kv_heads + hk) * D;
-    const uint16_t* vbase = (const uint16_t*)a.vc + (s.k_start * a.kv_heads + hk) * D;
-
-    // direct loads: block i covers cache rows i * kRowsPerBlock + lane / CPR
-    const int dma_r = lane / C::CPR;
-    int dma_off[C::kDma];
-#pragma unroll
-    for (int i = 0; i < C::kDma; ++i) {
-        const int row = i * C::kRowsPerBlock + dma_r;
-        dma_off[i] = ((lane % C::CPR) ^ swz<C::CPR>(row)) * 8;
+    for (int i = 0; i < C::kLd; ++i) {
+        const int row = i * C::kRowsPerLd + ld_r;
+        st_off[i] = row * D + ((ld_c ^ swz<C::CPR>(row)) * 8);
     }
     int k_rd[KS];
 #pragma unroll
@@ -118,134 +174,216 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(DecArgs a)
     int v_rd[2][DB];
     tr_offsets<D, DB>(lane, v_rd);
 
-    f32x16 acc[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db) acc[db] = f32x16{0};
-    float m_run = kNegInf, l_part = 0.f;
-    const float c = a.scale_log2;
+    // ---- pieces -------------------------------------------------------------------
+    int st_lo, n;
+    dec_steps(a, b, st_lo, n);
+    int64_t pos = pos0;
+    int seg = (int)((pos - seq_base) / n);  // segment (row block) inside sequence b
+    int off = (int)((pos - seq_base) % n);  // first step inside it
+    while (true) {
+        const int cnt = (int)min((int64_t)(n - off), pos1 - pos);
+        const int rb = seg;
+        const int64_t slot = ((int64_t)grp + (int64_t)b * HR + seg) * a.kv_heads + hk;
 
-    auto issue = [&](int st, int p) {
-        const int key0 = st * kDecBK;
+        const int len_k = dec_len(a, b);
+        const Seq s = dec_seq(a, b, len_k);
+        // this lane's row: query head hq, token t
+        const int rr = rb * 32 + r32;
+        const bool live = rr < rows;
+        const int t = live ? rr % nq : 0;
+        const int hq = hk * g + (live ? rr / nq : 0);
+        const int lo_q = mk.lo_of(t, s), hi_q = live ? mk.hi_of(t, s) : -1;
+        // no row of the block needs a mask inside [full_lo, full_hi] (uniform)
+        const int full_lo = mk.lo_of(nq - 1, s), full_hi = mk.hi_of(0, s);
+
+        u32x4 qf[KS];
+        {
+            const uint16_t* qrow = (const uint16_t*)a.q + ((s.q_start + t) * a.heads + hq) * D;
 #pragma unroll
-        for (int i = 0; i < C::kDma; ++i) {
-            const int row = min(key0 + i * C::kRowsPerBlock + dma_r, len_k - 1);  // clamp: in bounds
-            const int64_t off = (int64_t)row * kv_stride + dma_off[i];
-            dma16(kbase + off, kst(p) + i * 512);
-            dma16(vbase + off, vst(p) + i * 512);
+            for (int ks = 0; ks < KS; ++ks)
+                qf[ks] = live ? *(const u32x4*)(qrow + ks * 16 + 8 * half) : u32x4{0, 0, 0, 0};
         }
-    };
+        const uint16_t* kbase = (const uint16_t*)a.kc + (s.k_start * a.kv_heads + hk) * D;
+        const uint16_t* vbase = (const uint16_t*)a.vc + (s.k_start * a.kv_heads + hk) * D;
 
-    auto compute = [&](int st, int p) {
-        const int key0 = st * kDecBK;
-        const uint16_t* kt = kst(p);
-        const uint16_t* vt = vst(p);
-        f32x16 sacc = f32x16{0};
+        f32x16 acc[DB];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) sacc = mfma32<BF16>(*(const u32x4*)(kt + k_rd[ks]), qf[ks], sacc);
-        if (!(key0 >= full_lo && key0 + kDecBK - 1 <= full_hi)) {  // uniform: edge steps only
-            const int klo = max(lo_q, k_begin), khi = min(hi_q, k_end - 1);
+        for (int db = 0; db < DB; ++db) acc[db] = f32x16{0};
+        float m_run = kNegInf, l_part = 0.f;
+
+        // registers of the steps in flight
+        u32x4 kr[kDecAhead][C::kLd], vr[kDecAhead][C::kLd];
+        auto load = [&](int st, u32x4 (&kx)[C::kLd], u32x4 (&vx)[C::kLd]) {
+            const int key0 = st * kDecBK;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int key = key0 + 8 * (i / 4) + 4 * half + (i % 4);
-                sacc[i] = (key < klo || key > khi) ? kNegInf : sacc[i];
+            for (int i = 0; i < C::kLd; ++i) {
+                // rows past the end (the look-ahead of the last steps) re-read the last row
+                const int row = min(key0 + i * C::kRowsPerLd + ld_r, len_k - 1);
+                const int64_t o = (int64_t)row * kv_stride + ld_c * 8;
+                kx[i] = *(const u32x4*)(kbase + o);
+                vx[i] = *(const u32x4*)(vbase + o);
+            }
+        };
+        auto stage = [&](const u32x4 (&kx)[C::kLd], const u32x4 (&vx)[C::kLd]) {
+#pragma unroll
+            for (int i = 0; i < C::kLd; ++i) {
+                *(u32x4*)(kt + st_off[i]) = kx[i];
+                *(u32x4*)(vt + st_off[i]) = vx[i];
+            }
+        };
+        auto compute = [&](int st) {
+            const int key0 = st * kDecBK;
+            f32x16 sacc = f32x16{0};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) sacc = mfma32<BF16>(*(const u32x4*)(kt + k_rd[ks]), qf[ks], sacc);
+            if (!(key0 >= full_lo && key0 + kDecBK - 1 <= full_hi)) {  // uniform: edge steps only
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = key0 + 8 * (i / 4) + 4 * half + (i % 4);
+                    sacc[i] = (key < lo_q || key > hi_q) ? kNegInf : sacc[i];
+                }
+            }
+            float mx = kNegInf;
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[i], sacc[i + 1]));
+            mx = max_halves(mx);
+            const bool up = (mx > m_run) & ((m_run == kNegInf) | ((mx - m_run) * c > kDecLazyLog2));
+            if (__builtin_amdgcn_ballot_w64(up)) {
+                const float alpha = !up ? 1.f : (m_run == kNegInf ? 0.f : fast_exp2((m_run - mx) * c));
+                m_run = up ? mx : m_run;
+                l_part *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+            }
+            const float mc = m_run == kNegInf ? 0.f : m_run * c;
+            uint32_t pk[8];
+            float lsum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) {
+                const float p0 = fast_exp2(__builtin_fmaf(sacc[i], c, -mc));
+                const float p1 = fast_exp2(__builtin_fmaf(sacc[i + 1], c, -mc));
+                lsum += p0 + p1;
+                pk[i / 2] = pack2<BF16>(p0, p1);
+            }
+            l_part += lsum;
+#pragma unroll
+            for (int hs = 0; hs < 2; ++hs) {
+                const u32x4 pb = u32x4{pk[4 * hs], pk[4 * hs + 1], pk[4 * hs + 2], pk[4 * hs + 3]};
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    acc[db] = mfma32<BF16>(read_tr<D, DB>(vt, hs, db, v_rd), pb, acc[db]);
+            }
+        };
+
+        const int sa = st_lo + off, se = sa + cnt;
+#pragma unroll
+        for (int j = 0; j < kDecAhead; ++j) load(sa + j, kr[j], vr[j]);
+        // Whole groups of kDecAhead steps (each step's registers fixed, one
+        // exit), then the last < kDecAhead steps, which load nothing more.
+        int st = sa;
+        const int groups = cnt / kDecAhead;
+        for (int it = 0; it < groups; ++it, st += kDecAhead) {
+#pragma unroll
+            for (int j = 0; j < kDecAhead; ++j) {
+                stage(kr[j], vr[j]);
+                load(st + j + kDecAhead, kr[j], vr[j]);
+                compute(st + j);
             }
         }
-        float mx = kNegInf;
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[i], sacc[i + 1]));
-        mx = max_halves(mx);
-        const bool up = (mx > m_run) & ((m_run == kNegInf) | ((mx - m_run) * c > kDecLazyLog2));
-        if (__builtin_amdgcn_ballot_w64(up)) {
-            const float alpha = !up ? 1.f : (m_run == kNegInf ? 0.f : fast_exp2((m_run - mx) * c));
-            m_run = up ? mx : m_run;
-            l_part *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+        for (int j = 0; j < kDecAhead - 1; ++j) {
+            if (st + j < se) {
+                stage(kr[j], vr[j]);
+                compute(st + j);
+            }
         }
-        const float mc = m_run == kNegInf ? 0.f : m_run * c;
-        uint32_t pk[8];
-        float lsum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-            const float p0 = fast_exp2(__builtin_fmaf(sacc[i], c, -mc));
-            const float p1 = fast_exp2(__builtin_fmaf(sacc[i + 1], c, -mc));
-            lsum += p0 + p1;
-            pk[i / 2] = pack2<BF16>(p0, p1);
-        }
-        l_part += lsum;
-#pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
-            const u32x4 pb = u32x4{pk[4 * hs], pk[4 * hs + 1], pk[4 * hs + 2], pk[4 * hs + 3]};
-#pragma unroll
-            for (int db = 0; db < DB; ++db) acc[db] = mfma32<BF16>(read_tr<D, DB>(vt, hs, db, v_rd), pb, acc[db]);
-        }
-    };
 
-    if (vis_lo <= vis_hi) {
-        const int st_lo = vis_lo / kDecBK, st_hi = vis_hi / kDecBK + 1;
-        // Two steps per iteration so the stage index stays a constant.  The
-        // first DMA is issued inside the loop (the compute of the step
-        // before st_lo is skipped); loads past the last step read the
-        // clamped last cache row and are drained before the wave exits.
-        int st = st_lo - 1;  // step held in stage 1
-        for (;;) {
-            issue(st + 1, 0);
-            wait_vmcnt<2 * C::kDma>();
-            if (st >= st_lo) compute(st, 1);
-            if (st + 1 >= st_hi) break;
-            issue(st + 2, 1);
-            wait_vmcnt<2 * C::kDma>();
-            compute(st + 1, 0);
-            st += 2;
-            if (st >= st_hi) break;
+        // partial O (normalised, fp32) and LSE of this piece, live rows only
+        const float l = sum_halves(l_part);
+        if (live) {
+            const int64_t prow = slot * 32 + r32;
+            const float inv = l > 0.f ? 1.f / l : 0.f;
+            float* orow = a.ws_o + prow * D;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    float4 v;
+                    v.x = acc[db][4 * gq] * inv;
+                    v.y = acc[db][4 * gq + 1] * inv;
+                    v.z = acc[db][4 * gq + 2] * inv;
+                    v.w = acc[db][4 * gq + 3] * inv;
+                    *(float4*)(orow + db * 32 + 8 * gq + 4 * half) = v;
+                }
+            if (half == 0) a.ws_lse[prow] = l > 0.f ? m_run * a.scale + logf(l) : kNegInf;
         }
-        wait_vmcnt<0>();
+
+        pos += cnt;
+        if (pos >= pos1) break;
+        // next segment with steps: the next row block, else the next
+        // sequence that has any (one exists: pos < T)
+        off = 0;
+        if (++seg == HR) {
+            seg = 0;
+            do {
+                ++b;
+                dec_steps(a, b, st_lo, n);
+            } while (n == 0);
+        }
     }
-
-    // partial O (normalised, fp32) and LSE of this split
-    const float l = sum_halves(l_part);
-    if (!live) return;
-    const int64_t prow = (((int64_t)sp * a.batch + b) * a.heads + hq) * nq + t;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    float* orow = a.ws_o + prow * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-            float4 w;
-            w.x = acc[db][4 * gq] * inv;
-            w.y = acc[db][4 * gq + 1] * inv;
-            w.z = acc[db][4 * gq + 2] * inv;
-            w.w = acc[db][4 * gq + 3] * inv;
-            *(float4*)(orow + db * 32 + 8 * gq + 4 * half) = w;
-        }
-    if (half == 0) a.ws_lse[prow] = l > 0.f ? m_run * a.scale + logf(l) : kNegInf;
+    // loads issued past a piece's end have landed before the wave ends
+    wait_vmcnt<0>();
 }
 
-// One workgroup of D threads per (batch, query head, token): merge the splits.
+// One workgroup of D threads per (batch, query head, token): merge the pieces
+// of the row's segment.
 template <bool BF16, int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecArgs a) {
     const int64_t row = blockIdx.x;  // ((b * heads) + hq) * nq + t
     const int nq = a.seqlen_q;
-    const int64_t nrows = (int64_t)a.batch * a.heads * nq;
     const int d = threadIdx.x;
-    float mx = kNegInf;
-    for (int sp = 0; sp < a.nsplit; ++sp) mx = fmaxf(mx, a.ws_lse[sp * nrows + row]);
-    float wsum = 0.f, o = 0.f;
-    if (mx != kNegInf) {
-        for (int sp = 0; sp < a.nsplit; ++sp) {
-            const float ls = a.ws_lse[sp * nrows + row];
-            const float w = ls == kNegInf ? 0.f : expf(ls - mx);
-            wsum += w;
-            o += w * a.ws_o[(sp * nrows + row) * D + d];
-        }
-        o /= wsum;
-    }
     const int t = (int)(row % nq);
     const int64_t bh = row / nq;
     const int hq = (int)(bh % a.heads);
-    const int64_t bb = bh / a.heads;
-    uint16_t* out = (uint16_t*)a.o + ((bb * nq + t) * a.heads + hq) * D;
+    const int b = (int)(bh / a.heads);
+    const int g = a.heads / a.kv_heads;
+    const int hk = hq / g;
+    const int r = (hq - hk * g) * nq + t;  // row inside the kv head's packed rows
+    const int rb = r / 32, r32 = r % 32;
+    const int HR = a.row_blocks;
+    const int G = a.waves / a.kv_heads;
+    const int64_t pb = a.prefix[b], T = a.prefix[a.batch] * HR;
+    const int64_t n = a.prefix[b + 1] - pb;  // steps of each segment of sequence b
+    float o = 0.f, lse = kNegInf;
+    if (n > 0) {
+        const int64_t p0 = pb * HR + rb * n, p1 = p0 + n - 1;  // the segment's first and last step
+        const int64_t j0 = dec_group_of(p0, T, G), j1 = dec_group_of(p1, T, G);
+        const int64_t s = (int64_t)b * HR + rb;
+        // one pass, rescaling to the running max; groups between j0 and j1
+        // with an empty range (more groups than steps) wrote nothing
+        float mx = kNegInf, wsum = 0.f;
+        for (int64_t j = j0; j <= j1; ++j) {
+            if (T * j / G == T * (j + 1) / G) continue;
+            const int64_t prow = ((j + s) * a.kv_heads + hk) * 32 + r32;
+            const float ls = a.ws_lse[prow];
+            const float ov = a.ws_o[prow * D + d];
+            if (ls == kNegInf) continue;
+            if (ls > mx) {
+                const float f = mx == kNegInf ? 0.f : expf(mx - ls);
+                wsum *= f;
+                o *= f;
+                mx = ls;
+            }
+            const float wt = expf(ls - mx);
+            wsum += wt;
+            o += wt * ov;
+        }
+        if (mx != kNegInf) {
+            o /= wsum;
+            lse = mx + logf(wsum);
+        }
+    }
+    uint16_t* out = (uint16_t*)a.o + (((int64_t)b * nq + t) * a.heads + hq) * D;
     if constexpr (BF16) {
         const __bf16 hv = (__bf16)o;
         out[d] = __builtin_bit_cast(uint16_t, hv);
@@ -253,14 +391,13 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecArgs a) {
         const _Float16 hv = (_Float16)o;
         out[d] = __builtin_bit_cast(uint16_t, hv);
     }
-    if (d == 0) a.lse[row] = mx == kNegInf ? kNegInf : mx + logf(wsum);
+    if (d == 0) a.lse[row] = lse;
 }
 
 template <bool BF16, int D>
 int launch_decode_t(const DecArgs& a, hipStream_t stream) {
     if (a.batch == 0 || a.seqlen_q == 0) return 0;
-    dim3 grid(a.batch * a.kv_heads, (a.nsplit + kDecWaves - 1) / kDecWaves, a.row_blocks);
-    hipLaunchKernelGGL((decode_split_kernel<BF16, D>), grid, dim3(64 * kDecWaves), 0, stream, a);
+    hipLaunchKernelGGL((decode_split_kernel<BF16, D>), dim3(a.waves), dim3(64), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return 1;
     const int64_t nrows = (int64_t)a.batch * a.heads * a.seqlen_q;
     hipLaunchKernelGGL((decode_combine_kernel<BF16, D>), dim3((unsigned)nrows), dim3(D), 0, stream, a);

@@ -50,15 +50,18 @@ struct DecArgs {
     void* o;             // like q
     float* lse;          // [batch, heads, seqlen_q]
     const int32_t* cache_lens;  // [batch] valid cache rows, or null (all seqlen_k)
-    float* ws_o;         // [nsplit, batch, heads, seqlen_q, D] partial O, normalised
-    float* ws_lse;       // [nsplit, batch, heads, seqlen_q] partial LSE
+    // workspace: one slot of 32 rows per piece and kv head
+    // ((groups + segments) * kv_heads slots)
+    float* ws_o;         // [slots, 32, D] partial O, normalised
+    float* ws_lse;       // [slots, 32] partial LSE
+    int64_t* prefix;     // [batch + 1] prefix sums of the per-sequence step counts
     int batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim;
     int causal, left, right;
     float scale;
     float scale_log2;
     int bf16;
-    int nsplit;          // key splits per (batch, kv head); each sequence's
-                         // valid keys are divided over them in 32-key steps
+    int waves;           // waves of the split pass: groups of kv_heads waves, one per
+                         // kv head, share out the step axis evenly
     int row_blocks;      // ceil(heads / kv_heads * seqlen_q / 32)
 };
 

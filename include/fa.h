@@ -154,11 +154,12 @@ int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const v
 /*
  * Decode over a key/value cache (the KV-cache call named on the overview
  * page, section 3.3, for incremental inference): the same exact attention
- * as fa_fwd for a few new query tokens per sequence against a long cache,
- * computed with the keys split over many workgroups and the partial results
- * merged by their LSE (overview page, section 2.2, online softmax: partial
- * results over disjoint key sets combine exactly through their row max and
- * row sum).
+ * as fa_fwd for a few new query tokens per sequence against a long cache.
+ * The visible keys of all sequences are divided evenly over many waves,
+ * whatever the sequence lengths, and the partial results are merged by
+ * their LSE (overview page, section 2.2, online softmax: partial results
+ * over disjoint key sets combine exactly through their row max and row
+ * sum).
  *   q, o      : [batch, seqlen_q, heads, head_dim], the new tokens
  *   k_cache,
  *   v_cache   : [batch, seqlen_k, kv_heads, head_dim]; seqlen_k is the
@@ -173,14 +174,19 @@ int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const v
  *               device.  Rows past a sequence's length are never used.
  *   workspace : device memory of at least fa_fwd_kvcache_workspace_size()
  *               bytes, 16-byte aligned, owned by the caller; contents on
- *               entry do not matter.  It holds the per-split partial O
- *               (float32) and LSE.
- *   num_splits: key splits per (batch, kv head); 0 picks a count that fills
- *               the device; larger counts are capped at the number of
- *               32-key steps in seqlen_k and at 1024.
+ *               entry do not matter.  It holds the partial O (float32) and
+ *               LSE of every piece of work and the per-sequence prefix sums.
+ *   num_splits: work division.  The query rows of a kv head (its query heads
+ *               times seqlen_q) form blocks of 32; a segment is one
+ *               (sequence, kv head, row block).  num_splits > 0 asks for
+ *               num_splits waves per segment on average (batch * kv_heads *
+ *               row blocks * num_splits waves in all); 0 gives about 512
+ *               waves (two per CU), rounded down to a multiple of kv_heads.
+ *               Capped at one wave per 32-key step of every segment at full
+ *               capacity, and at 65536.
  * All other arguments, the visibility rule, GQA, the empty-row convention
  * and the arithmetic are those of fa_fwd, except that P is rounded to 16
- * bits against each split's own running max and the splits are merged in
+ * bits against each piece's own running max and the pieces are merged in
  * float32, so O is not bit-identical to fa_fwd's (both are within rounding
  * of the exact result).  Two kernels run on `stream`: the split pass and
  * the merge.  Returns FA_OK or an fa_status code; nothing is enqueued on
@@ -195,8 +201,10 @@ int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, void
                    int head_dim, int causal, int window_left, int window_right,
                    float softmax_scale, int dtype, int num_splits, void* stream);
 
-/* The split count fa_fwd_kvcache uses for these sizes (0 for invalid sizes). */
-int fa_fwd_kvcache_splits(int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k, int num_splits);
+/* The number of waves fa_fwd_kvcache's split pass uses for these sizes (0 for
+ * invalid sizes). */
+int fa_fwd_kvcache_splits(int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k, int head_dim,
+                          int num_splits);
 
 /* Static text for a status code ("unknown status" for others). */
 const char* fa_strerror(int status);

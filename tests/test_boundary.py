@@ -182,6 +182,7 @@ BAD_DEC = [
     (dict(scale=float("nan")), INVALID), (dict(left=-7), INVALID),
     (dict(head_dim=80), UNSUPPORTED), (dict(dtype=5), UNSUPPORTED),
     (dict(wsb=16), WORKSPACE),
+    (dict(wsb=(512 + 2 * 2) * 32 * 129 * 4 + 3 * 8 - 1), WORKSPACE),  # one byte short (512 waves)
 ]
 
 
@@ -192,24 +193,26 @@ def test_kvcache_rejects_bad_arguments(L, over, code):
 
 def test_kvcache_split_plan(L):
     splits, size = L.fa_fwd_kvcache_splits, L.fa_fwd_kvcache_workspace_size
-    # auto: about 2048 waves over (batch, kv head, row block) units, at most one split per 32 keys
-    assert splits(8, 32, 8, 1, 32768, 0) == 32
-    assert splits(1, 2, 2, 1, 100, 0) == 4          # 100 keys = 4 steps of 32
-    assert splits(1, 32, 8, 1, 0, 0) == 1           # empty cache
-    assert splits(2, 8, 2, 1, 4096, 5) == 5
-    assert splits(2, 8, 2, 1, 4096, 5000) == 128    # capped at the step count
-    assert splits(1, 8, 2, 1, 1 << 20, 5000) == 1024  # and at 1024
-    assert splits(1, 3, 2, 1, 64, 0) == 0          # invalid sizes
-    # chunks are whole 32-key steps: 100 steps over 7 splits -> 15 steps each -> 7 splits
-    assert splits(1, 8, 2, 1, 3200, 7) == 7
-    assert splits(1, 8, 2, 1, 3200, 8) == 8         # 13 steps each, the last one 9
-    assert splits(1, 8, 2, 1, 3200, 9) == 9
-    assert splits(1, 8, 2, 1, 3200, 11) == 10       # 10 steps each -> only 10 splits needed
-    # workspace = splits x batch x heads x seqlen_q x (head_dim + 1) floats
-    for b, h, hk, nq, nk, d, ns in [(8, 32, 8, 1, 32768, 128, 0), (2, 16, 2, 8, 1000, 64, 3), (1, 4, 1, 16, 33, 128, 0)]:
-        n = splits(b, h, hk, nq, nk, ns)
-        assert size(b, h, hk, nq, nk, d, ns) == n * b * h * nq * (d + 1) * 4
-    assert size(0, 4, 2, 1, 100, 64, 0) == 16
+    # auto: about 512 waves (two per CU), a multiple of kv_heads ...
+    assert splits(8, 32, 8, 1, 32768, 128, 0) == 512
+    assert splits(8, 32, 8, 1, 32768, 64, 0) == 512
+    assert splits(8, 36, 12, 1, 32768, 64, 0) == 504
+    # ... capped at one group (kv_heads waves) per 32-key step of every (sequence, row block)
+    assert splits(1, 2, 2, 1, 100, 128, 0) == 2 * 4   # 2 segments x 4 steps
+    assert splits(1, 32, 8, 1, 0, 128, 0) == 8         # empty cache: one group of kv_heads waves
+    # num_splits > 0: waves per (sequence, kv head, row block); row blocks = ceil(g * seqlen_q / 32)
+    assert splits(2, 8, 2, 1, 4096, 128, 5) == 5 * 2 * 2
+    assert splits(2, 16, 2, 8, 4096, 128, 3) == 3 * 2 * 2 * 2  # 64 rows per kv head: 2 row blocks
+    assert splits(2, 8, 2, 1, 4096, 128, 5000) == 2 * 2 * 128  # one step per wave at most
+    assert splits(64, 8, 8, 1, 1 << 20, 128, 5000) == 65536
+    assert splits(1, 3, 2, 1, 64, 128, 0) == 0 and splits(1, 4, 2, 1, 64, 96, 0) == 0  # invalid
+    # workspace: (groups + sequences x row blocks) x kv_heads slots of 32 rows x (head_dim + 1)
+    # floats, then batch + 1 int64
+    for b, h, hk, nq, nk, d, ns in [(8, 32, 8, 1, 32768, 128, 0), (2, 16, 2, 8, 1000, 64, 3),
+                                    (1, 4, 1, 16, 33, 128, 0), (3, 4, 2, 2, 64, 64, 7)]:
+        w = splits(b, h, hk, nq, nk, d, ns)
+        seg = b * hk * ((h // hk * nq + 31) // 32)
+        assert size(b, h, hk, nq, nk, d, ns) == (w + seg) * 32 * (d + 1) * 4 + (b + 1) * 8
     assert size(1, 4, 2, 1, 100, 96, 0) == 0 and size(1, 4, 3, 1, 100, 64, 0) == 0
 
 
