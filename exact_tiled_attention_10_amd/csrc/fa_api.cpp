@@ -250,6 +250,11 @@ int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, void
     if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
         !aligned(lse, 4) || !aligned(cache_seqlens, 4) || !aligned(workspace, 16))
         return FA_ERR_INVALID_ARG;
+    // the kernels count steps of the split axis and output rows in 32 bits
+    const long long rblocks = ((long long)(heads / kv_heads) * seqlen_q + 31) / 32;
+    if ((long long)batch * rblocks * ((seqlen_k + 31) / 32) >= (1LL << 31) ||
+        (long long)batch * heads * seqlen_q >= (1LL << 31))
+        return FA_ERR_INVALID_ARG;
     if (has_q && workspace_bytes < fa_fwd_kvcache_workspace_size(batch, heads, kv_heads, seqlen_q, seqlen_k,
                                                                  head_dim, num_splits))
         return FA_ERR_WORKSPACE;

@@ -81,11 +81,20 @@ __device__ __forceinline__ void dec_steps(const DecArgs& a, int b, int& st_lo, i
     n = lo <= hi ? hi / kDecBK + 1 - st_lo : 0;
 }
 
-// Group holding position pos of the step axis: group j of G covers
-// [floor(j T / G), floor((j + 1) T / G)).
-__device__ __forceinline__ int64_t dec_group_of(int64_t pos, int64_t T, int G) {
-    return ((pos + 1) * G - 1) / T;
-}
+// Even division of the T steps of the step axis over G groups: the first R
+// groups take Q + 1 steps, the others Q (Q = T / G, R = T % G).  T < 2^31 is
+// guaranteed by the host.
+struct DecPart {
+    int T, G, Q, R;
+    __device__ __forceinline__ DecPart(int T_, int G_) : T(T_), G(G_), Q(T_ / G_), R(T_ % G_) {}
+    __device__ __forceinline__ int start(int j) const { return j * Q + min(j, R); }
+    __device__ __forceinline__ bool empty(int j) const { return Q == 0 && j >= R; }
+    // group holding position pos (0 <= pos < T)
+    __device__ __forceinline__ int group_of(int pos) const {
+        const int big = R * (Q + 1);
+        return pos < big ? pos / (Q + 1) : R + (pos - big) / Q;
+    }
+};
 
 // Inclusive prefix sum over the wave's lanes.
 __device__ __forceinline__ int64_t wave_scan(int64_t x, int lane) {
@@ -127,10 +136,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecArgs a) {
     }
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) total += __shfl_xor(total, d, 64);
-    const int64_t T = total * HR;
-    const int64_t pos0 = T * grp / G, pos1 = T * (grp + 1) / G;
+    const DecPart part((int)(total * HR), G);
+    const int pos0 = part.start(grp), pos1 = part.start(grp + 1);
     int b = -1;
-    int64_t seq_base = 0;  // step-axis position of sequence b's first segment
+    int seq_base = 0;  // step-axis position of sequence b's first segment
     {
         int64_t carry = 0;
         for (int c0 = 0; c0 < a.batch; c0 += 64) {
@@ -144,7 +153,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecArgs a) {
             if (b < 0 && m) {
                 const int src = __builtin_ctzll(m);
                 b = c0 + src;
-                seq_base = __shfl(excl, src, 64) * HR;
+                seq_base = (int)(__shfl(excl, src, 64) * HR);
             }
             carry = __shfl(incl, 63, 64);
         }
@@ -177,11 +186,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecArgs a) {
     // ---- pieces -------------------------------------------------------------------
     int st_lo, n;
     dec_steps(a, b, st_lo, n);
-    int64_t pos = pos0;
-    int seg = (int)((pos - seq_base) / n);  // segment (row block) inside sequence b
-    int off = (int)((pos - seq_base) % n);  // first step inside it
+    int pos = pos0;
+    int seg = (pos - seq_base) / n;  // segment (row block) inside sequence b
+    int off = (pos - seq_base) % n;  // first step inside it
     while (true) {
-        const int cnt = (int)min((int64_t)(n - off), pos1 - pos);
+        const int cnt = min(n - off, pos1 - pos);
         const int rb = seg;
         const int64_t slot = ((int64_t)grp + (int64_t)b * HR + seg) * a.kv_heads + hk;
 
@@ -336,51 +345,67 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecArgs a) {
 }
 
 // One workgroup of D threads per (batch, query head, token): merge the pieces
-// of the row's segment.
+// of the row's segment.  Thread d merges column d; the pieces are taken in
+// batches of kMergeBatch whose loads (LSE, broadcast, and O) are all issued
+// before any is used, so a typical row costs one round trip to memory after
+// the prefix sums.
+constexpr int kMergeBatch = 16;
+
 template <bool BF16, int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecArgs a) {
-    const int64_t row = blockIdx.x;  // ((b * heads) + hq) * nq + t
+    const int row = blockIdx.x;  // ((b * heads) + hq) * nq + t, below 2^31 (host check)
     const int nq = a.seqlen_q;
     const int d = threadIdx.x;
-    const int t = (int)(row % nq);
-    const int64_t bh = row / nq;
-    const int hq = (int)(bh % a.heads);
-    const int b = (int)(bh / a.heads);
+    const int t = row % nq;
+    const int bh = row / nq;
+    const int hq = bh % a.heads;
+    const int b = bh / a.heads;
     const int g = a.heads / a.kv_heads;
     const int hk = hq / g;
     const int r = (hq - hk * g) * nq + t;  // row inside the kv head's packed rows
     const int rb = r / 32, r32 = r % 32;
     const int HR = a.row_blocks;
     const int G = a.waves / a.kv_heads;
-    const int64_t pb = a.prefix[b], T = a.prefix[a.batch] * HR;
-    const int64_t n = a.prefix[b + 1] - pb;  // steps of each segment of sequence b
+    const int pb = (int)a.prefix[b];
+    const DecPart part((int)a.prefix[a.batch] * HR, G);
+    const int n = (int)a.prefix[b + 1] - pb;  // steps of each segment of sequence b
     float o = 0.f, lse = kNegInf;
     if (n > 0) {
-        const int64_t p0 = pb * HR + rb * n, p1 = p0 + n - 1;  // the segment's first and last step
-        const int64_t j0 = dec_group_of(p0, T, G), j1 = dec_group_of(p1, T, G);
+        const int p0 = pb * HR + rb * n, p1 = p0 + n - 1;  // the segment's first and last step
+        const int j0 = part.group_of(p0), j1 = part.group_of(p1);
         const int64_t s = (int64_t)b * HR + rb;
-        // one pass, rescaling to the running max; groups between j0 and j1
-        // with an empty range (more groups than steps) wrote nothing
         float mx = kNegInf, wsum = 0.f;
-        for (int64_t j = j0; j <= j1; ++j) {
-            if (T * j / G == T * (j + 1) / G) continue;
-            const int64_t prow = ((j + s) * a.kv_heads + hk) * 32 + r32;
-            const float ls = a.ws_lse[prow];
-            const float ov = a.ws_o[prow * D + d];
-            if (ls == kNegInf) continue;
-            if (ls > mx) {
-                const float f = mx == kNegInf ? 0.f : expf(mx - ls);
-                wsum *= f;
-                o *= f;
-                mx = ls;
+        for (int jb = j0; jb <= j1; jb += kMergeBatch) {
+            float ls[kMergeBatch], ov[kMergeBatch];
+#pragma unroll
+            for (int i = 0; i < kMergeBatch; ++i) {
+                const int j = jb + i;
+                // past the segment's last group, or a group with an empty range
+                // (more groups than steps): no piece, never read
+                const bool has = j <= j1 && !part.empty(j);
+                const int64_t prow = ((j + s) * a.kv_heads + hk) * 32 + r32;
+                ls[i] = has ? a.ws_lse[prow] : kNegInf;
+                ov[i] = has ? a.ws_o[prow * D + d] : 0.f;
             }
-            const float wt = expf(ls - mx);
-            wsum += wt;
-            o += wt * ov;
+            float m2 = mx;
+#pragma unroll
+            for (int i = 0; i < kMergeBatch; ++i) m2 = fmaxf(m2, ls[i]);
+            if (m2 == kNegInf) continue;
+            const float f = mx == kNegInf ? 0.f : __expf(mx - m2);  // rescale what came before
+            wsum *= f;
+            o *= f;
+#pragma unroll
+            for (int i = 0; i < kMergeBatch; ++i) {
+                if (ls[i] == kNegInf) continue;
+                const float wt = __expf(ls[i] - m2);
+                wsum += wt;
+                o = __builtin_fmaf(wt, ov[i], o);
+            }
+            mx = m2;
         }
         if (mx != kNegInf) {
             o /= wsum;
-            lse = mx + logf(wsum);
+            lse = mx + __logf(wsum);
         }
     }
     uint16_t* out = (uint16_t*)a.o + (((int64_t)b * nq + t) * a.heads + hq) * D;

@@ -184,6 +184,9 @@ int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const v
  *               waves (two per CU), rounded down to a multiple of kv_heads.
  *               Capped at one wave per 32-key step of every segment at full
  *               capacity, and at 65536.
+ * Sizes: batch * heads * seqlen_q and batch * ceil(heads / kv_heads *
+ * seqlen_q / 32) * ceil(seqlen_k / 32) must stay below 2^31
+ * (FA_ERR_INVALID_ARG otherwise).
  * All other arguments, the visibility rule, GQA, the empty-row convention
  * and the arithmetic are those of fa_fwd, except that P is rounded to 16
  * bits against each piece's own running max and the pieces are merged in

@@ -181,6 +181,8 @@ BAD_DEC = [
     (dict(heads=6, kv_heads=4), INVALID), (dict(seqlen_q=-1), INVALID), (dict(causal=3), INVALID),
     (dict(scale=float("nan")), INVALID), (dict(left=-7), INVALID),
     (dict(head_dim=80), UNSUPPORTED), (dict(dtype=5), UNSUPPORTED),
+    (dict(batch=1 << 16, seqlen_k=1 << 20), INVALID),      # 2^16 x 2^15 steps: beyond 32 bits
+    (dict(batch=1 << 20, heads=2048, kv_heads=2048), INVALID),  # 2^31 output rows
     (dict(wsb=16), WORKSPACE),
     (dict(wsb=(512 + 2 * 2) * 32 * 129 * 4 + 3 * 8 - 1), WORKSPACE),  # one byte short (512 waves)
 ]
