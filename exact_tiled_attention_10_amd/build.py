@@ -1,5 +1,7 @@
 """Build libfa.so (the C-ABI attention library) in-tree with hipcc, for
-gfx950 only.  Usage: python -m exact_tiled_attention_10_amd.build"""
+gfx950 only, and libfacalib.so (the streaming-read kernel that calibrates
+the HBM byte counters for profiling).  Usage:
+python -m exact_tiled_attention_10_amd.build"""
 from __future__ import annotations
 
 import concurrent.futures as cf
@@ -10,6 +12,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libfa.so")
+CALIB_OUT = os.path.join(HERE, "libfacalib.so")
+CALIB_SOURCE = "fa_calib.hip"
 BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip"]
@@ -46,18 +50,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp"
+def _link(objs: list, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
+        objs = list(ex.map(_compile, SOURCES + [CALIB_SOURCE]))
+    _link(objs[:-1], OUT)
+    _link(objs[-1:], CALIB_OUT)
     if verbose:
-        print(f"built {OUT}")
+        print(f"built {OUT} and {CALIB_OUT}")
     return OUT
 
 

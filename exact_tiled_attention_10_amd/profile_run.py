@@ -8,16 +8,17 @@ Subcommands (run from anywhere; the repository root is found from this file):
           `decode` runs the KV-cache decode call, split pass and merge, on a
           named decode workload).  Meant to sit under `rocprofv3 --pmc ...`.
   copy    [--mib M] [--iters N]
-          Run a plain device copy of M MiB (read M MiB, write M MiB) N times:
-          the calibration for the HBM byte counters.
+          Run the calibration copy (libfacalib.so: read M MiB, write M MiB with
+          16-byte-per-lane loads and stores of whole lines, as the attention
+          kernels do) N times: the reference for the HBM byte counters.
   traffic --workload W --kernel K --fetch DIR --write DIR --copy-fetch DIR
           --copy-write DIR [--mib M]
           Read the counter CSVs of four `rocprofv3 --pmc` runs (FETCH_SIZE and
-          WRITE_SIZE, for the kernel and for the copy), scale the kernel's
-          counts by the copy's measured/known ratio, and record the bytes per
-          launch in profiles/traffic.json together with the hash of the
-          kernel's sources (bench.py reports the figure only while the hash
-          still matches).
+          WRITE_SIZE, for the kernel and for the calibration copy), scale the
+          kernel's counts by the copy's known/counted ratio, and record the
+          bytes per launch in profiles/traffic.json together with the hash of
+          the kernel's sources (bench.py reports the figure only while the
+          hash still matches).
   trace   --db FILE --title T --command C
           Print a markdown table of a rocprofv3 kernel-trace database.
 """
@@ -49,7 +50,8 @@ KERNEL_SOURCES = {
 # Kernel-name substrings in rocprofv3 output.
 KERNEL_NAMES = {"fwd": "fwd_kernel", "rowdot": "bwd_rowdot_kernel", "dkdv": "bwd_dkdv_kernel",
                 "dq": "bwd_dq_kernel", "decode": "decode_split_kernel"}
-COPY_NAME = "elementwise"
+COPY_NAME = "calib_copy_kernel"
+CALIB_LIB = os.path.join(HERE, "libfacalib.so")
 
 
 def source_hash(kernel: str) -> str:
@@ -112,12 +114,21 @@ def _run(args):
 
 
 def _copy(args):
+    import ctypes
     import torch
-    n = args.mib * (1 << 20) // 4
-    x = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    if not os.path.exists(CALIB_LIB):
+        raise RuntimeError(f"{CALIB_LIB} is not built; run `python -m exact_tiled_attention_10_amd.build`")
+    L = ctypes.CDLL(CALIB_LIB)
+    L.fa_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    L.fa_calib_copy.restype = ctypes.c_int
+    nbytes = args.mib * (1 << 20)
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
     y = torch.empty_like(x)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     for _ in range(args.iters):
-        torch.mul(x, 1.0, out=y)  # an elementwise kernel: reads x once, writes y once
+        rc = L.fa_calib_copy(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()), nbytes, 1024, stream)
+        if rc != 0:
+            raise RuntimeError(f"fa_calib_copy returned {rc}")
     torch.cuda.synchronize()
     print(f"copied {args.mib} MiB x{args.iters}", flush=True)
 
@@ -202,9 +213,12 @@ def _trace(args):
             line = next((l for l in fh if l.startswith('{"metric"')), None)
         if line:
             d = json.loads(line)
+            summary = {"ms_per_step": d["ms_per_step"], "value": d["value"],
+                       "kernels_ms": {k: v["ms"] for k, v in d["kernels"].items()}}
+            if d.get("decode"):
+                summary["decode"] = {k: d["decode"][k] for k in ("workload", "ms_per_call", "achieved", "unit")}
             out += ["", "bench.py line of the same run (HIP-event kernel times, ms):", "", "```",
-                    json.dumps({"ms_per_step": d["ms_per_step"], "value": d["value"],
-                                "kernels_ms": {k: v["ms"] for k, v in d["kernels"].items()}}), "```"]
+                    json.dumps(summary), "```"]
     print("\n".join(out))
 
 
