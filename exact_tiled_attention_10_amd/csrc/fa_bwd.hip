@@ -282,7 +282,7 @@ void bwd_dq_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dK, dV: one workgroup per (batch, kv head, 128-key tile); 4 waves x 32 keys,
 // one wave per SIMD (the dK/dV accumulators live beside resident K^T / V^T
-// operand fragments).  Per streamed 64-row query tile and wave:
+// operand fragments).  Per streamed 128-row query tile (four 32-row blocks) and wave:
 //   S = Q K^T, dP = dO V^T      (A from the Q / dO tiles, B resident)
 //   P = exp2(c S - lse2), dS = P o (dP - D)      (one key per lane column)
 //   dV^T += dO^T P, dK^T += Q^T dS   (A from transposing reads of the tiles)
