@@ -71,7 +71,7 @@ def decode_bytes(p) -> float:
     return kv + qo + 4.0 * p.batch * p.heads * p.seqlen_q
 
 
-def bench_decode(fa, synth, torch, steps: int, warmup: int):
+def bench_decode(fa, synth, torch, steps: int, warmup: int, measured_traffic):
     dev = torch.device("cuda:0")
     p = synth.decode_workload(DECODE_WORKLOAD)
     q, kc, vc = p.q.to(dev), p.k_cache.to(dev), p.v_cache.to(dev)
@@ -92,6 +92,7 @@ def bench_decode(fa, synth, torch, steps: int, warmup: int):
             "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(gbs / PEAK_HBM_GBS, 4), "splits": plan.nsplit,
             "bytes_per_call": int(decode_bytes(p)),
+            "traffic": measured_traffic("decode", DECODE_WORKLOAD),
             "tokens_per_s": round(p.batch * p.seqlen_q / (ms / 1e3), 1)}
 
 
@@ -233,7 +234,7 @@ def main():
         "decode": None,
     }
     if not args.no_decode:
-        out["decode"] = bench_decode(fa, synth, torch, max(K, 20), max(args.warmup, 3))
+        out["decode"] = bench_decode(fa, synth, torch, max(K, 20), max(args.warmup, 3), measured_traffic)
     if not args.no_cpu_baseline:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         out["cpu_baseline"] = cpu_baseline(p, threads)

@@ -30,6 +30,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sqlite3
 import sys
 from collections import defaultdict
@@ -54,11 +55,19 @@ COPY_NAME = "calib_copy_kernel"
 CALIB_LIB = os.path.join(HERE, "libfacalib.so")
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and with whitespace collapsed: what the
+    compiler sees, so edits to comments keep a counter record valid."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash(kernel: str) -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
