@@ -40,12 +40,21 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         I = ctypes.c_int
+        D, U64 = ctypes.c_double, ctypes.c_uint64
         lib.oracle_attention_fwd.argtypes = [P] * 7 + [I] * 9 + \
-            [ctypes.c_double, P, I, P, I, I]
+            [D, P, I, P, I, I, D, U64]
         lib.oracle_attention_fwd.restype = I
         lib.oracle_attention_bwd.argtypes = [P] * 11 + [I] * 9 + \
-            [ctypes.c_double, P, I, P, I, P, I, I]
+            [D, P, I, P, I, P, I, I, D, U64]
         lib.oracle_attention_bwd.restype = I
+        lib.oracle_philox4x32_10.argtypes = [P, P, P]
+        lib.oracle_philox4x32_10.restype = None
+        lib.oracle_philox4x64_10.argtypes = [P, P, P]
+        lib.oracle_philox4x64_10.restype = None
+        lib.oracle_dropout_threshold.argtypes = [D]
+        lib.oracle_dropout_threshold.restype = I
+        lib.oracle_dropout_mask.argtypes = [I, I, I, I, D, U64, P]
+        lib.oracle_dropout_mask.restype = None
         _lib = lib
     return _lib
 
@@ -83,12 +92,14 @@ def _geometry(q, k, heads_hint, cu):
 
 
 def attention_fwd(q, k, v, *, scale, causal=False, window=(-1, -1),
-                  cu_seqlens=None, rows=None, heads=None, threads=0):
+                  cu_seqlens=None, rows=None, heads=None, threads=0,
+                  dropout_p=0.0, seed=0):
     """O and LSE of exact attention.  q: (B, Nq, H, d) or packed (T, H, d);
     k, v: (B, Nk, Hkv, d) or (T, Hkv, d).  ``cu_seqlens`` (B+1 prefix sums)
     marks a packed batch, used for both queries and keys.  ``rows`` /
     ``heads`` restrict the computed query rows (positions within each
-    sequence) / query heads; the rest stays NaN."""
+    sequence) / query heads; the rest stays NaN.  ``dropout_p`` / ``seed``:
+    dropout with the Philox4x32-10 keep decisions (see the C++ header)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     cu = _i32(cu_seqlens)
     B, H, HK, NQ, NK, D = _geometry(q, k, None, cu)
@@ -99,7 +110,8 @@ def attention_fwd(q, k, v, *, scale, causal=False, window=(-1, -1),
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu), _ptr(cu),
         B, H, HK, NQ, NK, D, int(bool(causal)), int(window[0]), int(window[1]),
         float(scale), _ptr(rs), 0 if rs is None else len(rs),
-        _ptr(hs), 0 if hs is None else len(hs), int(threads))
+        _ptr(hs), 0 if hs is None else len(hs), int(threads),
+        float(dropout_p), int(seed) & (2**64 - 1))
     if rc:
         raise ValueError("oracle_attention_fwd: bad arguments")
     return o, lse
@@ -107,7 +119,7 @@ def attention_fwd(q, k, v, *, scale, causal=False, window=(-1, -1),
 
 def attention_bwd(q, k, v, dout, *, scale, causal=False, window=(-1, -1),
                   cu_seqlens=None, q_rows=None, k_rows=None, kv_heads=None,
-                  threads=0):
+                  threads=0, dropout_p=0.0, seed=0):
     """dQ, dK, dV (and the oracle's own O, LSE on the rows it needed) of exact
     attention for upstream gradient ``dout``.  ``q_rows`` restricts dQ rows,
     ``k_rows`` the dK/dV rows, ``kv_heads`` the kv heads (with all query
@@ -127,7 +139,39 @@ def attention_bwd(q, k, v, dout, *, scale, causal=False, window=(-1, -1),
         B, H, HK, NQ, NK, D, int(bool(causal)), int(window[0]), int(window[1]),
         float(scale), _ptr(qr), 0 if qr is None else len(qr),
         _ptr(kr), 0 if kr is None else len(kr),
-        _ptr(kh), 0 if kh is None else len(kh), int(threads))
+        _ptr(kh), 0 if kh is None else len(kh), int(threads),
+        float(dropout_p), int(seed) & (2**64 - 1))
     if rc:
         raise ValueError("oracle_attention_bwd: bad arguments")
     return dq, dk, dv, o, lse
+
+
+def philox4x32_10(counter, key):
+    """Philox4x32-10 output block for a 4-word counter and 2-word key."""
+    c = np.ascontiguousarray(counter, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.zeros(4, dtype=np.uint32)
+    _load().oracle_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def philox4x64_10(counter, key):
+    """Philox4x64-10 output block (checks the shared round structure)."""
+    c = np.ascontiguousarray(counter, dtype=np.uint64)
+    k = np.ascontiguousarray(key, dtype=np.uint64)
+    out = np.zeros(4, dtype=np.uint64)
+    _load().oracle_philox4x64_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def dropout_threshold(p: float) -> int:
+    """Keep threshold T: an element is kept iff its 8-bit draw is below T."""
+    return int(_load().oracle_dropout_threshold(float(p)))
+
+
+def dropout_mask(batch, heads, lq, lk, p, seed):
+    """Keep decisions (uint8, 1 = kept) of elements (b, h, i, j)."""
+    out = np.zeros((batch, heads, lq, lk), dtype=np.uint8)
+    _load().oracle_dropout_mask(int(batch), int(heads), int(lq), int(lk), float(p),
+                                int(seed) & (2**64 - 1), _ptr(out))
+    return out

@@ -25,6 +25,22 @@
 //   dQ_i  = scale * sum_j dS_ij k_j
 //   dK_j += scale * dS_ij q_i
 //
+// Dropout (the dropout_p argument of the attention call, overview page section
+// 3.3; every call on the pages passes 0): each probability P_ij is kept with
+// probability T/256 and scaled by 256/T, or dropped (set to 0), after the
+// softmax and before the weighted sum; LSE stays that of the softmax.  The
+// keep decision of element (sequence b, query head h, query row i, key j) is
+// an 8-bit draw from the counter-based generator Philox4x32-10 (Salmon, Moraes,
+// Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011):
+//   counter = (j / 4, i / 4, h, b), key = (seed low 32 bits, seed high 32 bits),
+//   u = byte (j mod 4) of output word (i mod 4), kept iff u < T,
+//   T = floor((1 - dropout_p) * 256 + 1/2).
+// With M_ij = kept / dropped (1 / 0) and s = 256 / T (0 when T = 0):
+//   O_i = sum_j P_ij M_ij s v_j
+//   dV_j += P_ij M_ij s dO_i,  dP_ij = dO_i . v_j,
+//   dS_ij = P_ij (M_ij s dP_ij - D_i),  D_i = sum_k P_ik M_ik s dP_ik = dO_i . O_i
+// (the gradient of O = (P o M s) V with P the softmax of the score row).
+//
 // Readings where the pages are silent (each also listed in the design notes):
 //   * visible set of query row i in a sequence with Lq queries and Lk keys:
 //     with p = i + (Lk - Lq) (bottom-right alignment), key j is visible iff
@@ -55,12 +71,67 @@
 
 namespace {
 
+// Philox4x32-10 as published: ten rounds of
+//   (c0, c1, c2, c3) -> (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0))
+// with the key bumped by the Weyl constants between rounds.
+void philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], uint32_t out[4]) {
+    const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u, W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+    uint32_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
+    uint32_t k0 = key_in[0], k1 = key_in[1];
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) { k0 += W0; k1 += W1; }
+        const uint64_t p0 = (uint64_t)M0 * c0, p1 = (uint64_t)M1 * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n1 = (uint32_t)p1;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1, n3 = (uint32_t)p0;
+        c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+// The same construction on 64-bit words (Philox4x64-10), used only to check the
+// round structure against an independent library implementation.
+void philox4x64_10(const uint64_t ctr_in[4], const uint64_t key_in[2], uint64_t out[4]) {
+    const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+    const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+    uint64_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
+    uint64_t k0 = key_in[0], k1 = key_in[1];
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) { k0 += W0; k1 += W1; }
+        const unsigned __int128 p0 = (unsigned __int128)M0 * c0, p1 = (unsigned __int128)M1 * c2;
+        const uint64_t n0 = (uint64_t)(p1 >> 64) ^ c1 ^ k0, n1 = (uint64_t)p1;
+        const uint64_t n2 = (uint64_t)(p0 >> 64) ^ c3 ^ k1, n3 = (uint64_t)p0;
+        c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+// Keep threshold T for a dropout probability p.
+int dropout_threshold(double p) {
+    double t = std::floor((1.0 - p) * 256.0 + 0.5);
+    if (t < 0.0) t = 0.0;
+    if (t > 256.0) t = 256.0;
+    return (int)t;
+}
+
 struct Geometry {
     int batch, heads, kv_heads, seqlen_q, seqlen_k, d;
     int causal, left, right;
     double scale;
     const int32_t* cu_q;  // host pointers or null
     const int32_t* cu_k;
+    int drop_t = 256;        // keep threshold (256: no dropout)
+    uint64_t seed = 0;
+    double drop_scale() const { return drop_t > 0 ? 256.0 / drop_t : 0.0; }
+    // M_ij times the kept-value scale: s when kept, 0 when dropped
+    double keep(int b, int h, int i, int j) const {
+        if (drop_t >= 256) return 1.0;
+        const uint32_t ctr[4] = {(uint32_t)j >> 2, (uint32_t)i >> 2, (uint32_t)h, (uint32_t)b};
+        const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+        uint32_t w[4];
+        philox4x32_10(ctr, key, w);
+        const uint32_t u = (w[i & 3] >> (8 * (j & 3))) & 0xffu;
+        return (int)u < drop_t ? drop_scale() : 0.0;
+    }
     bool packed() const { return cu_q != nullptr; }
     int64_t q_start(int b) const { return packed() ? cu_q[b] : (int64_t)b * seqlen_q; }
     int64_t k_start(int b) const { return packed() ? cu_k[b] : (int64_t)b * seqlen_k; }
@@ -124,6 +195,8 @@ RowResult attend_row(const Geometry& g, const double* q, const double* k, const 
     const int d = g.d, lk = g.len_k(b), hk = h / g.group();
     const double* qi = q + g.qoff(b, i, h);
     s.assign(lk, 0.0);
+    thread_local std::vector<double> km;  // M_ij s of the row (dropout)
+    km.assign(lk, 1.0);
     std::vector<char> vis(lk, 0);
     // materialise the score row
     double m = -std::numeric_limits<double>::infinity();
@@ -132,6 +205,7 @@ RowResult attend_row(const Geometry& g, const double* q, const double* k, const 
         if (!g.visible(b, i, j)) continue;
         vis[j] = 1;
         ++nvis;
+        km[j] = g.keep(b, h, i, j);
         s[j] = g.scale * dot(qi, k + g.koff(b, j, hk), d);
         if (s[j] > m) m = s[j];
     }
@@ -148,7 +222,7 @@ RowResult attend_row(const Geometry& g, const double* q, const double* k, const 
         for (int j = 0; j < lk; ++j) {
             if (!vis[j]) continue;
             const double* vj = v + g.koff(b, j, hk);
-            for (int c = 0; c < d; ++c) o_row[c] += s[j] * vj[c];
+            for (int c = 0; c < d; ++c) o_row[c] += s[j] * km[j] * vj[c];
         }
     }
     if (dout) {
@@ -158,13 +232,13 @@ RowResult attend_row(const Geometry& g, const double* q, const double* k, const 
         for (int j = 0; j < lk; ++j) {
             if (!vis[j]) continue;
             dp[j] = dot(doi, v + g.koff(b, j, hk), d);
-            dsum += s[j] * dp[j];
+            dsum += s[j] * km[j] * dp[j];
         }
         r.dsum = dsum;
         if (dq_row) {
             for (int j = 0; j < lk; ++j) {
                 if (!vis[j]) continue;
-                const double ds = s[j] * (dp[j] - dsum);
+                const double ds = s[j] * (km[j] * dp[j] - dsum);
                 const double* kj = k + g.koff(b, j, hk);
                 for (int c = 0; c < d; ++c) dq_row[c] += g.scale * ds * kj[c];
             }
@@ -204,10 +278,14 @@ int oracle_attention_fwd(const double* q, const double* k, const double* v,
                          int head_dim, int causal, int window_left, int window_right,
                          double softmax_scale,
                          const int32_t* row_sel, int n_row_sel,
-                         const int32_t* head_sel, int n_head_sel, int n_threads) {
-    const Geometry g{batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim,
-                     causal, window_left, window_right, softmax_scale,
-                     cu_seqlens_q, cu_seqlens_k};
+                         const int32_t* head_sel, int n_head_sel, int n_threads,
+                         double dropout_p, uint64_t seed) {
+    Geometry g{batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim,
+               causal, window_left, window_right, softmax_scale,
+               cu_seqlens_q, cu_seqlens_k};
+    if (!(dropout_p >= 0.0 && dropout_p < 1.0)) return 1;
+    g.drop_t = dropout_threshold(dropout_p);
+    g.seed = seed;
     if (check_args(g)) return 1;
     int maxq = 0;
     for (int b = 0; b < batch; ++b) maxq = std::max(maxq, g.len_q(b));
@@ -242,10 +320,14 @@ int oracle_attention_bwd(const double* q, const double* k, const double* v,
                          double softmax_scale,
                          const int32_t* q_row_sel, int n_q_row_sel,
                          const int32_t* k_row_sel, int n_k_row_sel,
-                         const int32_t* kv_head_sel, int n_kv_head_sel, int n_threads) {
-    const Geometry g{batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim,
-                     causal, window_left, window_right, softmax_scale,
-                     cu_seqlens_q, cu_seqlens_k};
+                         const int32_t* kv_head_sel, int n_kv_head_sel, int n_threads,
+                         double dropout_p, uint64_t seed) {
+    Geometry g{batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim,
+               causal, window_left, window_right, softmax_scale,
+               cu_seqlens_q, cu_seqlens_k};
+    if (!(dropout_p >= 0.0 && dropout_p < 1.0)) return 1;
+    g.drop_t = dropout_threshold(dropout_p);
+    g.seed = seed;
     if (check_args(g)) return 1;
     const int d = head_dim, grp = g.group();
     int maxq = 0, maxk = 0;
@@ -312,15 +394,38 @@ int oracle_attention_bwd(const double* q, const double* k, const double* v,
                 const double* doi = dout + g.qoff(b, i, h);
                 const double p = std::exp(g.scale * dot(qi, kj, d) - row_lse[ri]);
                 const double dpij = dot(doi, vj, d);
-                const double ds = p * (dpij - row_dsum[ri]);
+                const double km = g.keep(b, h, i, j);
+                const double ds = p * (km * dpij - row_dsum[ri]);
                 for (int c = 0; c < d; ++c) {
-                    dvj[c] += p * doi[c];
+                    dvj[c] += p * km * doi[c];
                     dkj[c] += g.scale * ds * qi[c];
                 }
             }
         }
     });
     return 0;
+}
+
+// The generators and the dropout decision, exposed for their pins.
+void oracle_philox4x32_10(const uint32_t* ctr, const uint32_t* key, uint32_t* out) {
+    philox4x32_10(ctr, key, out);
+}
+void oracle_philox4x64_10(const uint64_t* ctr, const uint64_t* key, uint64_t* out) {
+    philox4x64_10(ctr, key, out);
+}
+int oracle_dropout_threshold(double p) { return dropout_threshold(p); }
+
+// keep[((b * heads + h) * lq + i) * lk + j] = 1 if element (b, h, i, j) is kept.
+void oracle_dropout_mask(int batch, int heads, int lq, int lk, double dropout_p, uint64_t seed,
+                         uint8_t* keep) {
+    Geometry g{batch, heads, heads, lq, lk, 1, 0, -1, -1, 1.0, nullptr, nullptr};
+    g.drop_t = dropout_threshold(dropout_p);
+    g.seed = seed;
+    for (int b = 0; b < batch; ++b)
+        for (int h = 0; h < heads; ++h)
+            for (int i = 0; i < lq; ++i)
+                for (int j = 0; j < lk; ++j)
+                    keep[(((int64_t)b * heads + h) * lq + i) * lk + j] = g.keep(b, h, i, j) != 0.0;
 }
 
 }  // extern "C"
