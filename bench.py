@@ -15,6 +15,10 @@ pair.  The roofline object describes the kernel with the largest share of
 the step.  The CPU baseline is the fp64 oracle timed on a bounded sample of
 the same workload (one head, all rows, forward + backward).
 
+An object "dropout" times the same step with dropout_p = 0.1 (Philox keep
+decisions drawn inside the forward, dK/dV and dQ kernels), against the same
+algorithmic FLOP count.
+
 A second object, "decode", times the KV-cache decode path on its own
 workload (one new token per sequence, GQA 32/8 heads, ragged caches of
 16K-32K tokens, d 128, bf16): bytes of the valid K/V cache rows read (plus
@@ -117,6 +121,30 @@ def cpu_baseline(p, threads: int):
                       f"forward + backward in fp64 ({flops / 1e9:.1f} GFLOP)"}
 
 
+def bench_dropout(fa, p, q, k, v, do, steps: int, warmup: int, flops: float, torch):
+    plan = fa.Plan(q, k, v, do, causal=p.causal, window_size=(p.window_left, p.window_right),
+                   softmax_scale=p.scale, dropout_p=0.1, dropout_seed=20240601)
+    calls = [plan.fwd, lambda: plan.bwd_stage(0), lambda: plan.bwd_stage(1), lambda: plan.bwd_stage(2)]
+    for _ in range(warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for s in range(steps):
+        ev[s][0].record(plan.stream)
+        calls[0]()
+        ev[s][1].record(plan.stream)
+        for c in calls[1:]:
+            c()
+        ev[s][2].record(plan.stream)
+    torch.cuda.synchronize()
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    step_ms = fwd_ms + bwd_ms
+    return {"dropout_p": 0.1, "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+            "step_ms": round(step_ms, 4), "tflops": round(flops / (step_ms / 1e3) / 1e12, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -124,6 +152,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the KV-cache decode measurement")
+    ap.add_argument("--no-dropout", action="store_true", help="skip the dropout step measurement")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (default min(16, cores))")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -231,8 +260,11 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": None,
+        "dropout": None,
         "decode": None,
     }
+    if not args.no_dropout:
+        out["dropout"] = bench_dropout(fa, p, q, k, v, do, K, args.warmup, fwd_flops + bwd_flops, torch)
     if not args.no_decode:
         out["decode"] = bench_decode(fa, synth, torch, max(K, 20), max(args.warmup, 3), measured_traffic)
     if not args.no_cpu_baseline:

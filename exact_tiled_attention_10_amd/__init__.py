@@ -24,7 +24,7 @@ __all__ = [
     "FaError", "lib", "forward", "backward", "Plan", "flash_attn_func",
     "flash_attn_varlen_func", "workspace_size", "FA_DTYPE_F16", "FA_DTYPE_BF16",
     "forward_kvcache", "kvcache_workspace_size", "kvcache_splits", "DecodePlan",
-    "flash_attn_with_kvcache",
+    "flash_attn_with_kvcache", "new_dropout_seed",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -51,13 +51,14 @@ def lib() -> ctypes.CDLL:
         raise RuntimeError(f"{LIB_PATH} is not built; run `python -m exact_tiled_attention_10_amd.build`")
     L = ctypes.CDLL(LIB_PATH)
     P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
-    L.fa_fwd.argtypes = [P] * 7 + [I] * 9 + [F, I, P]
+    U64 = ctypes.c_uint64
+    L.fa_fwd.argtypes = [P] * 7 + [I] * 9 + [F, F, U64, I, P]
     L.fa_fwd.restype = I
     L.fa_bwd_workspace_size.argtypes = [I] * 5
     L.fa_bwd_workspace_size.restype = S
-    L.fa_bwd.argtypes = [P] * 10 + [S] + [P] * 2 + [I] * 9 + [F, I, P]
+    L.fa_bwd.argtypes = [P] * 10 + [S] + [P] * 2 + [I] * 9 + [F, F, U64, I, P]
     L.fa_bwd.restype = I
-    L.fa_bwd_stage.argtypes = [I] + [P] * 10 + [S] + [P] * 2 + [I] * 9 + [F, I, P]
+    L.fa_bwd_stage.argtypes = [I] + [P] * 10 + [S] + [P] * 2 + [I] * 9 + [F, F, U64, I, P]
     L.fa_bwd_stage.restype = I
     L.fa_fwd_kvcache_workspace_size.argtypes = [I] * 7
     L.fa_fwd_kvcache_workspace_size.restype = S
@@ -141,12 +142,21 @@ def _default_scale(d: int, softmax_scale):
     return 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
 
 
+def _seed(seed) -> int:
+    return int(seed) & (2**64 - 1)
+
+
+def new_dropout_seed() -> int:
+    """A 64-bit dropout seed drawn from torch's default CPU generator."""
+    return int(torch.randint(0, 2**62, (1,), dtype=torch.int64).item())
+
+
 def forward(q, k, v, *, causal=False, window_size=(-1, -1), softmax_scale=None,
             cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
-            out=None, lse=None):
-    """O and LSE of exact attention (see include/fa.h for the definition).
-    Returns (out, lse); lse is float32 (batch, heads, seqlen_q) or
-    (heads, total_q) for packed batches."""
+            out=None, lse=None, dropout_p=0.0, dropout_seed=0):
+    """O and LSE of exact attention (see include/fa.h for the definition,
+    dropout included).  Returns (out, lse); lse is float32 (batch, heads,
+    seqlen_q) or (heads, total_q) for packed batches."""
     L = lib()
     dt = q.dtype
     _check(q, "q"); _check(k, "k", dt, q.device); _check(v, "v", dt, q.device)
@@ -168,7 +178,8 @@ def forward(q, k, v, *, causal=False, window_size=(-1, -1), softmax_scale=None,
                   _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
                   g.batch, g.heads, g.kv_heads, g.seqlen_q, g.seqlen_k, g.d,
                   int(bool(causal)), int(window_size[0]), int(window_size[1]),
-                  _default_scale(g.d, softmax_scale), _dtype_code(q), _stream(q.device))
+                  _default_scale(g.d, softmax_scale), float(dropout_p), _seed(dropout_seed),
+                  _dtype_code(q), _stream(q.device))
     if rc != 0:
         raise FaError(rc, "fa_fwd")
     return out, lse
@@ -182,7 +193,7 @@ def workspace_size(batch, heads, seqlen_q, head_dim, dtype) -> int:
 def backward(dout, q, k, v, out, lse, *, causal=False, window_size=(-1, -1),
              softmax_scale=None, cu_seqlens_q=None, cu_seqlens_k=None,
              max_seqlen_q=None, max_seqlen_k=None, dq=None, dk=None, dv=None,
-             workspace=None):
+             workspace=None, dropout_p=0.0, dropout_seed=0):
     """dQ, dK, dV of exact attention for upstream gradient ``dout``, from the
     forward's ``out`` and ``lse`` (recomputing the scores)."""
     L = lib()
@@ -209,7 +220,8 @@ def backward(dout, q, k, v, out, lse, *, causal=False, window_size=(-1, -1),
                   _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
                   g.batch, g.heads, g.kv_heads, g.seqlen_q, g.seqlen_k, g.d,
                   int(bool(causal)), int(window_size[0]), int(window_size[1]),
-                  _default_scale(g.d, softmax_scale), _dtype_code(q), _stream(q.device))
+                  _default_scale(g.d, softmax_scale), float(dropout_p), _seed(dropout_seed),
+                  _dtype_code(q), _stream(q.device))
     if rc != 0:
         raise FaError(rc, "fa_bwd")
     return dq, dk, dv
@@ -222,7 +234,8 @@ class Plan:
     current torch stream of q's device).  Buffers are allocated once here."""
 
     def __init__(self, q, k, v, dout=None, *, causal=False, window_size=(-1, -1), softmax_scale=None,
-                 cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, stream=None):
+                 cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, stream=None,
+                 dropout_p=0.0, dropout_seed=0):
         L = lib()
         dt = q.dtype
         _check(q, "q"); _check(k, "k", dt, q.device); _check(v, "v", dt, q.device)
@@ -237,7 +250,8 @@ class Plan:
         sp = ctypes.c_void_p(st.cuda_stream)
         common = [g.batch, g.heads, g.kv_heads, g.seqlen_q, g.seqlen_k, g.d,
                   int(bool(causal)), int(window_size[0]), int(window_size[1]),
-                  _default_scale(g.d, softmax_scale), _dtype_code(q), sp]
+                  _default_scale(g.d, softmax_scale), float(dropout_p), _seed(dropout_seed),
+                  _dtype_code(q), sp]
         self._fwd = [_ptr(q), _ptr(k), _ptr(v), _ptr(self.out), _ptr(self.lse),
                      _ptr(cu_seqlens_q), _ptr(cu_seqlens_k)] + common
         if dout is not None:
@@ -268,43 +282,50 @@ class Plan:
 
 class _FlashAttn(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, softmax_scale, causal, window_size, cu_q, cu_k, max_q, max_k):
+    def forward(ctx, q, k, v, softmax_scale, causal, window_size, cu_q, cu_k, max_q, max_k,
+                dropout_p, dropout_seed):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
         out, lse = forward(q, k, v, causal=causal, window_size=window_size,
                            softmax_scale=softmax_scale, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k,
-                           max_seqlen_q=max_q, max_seqlen_k=max_k)
+                           max_seqlen_q=max_q, max_seqlen_k=max_k,
+                           dropout_p=dropout_p, dropout_seed=dropout_seed)
         ctx.save_for_backward(q, k, v, out, lse, cu_q, cu_k)
-        ctx.args = (softmax_scale, causal, window_size, max_q, max_k)
+        ctx.args = (softmax_scale, causal, window_size, max_q, max_k, dropout_p, dropout_seed)
         return out
 
     @staticmethod
     def backward(ctx, dout):
         q, k, v, out, lse, cu_q, cu_k = ctx.saved_tensors
-        softmax_scale, causal, window_size, max_q, max_k = ctx.args
+        softmax_scale, causal, window_size, max_q, max_k, dropout_p, dropout_seed = ctx.args
         dq, dk, dv = backward(dout.contiguous(), q, k, v, out, lse, causal=causal,
                               window_size=window_size, softmax_scale=softmax_scale,
                               cu_seqlens_q=cu_q, cu_seqlens_k=cu_k,
-                              max_seqlen_q=max_q, max_seqlen_k=max_k)
-        return dq, dk, dv, None, None, None, None, None, None, None
+                              max_seqlen_q=max_q, max_seqlen_k=max_k,
+                              dropout_p=dropout_p, dropout_seed=dropout_seed)
+        return dq, dk, dv, None, None, None, None, None, None, None, None, None
 
 
 def flash_attn_func(q, k, v, dropout_p=0.0, softmax_scale=None, causal=False,
-                    window_size=(-1, -1)):
-    """Autograd entry with the call shape the pages use; dropout is not
-    implemented (every call on the pages passes 0.0)."""
-    if dropout_p != 0.0:
-        raise NotImplementedError("dropout_p > 0 is not implemented")
-    return _FlashAttn.apply(q, k, v, softmax_scale, causal, tuple(window_size), None, None, None, None)
+                    window_size=(-1, -1), dropout_seed=None):
+    """Autograd entry with the call shape the pages use.  With dropout_p > 0
+    and no dropout_seed, a seed is drawn from torch's default generator; the
+    backward reuses the forward's seed."""
+    if dropout_p > 0.0 and dropout_seed is None:
+        dropout_seed = new_dropout_seed()
+    return _FlashAttn.apply(q, k, v, softmax_scale, causal, tuple(window_size), None, None, None, None,
+                            float(dropout_p), 0 if dropout_seed is None else dropout_seed)
 
 
 def flash_attn_varlen_func(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
-                           dropout_p=0.0, softmax_scale=None, causal=False, window_size=(-1, -1)):
+                           dropout_p=0.0, softmax_scale=None, causal=False, window_size=(-1, -1),
+                           dropout_seed=None):
     """Packed variable-length batches: q (total_q, heads, d), k/v (total_k,
-    kv_heads, d), int32 prefix sums cu_seqlens_*."""
-    if dropout_p != 0.0:
-        raise NotImplementedError("dropout_p > 0 is not implemented")
+    kv_heads, d), int32 prefix sums cu_seqlens_*; dropout as flash_attn_func."""
+    if dropout_p > 0.0 and dropout_seed is None:
+        dropout_seed = new_dropout_seed()
     return _FlashAttn.apply(q, k, v, softmax_scale, causal, tuple(window_size),
-                            cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+                            cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                            float(dropout_p), 0 if dropout_seed is None else dropout_seed)
 
 
 # ---------------------------------------------------------------------------

@@ -68,6 +68,18 @@ float log2e_scaled(float s) {
     return c < 1.17549435e-38f ? 1.17549435e-38f : c;
 }
 
+// Dropout threshold T (elements kept iff their 8-bit draw is below T) and
+// the scale of kept probabilities, 256 / T (0 when T = 0).  p must lie in
+// [0, 1).
+bool dropout_params(float p, uint32_t& t, float& scale_kept) {
+    if (!std::isfinite(p) || p < 0.f || p >= 1.f) return false;
+    double tt = std::floor((1.0 - (double)p) * 256.0 + 0.5);
+    tt = tt < 0.0 ? 0.0 : (tt > 256.0 ? 256.0 : tt);
+    t = (uint32_t)tt;
+    scale_kept = t > 0 ? (float)(256.0 / tt) : 0.f;
+    return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -76,10 +88,13 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
            int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
            int head_dim, int causal, int window_left, int window_right,
-           float softmax_scale, int dtype, void* stream) {
+           float softmax_scale, float dropout_p, uint64_t dropout_seed, int dtype, void* stream) {
     int rc = check_common(batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim, causal, window_left,
                           window_right, softmax_scale, dtype, cu_seqlens_q, cu_seqlens_k);
     if (rc != FA_OK) return rc;
+    uint32_t drop_t;
+    float drop_scale;
+    if (!dropout_params(dropout_p, drop_t, drop_scale)) return FA_ERR_INVALID_ARG;
     const bool has_q = (long long)batch * seqlen_q > 0, has_k = (long long)batch * seqlen_k > 0;
     if ((has_q && (!q || !o || !lse)) || (has_k && (!k || !v))) return FA_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
@@ -94,6 +109,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
     a.causal = causal; a.left = window_left; a.right = window_right;
     a.scale = softmax_scale; a.scale_log2 = log2e_scaled(softmax_scale);
     a.bf16 = dtype == FA_DTYPE_BF16;
+    a.drop_t = drop_t; a.drop_scale = drop_scale;
+    a.seed_lo = (uint32_t)dropout_seed; a.seed_hi = (uint32_t)(dropout_seed >> 32);
     return fa::launch_fwd(a, (hipStream_t)stream) == 0 ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -117,10 +134,13 @@ int bwd_common(int stage_lo, int stage_hi,
                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
                int head_dim, int causal, int window_left, int window_right,
-               float softmax_scale, int dtype, void* stream) {
+               float softmax_scale, float dropout_p, uint64_t dropout_seed, int dtype, void* stream) {
     int rc = check_common(batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim, causal, window_left,
                           window_right, softmax_scale, dtype, cu_seqlens_q, cu_seqlens_k);
     if (rc != FA_OK) return rc;
+    uint32_t drop_t;
+    float drop_scale;
+    if (!dropout_params(dropout_p, drop_t, drop_scale)) return FA_ERR_INVALID_ARG;
     const bool has_q = (long long)batch * seqlen_q > 0, has_k = (long long)batch * seqlen_k > 0;
     if ((has_q && (!q || !o || !lse || !dout || !dq)) || (has_k && (!k || !v || !dk || !dv)) || !workspace)
         return FA_ERR_INVALID_ARG;
@@ -142,6 +162,8 @@ int bwd_common(int stage_lo, int stage_hi,
     a.causal = causal; a.left = window_left; a.right = window_right;
     a.scale = softmax_scale; a.scale_log2 = log2e_scaled(softmax_scale);
     a.bf16 = dtype == FA_DTYPE_BF16;
+    a.drop_t = drop_t; a.drop_scale = drop_scale;
+    a.seed_lo = (uint32_t)dropout_seed; a.seed_hi = (uint32_t)(dropout_seed >> 32);
     for (int st = stage_lo; st <= stage_hi; ++st)
         if (fa::launch_bwd(a, st, (hipStream_t)stream) != 0) return FA_ERR_LAUNCH;
     return FA_OK;
@@ -157,10 +179,11 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
            int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
            int head_dim, int causal, int window_left, int window_right,
-           float softmax_scale, int dtype, void* stream) {
+           float softmax_scale, float dropout_p, uint64_t dropout_seed, int dtype, void* stream) {
     return bwd_common(0, 2, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes,
                       cu_seqlens_q, cu_seqlens_k, batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim,
-                      causal, window_left, window_right, softmax_scale, dtype, stream);
+                      causal, window_left, window_right, softmax_scale, dropout_p, dropout_seed, dtype,
+                      stream);
 }
 
 int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o,
@@ -169,11 +192,12 @@ int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const v
                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                  int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
                  int head_dim, int causal, int window_left, int window_right,
-                 float softmax_scale, int dtype, void* stream) {
+                 float softmax_scale, float dropout_p, uint64_t dropout_seed, int dtype, void* stream) {
     if (stage < 0 || stage > 2) return FA_ERR_INVALID_ARG;
     return bwd_common(stage, stage, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes,
                       cu_seqlens_q, cu_seqlens_k, batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim,
-                      causal, window_left, window_right, softmax_scale, dtype, stream);
+                      causal, window_left, window_right, softmax_scale, dropout_p, dropout_seed, dtype,
+                      stream);
 }
 
 }  // extern "C"

@@ -9,6 +9,11 @@
 //   dP = dO V^T,  dS = P o (dP - D),  dV = P^T dO,  dK = scale dS^T Q,
 //   dQ = scale dS K.
 //
+// With dropout (DROP; keep decisions as in the forward, fa_device.hpp), P
+// below is the undropped softmax, M the keep mask and s = 256 / T:
+//   dV = (P o M)^T dO * s,  dS = P o (M o dP * s - D),  D_i = dO_i . O_i
+// (O being the dropped output, D needs no change).
+//
 // Three kernels on one stream:
 //   bwd_rowdot   D_i = dO_i . O_i and LSE_i * log2(e) into the workspace
 //   bwd_dkdv     per key tile (outer) and every visible query tile of every
@@ -121,7 +126,7 @@ struct DqCfg {
     static constexpr int stageElems = 2 * tileElems;  // K then V
 };
 
-template <bool BF16, int D, int NW, int BN>
+template <bool BF16, int D, int NW, int BN, bool DROP>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdArgs a) {
     using C = DqCfg<D, NW, BN>;
@@ -228,7 +233,12 @@ void bwd_dq_kernel(BwdArgs a) {
         const int lo = row_lo - key0, hi = row_hi - key0;
         uint32_t dsp[KB][8];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb) {
+            u32x4 kw;  // dropout keep words of this lane's query row, as in the forward
+            if constexpr (DROP) {
+                const uint32_t jq = (uint32_t)(key0 + 32 * kb) / 4 + 2 * (r32 & 3) + half;
+                kw = quad_transpose(philox4x32_10(jq, (uint32_t)row / 4, h, b, a.seed_lo, a.seed_hi));
+            }
 #pragma unroll
             for (int i = 0; i < 16; i += 2) {
                 float p0 = fast_exp2(__builtin_fmaf(sacc[kb][i], c, -lse2));
@@ -238,8 +248,14 @@ void bwd_dq_kernel(BwdArgs a) {
                     p0 = (k0 < lo || k0 > hi) ? 0.f : p0;
                     p1 = (k0 + 1 < lo || k0 + 1 > hi) ? 0.f : p1;
                 }
-                dsp[kb][i / 2] = pack2<BF16>(p0 * (dpacc[kb][i] - dsum), p1 * (dpacc[kb][i + 1] - dsum));
+                float dp0 = dpacc[kb][i], dp1 = dpacc[kb][i + 1];
+                if constexpr (DROP) {
+                    dp0 = keep_byte(kw[i / 4], i % 4, a.drop_t) ? dp0 * a.drop_scale : 0.f;
+                    dp1 = keep_byte(kw[i / 4], (i + 1) % 4, a.drop_t) ? dp1 * a.drop_scale : 0.f;
+                }
+                dsp[kb][i / 2] = pack2<BF16>(p0 * (dp0 - dsum), p1 * (dp1 - dsum));
             }
+        }
         // dQ^T += K^T dS^T over the BN keys (k-steps of 16)
 #pragma unroll
         for (int kk = 0; kk < BN / 16; ++kk) {
@@ -299,7 +315,7 @@ struct DkdvCfg {
     static constexpr int stageBytes = 2 * tileElems * 2 + 2 * kKvBM * 4;
 };
 
-template <bool BF16, int D>
+template <bool BF16, int D, bool DROP>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdArgs a) {
     using C = DkdvCfg<D>;
@@ -413,6 +429,16 @@ void bwd_dkdv_kernel(BwdArgs a) {
         const float* dss = lses + kKvBM;
         const int lo = q_lo - row0, hi = q_hi - row0;
 
+        const int hq = hk * g + n / nt;  // query head of this step
+        // Dropout keep words of the softmax block: word g_ holds the draws of
+        // this lane's key for query rows 8 g_ + 4 half + 0..3 of the block, one
+        // byte per row.
+        u32x4 kwd;
+        auto keep_words = [&](int qb) {
+            const uint32_t iq = (uint32_t)(row0 + 32 * qb) / 4 + 2 * (r32 & 3) + half;
+            return quad_transpose(
+                byte_transpose(philox4x32_10((uint32_t)key / 4, iq, hq, b, a.seed_lo, a.seed_hi)));
+        };
         f32x16 sacc[QBS], dpacc[QBS];
         u32x4 qa[QBS][KS], da[QBS][KS];  // A operands Q, dO of each block (row r32, k-step ks)
         f32x4 l4[QBS][4], d4[QBS][4];    // lse2 and D of the rows of register group gq
@@ -453,8 +479,14 @@ void bwd_dkdv_kernel(BwdArgs a) {
             for (int t = 0; t < 2; ++t) {
                 const int i = 2 * m + t;
                 const float pr = fast_exp2(__builtin_fmaf(sacc[qb][i], c, -l4[qb][i / 4][i % 4]));
-                pv[t] = pr;
-                dv2[t] = pr * (dpacc[qb][i] - d4[qb][i / 4][i % 4]);
+                if constexpr (DROP) {
+                    const bool kp = keep_byte(kwd[i / 4], i % 4, a.drop_t);
+                    pv[t] = kp ? pr : 0.f;
+                    dv2[t] = pr * ((kp ? dpacc[qb][i] * a.drop_scale : 0.f) - d4[qb][i / 4][i % 4]);
+                } else {
+                    pv[t] = pr;
+                    dv2[t] = pr * (dpacc[qb][i] - d4[qb][i / 4][i % 4]);
+                }
             }
             pp[qb][m] = pack2<BF16>(pv[0], pv[1]);
             dsp[qb][m] = pack2<BF16>(dv2[0], dv2[1]);
@@ -481,6 +513,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
             const int bs = ph, bv = ph - 1, bp = ph - 2;  // S/dP, softmax and dV/dK blocks
             const bool hs = bs < QBS, hv = bv >= 0 && bv < QBS, hp = bp >= 0;
             if (hp && !full) mask_block(bp);
+            if constexpr (DROP) {
+                if (hv) kwd = keep_words(bv);
+            }
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 if (hs) sdp(bs, ks);
@@ -554,8 +589,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
             u32x2 wk, wv;
             wk.x = pack2<BF16>(dk[db][4 * gq] * a.scale, dk[db][4 * gq + 1] * a.scale);
             wk.y = pack2<BF16>(dk[db][4 * gq + 2] * a.scale, dk[db][4 * gq + 3] * a.scale);
-            wv.x = pack2<BF16>(dv[db][4 * gq], dv[db][4 * gq + 1]);
-            wv.y = pack2<BF16>(dv[db][4 * gq + 2], dv[db][4 * gq + 3]);
+            const float sv = DROP ? a.drop_scale : 1.f;
+            wv.x = pack2<BF16>(dv[db][4 * gq] * sv, dv[db][4 * gq + 1] * sv);
+            wv.y = pack2<BF16>(dv[db][4 * gq + 2] * sv, dv[db][4 * gq + 3] * sv);
             *(u32x2*)(dkrow + col) = wk;
             *(u32x2*)(dvrow + col) = wv;
         }
@@ -580,8 +616,8 @@ int launch_bwd_t(const BwdArgs& a, int stage, hipStream_t stream) {
     if (stage == 1) {  // dK, dV
         const int ntiles = (a.seqlen_k + kKvBN - 1) / kKvBN;
         if (ntiles > 0 && a.batch > 0) {
-            hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D>), dim3(a.batch * a.kv_heads, ntiles), dim3(256), 0,
-                               stream, a);
+            auto kern = a.drop_t < 256 ? bwd_dkdv_kernel<BF16, D, true> : bwd_dkdv_kernel<BF16, D, false>;
+            hipLaunchKernelGGL(kern, dim3(a.batch * a.kv_heads, ntiles), dim3(256), 0, stream, a);
             if (hipGetLastError() != hipSuccess) return 1;
         }
         return 0;
@@ -591,7 +627,7 @@ int launch_bwd_t(const BwdArgs& a, int stage, hipStream_t stream) {
     constexpr int BM = 32 * NW;
     const int ntiles = (a.seqlen_q + BM - 1) / BM;
     if (ntiles > 0 && a.batch > 0) {
-        auto kern = bwd_dq_kernel<BF16, D, NW, BN>;
+        auto kern = a.drop_t < 256 ? bwd_dq_kernel<BF16, D, NW, BN, true> : bwd_dq_kernel<BF16, D, NW, BN, false>;
         hipLaunchKernelGGL(kern, dim3(a.batch * a.heads, ntiles), dim3(64 * NW), 0, stream, a);
         if (hipGetLastError() != hipSuccess) return 1;
     }

@@ -175,6 +175,87 @@ __device__ __forceinline__ u32x4 read_tr(const uint16_t* tile, int ks, int mb, c
     return u32x4{l2.x, l2.y, h2.x, h2.y};
 }
 
+// ---------------------------------------------------------------------------
+// Dropout keep decisions.
+//
+// Element (sequence b, query head h, query row i, key j) is kept iff byte
+// (j mod 4) of word (i mod 4) of the Philox4x32-10 block at counter
+// (j / 4, i / 4, h, b), keyed by the 64-bit seed, is below the threshold T.
+// Philox4x32-10 is the counter-based generator of Salmon, Moraes, Dror and
+// Shaw ("Parallel random numbers: as easy as 1, 2, 3", SC 2011): ten rounds
+// of two 32 x 32 -> 64-bit products, the key advanced by two Weyl constants
+// between rounds.
+//
+// In either MFMA C layout a lane holds one row (or column) of a 32 x 32 block
+// and four runs of four consecutive columns (or rows), and the four lanes of a
+// quad (consecutive lanes, same half) share the 4 x 4 sub-blocks of those
+// runs.  So each lane draws one block (its run = its index in the quad) and the
+// quad exchanges words (quad_transpose) to give every lane the words of its
+// own row in all four runs.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                               uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c1 = (uint32_t)p1;
+        c3 = (uint32_t)p0;
+        c0 = n0;
+        c2 = n2;
+    }
+    return u32x4{c0, c1, c2, c3};
+}
+
+// One round of quad_transpose: lane t receives, from lane (t + R) mod 4, that
+// lane's word t, and stores it as out[(t + R) mod 4].
+template <int R>
+__device__ __forceinline__ void quad_round(const u32x4& w, u32x4& out, int t) {
+    // quad_perm control: lane k of the quad reads lane (k + R) mod 4
+    constexpr int kPerm = ((0 + R) & 3) | (((1 + R) & 3) << 2) | (((2 + R) & 3) << 4) | (((3 + R) & 3) << 6);
+    const int si = (t - R) & 3;  // the word lane (t - R) mod 4 wants from this lane
+    const uint32_t x = si == 0 ? w[0] : si == 1 ? w[1] : si == 2 ? w[2] : w[3];
+    const uint32_t y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kPerm, 0xF, 0xF, false);
+    const int di = (t + R) & 3;
+    out[0] = di == 0 ? y : out[0];
+    out[1] = di == 1 ? y : out[1];
+    out[2] = di == 2 ? y : out[2];
+    out[3] = di == 3 ? y : out[3];
+}
+
+// Lane t of every quad holds words w[0..3]; returns, for each g, word t of the
+// quad's lane g (a 4 x 4 transpose across the quad).
+__device__ __forceinline__ u32x4 quad_transpose(u32x4 w) {
+    const int t = threadIdx.x & 3;
+    u32x4 out = w;  // out[t] = w[t] already; the other three come from the rounds
+    quad_round<1>(w, out, t);
+    quad_round<2>(w, out, t);
+    quad_round<3>(w, out, t);
+    return out;
+}
+
+// 4 x 4 byte transpose inside a lane: byte e of out[k] = byte k of w[e].
+__device__ __forceinline__ u32x4 byte_transpose(u32x4 w) {
+    // v_perm_b32 selector bytes: 0-3 pick from the second operand, 4-7 from the first
+    const uint32_t a = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);  // w0b0 w1b0 w0b1 w1b1
+    const uint32_t b = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);  // w0b2 w1b2 w0b3 w1b3
+    const uint32_t c = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);  // w2b0 w3b0 w2b1 w3b1
+    const uint32_t d = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);  // w2b2 w3b2 w2b3 w3b3
+    return u32x4{__builtin_amdgcn_perm(c, a, 0x05040100u), __builtin_amdgcn_perm(c, a, 0x07060302u),
+                 __builtin_amdgcn_perm(d, b, 0x05040100u), __builtin_amdgcn_perm(d, b, 0x07060302u)};
+}
+
+// Byte e of a word, compared with the keep threshold.
+__device__ __forceinline__ bool keep_byte(uint32_t w, int e, uint32_t thresh) {
+    return ((w >> (8 * e)) & 0xFFu) < thresh;
+}
+
 // Geometry of one (batch, head) problem slice, resolved from cu_seqlens.
 struct Seq {
     int64_t q_start, k_start;  // first packed row of the sequence

@@ -26,6 +26,11 @@
 // and the final O = acc / l and LSE = m + ln l are the same numbers.  This
 // skips the rescale of the accumulator registers on almost every tile.
 //
+// Dropout (DROP): after the exponent each probability is kept or zeroed by
+// its Philox draw (fa_device.hpp) before it enters P.V; the row sum l keeps
+// every probability, and the kept ones are scaled by 256 / T in the epilogue,
+// so O = (P o M) V * 256 / T and LSE is that of the undropped softmax.
+//
 // Masked scores are set to -inf before the exponent; the host clamps
 // scale*log2(e) to at least the smallest normal float, so -inf * c stays -inf
 // and exp2 gives an exact 0 even for softmax_scale == 0 (where every finite
@@ -55,7 +60,7 @@ struct FwdCfg {
     static_assert(kDmaBlocks % NW == 0, "tiles must split evenly into 1 KiB blocks per wave");
 };
 
-template <bool BF16, int D, int NW, int QB, int BN, int WPE>
+template <bool BF16, int D, int NW, int QB, int BN, int WPE, bool DROP>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(WPE, WPE)))
 void fwd_kernel(FwdArgs a) {
     using C = FwdCfg<D, NW, BN>;
@@ -216,6 +221,19 @@ void fwd_kernel(FwdArgs a) {
                     }
             }
         }
+        // Dropout: this lane's keep words, one per 32 x 32 block: word g holds the
+        // draws of its query row for keys 8 g + 4 half + 0..3 of the block.
+        u32x4 kw[DROP ? KB : 1][DROP ? QB : 1];
+        if constexpr (DROP) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    const uint32_t jq = (uint32_t)(key0 + 32 * kb) / 4 + 2 * (r32 & 3) + half;
+                    const uint32_t iq = (uint32_t)(wq0 + 32 * qb + r32) / 4;
+                    kw[kb][qb] = quad_transpose(philox4x32_10(jq, iq, h, b, a.seed_lo, a.seed_hi));
+                }
+        }
         // V^T fragments of the first key step: read now, used after the softmax.
         auto read_vt = [&](int kk, int db) { return read_tr<D, DB>(vs_lds, kk, db, v_rd); };
         u32x4 vf0[DB];
@@ -246,9 +264,14 @@ void fwd_kernel(FwdArgs a) {
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; i += 2) {
-                    const float p0 = fast_exp2(__builtin_fmaf(sacc[kb][qb][i], c, -mc));
-                    const float p1 = fast_exp2(__builtin_fmaf(sacc[kb][qb][i + 1], c, -mc));
+                    float p0 = fast_exp2(__builtin_fmaf(sacc[kb][qb][i], c, -mc));
+                    float p1 = fast_exp2(__builtin_fmaf(sacc[kb][qb][i + 1], c, -mc));
                     lsum += p0 + p1;
+                    if constexpr (DROP) {
+                        const uint32_t w = kw[kb][qb][i / 4];
+                        p0 = keep_byte(w, i % 4, a.drop_t) ? p0 : 0.f;
+                        p1 = keep_byte(w, (i + 1) % 4, a.drop_t) ? p1 : 0.f;
+                    }
                     pk[kb][qb][i / 2] = pack2<BF16>(p0, p1);
                 }
             l_part[qb] += lsum;
@@ -295,7 +318,7 @@ void fwd_kernel(FwdArgs a) {
     for (int qb = 0; qb < QB; ++qb) {
         const int row = wq0 + 32 * qb + r32;
         const float l = sum_halves(l_part[qb]);
-        const float inv = l > 0.f ? 1.f / l : 0.f;
+        const float inv = l > 0.f ? (DROP ? a.drop_scale : 1.f) / l : 0.f;
         if (row < s.len_q) {
             uint16_t* orow = obase + (int64_t)row * q_row_stride;
 #pragma unroll
@@ -319,7 +342,8 @@ int launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
     using C = FwdCfg<D, NW, BN>;
     const int ntiles = (a.seqlen_q + BM - 1) / BM;
     if (ntiles == 0 || a.batch == 0) return 0;
-    auto kern = fwd_kernel<BF16, D, NW, QB, BN, WPE>;
+    auto kern = a.drop_t < 256 ? fwd_kernel<BF16, D, NW, QB, BN, WPE, true>
+                               : fwd_kernel<BF16, D, NW, QB, BN, WPE, false>;
     dim3 grid(a.batch * a.heads, ntiles);
     hipLaunchKernelGGL(kern, grid, dim3(C::kThreads), 0, stream, a);
     return hipGetLastError() == hipSuccess ? 0 : 1;

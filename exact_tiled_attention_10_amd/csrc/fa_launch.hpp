@@ -20,6 +20,11 @@ struct FwdArgs {
     float scale;       // softmax scale
     float scale_log2;  // softmax scale * log2(e)
     int bf16;
+    // dropout: keep iff the element's 8-bit draw < drop_t (256: no dropout);
+    // kept probabilities are scaled by drop_scale = 256 / drop_t
+    uint32_t drop_t;
+    float drop_scale;
+    uint32_t seed_lo, seed_hi;
 };
 
 struct BwdArgs {
@@ -41,6 +46,9 @@ struct BwdArgs {
     float scale;
     float scale_log2;
     int bf16;
+    uint32_t drop_t;     // as in FwdArgs
+    float drop_scale;
+    uint32_t seed_lo, seed_hi;
 };
 
 struct DecArgs {

@@ -40,6 +40,19 @@
  *
  * LSE[i] = ln(sum over visible j of exp(softmax_scale * q_i . k_j)).
  *
+ * Dropout (the dropout_p argument of the attention call, overview page
+ * section 3.3): with T = floor((1 - dropout_p) * 256 + 1/2), computed from
+ * the float dropout_p, each softmax probability P_ij is kept and scaled by
+ * 256 / T, or set to 0, before the weighted sum of V: O_i = sum_j P_ij M_ij
+ * (256 / T) v_j.  LSE stays that of the undropped softmax.  Element
+ * (sequence b, query head h, query row i, key j; i and j counted inside the
+ * sequence) is kept iff byte (j mod 4) of word (i mod 4) of the
+ * Philox4x32-10 block (Salmon et al., SC 2011) at counter (j / 4, i / 4, h,
+ * b) with key (dropout_seed low 32 bits, high 32 bits) is below T.  The
+ * backward given the same dropout_p and dropout_seed differentiates exactly
+ * that function.  dropout_p = 0 (T = 256) is plain attention; T = 0 drops
+ * everything (O = 0).
+ *
  * Arithmetic: 16-bit inputs (fp16 or bf16, same type for every tensor),
  * products on the matrix cores with fp32 accumulation, softmax statistics
  * in fp32, P rounded to the input type before P.V, outputs rounded to
@@ -97,13 +110,14 @@ enum fa_dtype { FA_DTYPE_F16 = 0, FA_DTYPE_BF16 = 1 };
  *   causal in {0, 1}, window_left >= -1, window_right >= -1 (-1 = unbounded),
  *   softmax_scale finite and >= 0 (callers wanting the default pass
  *   1/sqrt(head_dim)), dtype one of fa_dtype.
+ *   dropout_p in [0, 1), dropout_seed any 64-bit value: see "Dropout" below.
  * Returns FA_OK or an fa_status code; nothing is enqueued on error.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
            int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
            int head_dim, int causal, int window_left, int window_right,
-           float softmax_scale, int dtype, void* stream);
+           float softmax_scale, float dropout_p, uint64_t dropout_seed, int dtype, void* stream);
 
 /*
  * Bytes of device workspace fa_bwd needs for these sizes: two float32
@@ -125,7 +139,7 @@ size_t fa_bwd_workspace_size(int batch, int heads, int seqlen_q, int head_dim, i
  *   fa_bwd_workspace_size(batch, heads, seqlen_q, head_dim, dtype) bytes,
  *   owned by the caller; its contents on entry do not matter.
  * All other arguments as for fa_fwd, which must have produced o and lse
- * with the same arguments.
+ * with the same arguments (dropout_p and dropout_seed included).
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const float* lse, const void* dout, void* dq, void* dk, void* dv,
@@ -133,7 +147,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
            int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
            int head_dim, int causal, int window_left, int window_right,
-           float softmax_scale, int dtype, void* stream);
+           float softmax_scale, float dropout_p, uint64_t dropout_seed, int dtype, void* stream);
 
 /*
  * One stage of fa_bwd, for callers that schedule or time the three kernels
@@ -149,7 +163,7 @@ int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const v
                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                  int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
                  int head_dim, int causal, int window_left, int window_right,
-                 float softmax_scale, int dtype, void* stream);
+                 float softmax_scale, float dropout_p, uint64_t dropout_seed, int dtype, void* stream);
 
 /*
  * Decode over a key/value cache (the KV-cache call named on the overview
