@@ -21,6 +21,11 @@ std::atomic<int> g_arch_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
+// Supported head dimensions: multiples of 8 (16-byte rows) up to 128; the
+// kernels run them in tiles 64 or 128 wide.
+bool head_dim_ok(int d) { return d >= 8 && d <= 128 && d % 8 == 0; }
+int tile_width(int d) { return d > 64 ? 128 : 64; }
+
 int check_common(int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k, int head_dim,
                  int causal, int window_left, int window_right, float softmax_scale, int dtype,
                  const int32_t* cu_q, const int32_t* cu_k) {
@@ -34,7 +39,7 @@ int check_common(int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
     // indices are 32-bit inside a sequence, 64-bit across the batch
     if ((long long)batch * heads > (1LL << 31) - 1) return FA_ERR_INVALID_ARG;
     if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
-    if (head_dim != 64 && head_dim != 128) return FA_ERR_UNSUPPORTED;
+    if (!head_dim_ok(head_dim)) return FA_ERR_UNSUPPORTED;
     return FA_OK;
 }
 
@@ -116,7 +121,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 size_t fa_bwd_workspace_size(int batch, int heads, int seqlen_q, int head_dim, int dtype) {
     if (batch < 0 || heads < 1 || seqlen_q < 0) return 0;
-    if (head_dim != 64 && head_dim != 128) return 0;
+    if (!head_dim_ok(head_dim)) return 0;
     if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return 0;
     // two float arrays (D and LSE * log2 e), each one entry per query row and head
     const size_t n = 2 * (size_t)batch * (size_t)heads * (size_t)seqlen_q * sizeof(float);
@@ -254,9 +259,9 @@ size_t fa_fwd_kvcache_workspace_size(int batch, int heads, int kv_heads, int seq
                                      int head_dim, int num_splits) {
     if (batch < 0 || heads < 1 || kv_heads < 1 || heads % kv_heads != 0 || seqlen_q < 0 || seqlen_k < 0)
         return 0;
-    if (head_dim != 64 && head_dim != 128) return 0;
+    if (!head_dim_ok(head_dim)) return 0;
     const DecPlan p = dec_plan(batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim, num_splits);
-    return (dec_ws_o_elems(p, kv_heads, head_dim) + dec_ws_lse_elems(p, kv_heads)) * sizeof(float) +
+    return (dec_ws_o_elems(p, kv_heads, tile_width(head_dim)) + dec_ws_lse_elems(p, kv_heads)) * sizeof(float) +
            ((size_t)batch + 1) * sizeof(int64_t);
 }
 
@@ -290,7 +295,7 @@ int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, void
     a.q = q; a.kc = k_cache; a.vc = v_cache; a.o = o; a.lse = lse;
     a.cache_lens = cache_seqlens;
     a.ws_o = (float*)workspace;
-    a.ws_lse = a.ws_o + dec_ws_o_elems(p, kv_heads, head_dim);
+    a.ws_lse = a.ws_o + dec_ws_o_elems(p, kv_heads, tile_width(head_dim));
     a.prefix = (int64_t*)(a.ws_lse + dec_ws_lse_elems(p, kv_heads));
     a.batch = batch; a.heads = heads; a.kv_heads = kv_heads;
     a.seqlen_q = seqlen_q; a.seqlen_k = seqlen_k; a.head_dim = head_dim;
@@ -305,7 +310,7 @@ int fa_fwd_kvcache_splits(int batch, int heads, int kv_heads, int seqlen_q, int 
                           int num_splits) {
     if (batch < 0 || heads < 1 || kv_heads < 1 || heads % kv_heads != 0 || seqlen_q < 0 || seqlen_k < 0)
         return 0;
-    if (head_dim != 64 && head_dim != 128) return 0;
+    if (!head_dim_ok(head_dim)) return 0;
     return dec_plan(batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim, num_splits).waves;
 }
 
@@ -313,7 +318,7 @@ const char* fa_strerror(int status) {
     switch (status) {
         case FA_OK: return "ok";
         case FA_ERR_INVALID_ARG: return "invalid argument";
-        case FA_ERR_UNSUPPORTED: return "unsupported head_dim or dtype";
+        case FA_ERR_UNSUPPORTED: return "unsupported head_dim (a multiple of 8 up to 128) or dtype";
         case FA_ERR_ARCH: return "no gfx950 (MI355X) device is current";
         case FA_ERR_WORKSPACE: return "workspace too small";
         case FA_ERR_LAUNCH: return "kernel launch failed";

@@ -14,6 +14,11 @@
 //   dV = (P o M)^T dO * s,  dS = P o (M o dP * s - D),  D_i = dO_i . O_i
 // (O being the dropped output, D needs no change).
 //
+// Head dimension: as in the forward, tiles are D = 64 or 128 wide and any
+// head_dim dh that is a multiple of 8 up to D runs in them: global rows are dh
+// long, register-resident fragments are zero past dh, direct loads repeat the
+// row's last valid chunk past dh, and columns past dh are not stored.
+//
 // Three kernels on one stream:
 //   bwd_rowdot   D_i = dO_i . O_i and LSE_i * log2(e) into the workspace
 //   bwd_dkdv     per key tile (outer) and every visible query tile of every
@@ -53,8 +58,8 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(BwdArgs a) {
     const int h = (int)(item % a.heads);
     float acc = 0.f;
     const bool live = t < rows;
-    if (live) {
-        const int64_t off = (t * a.heads + h) * D + part * 8;
+    if (live && part * 8 < a.head_dim) {
+        const int64_t off = (t * a.heads + h) * a.head_dim + part * 8;
         const u32x4 o4 = *(const u32x4*)((const uint16_t*)a.o + off);
         const u32x4 d4 = *(const u32x4*)((const uint16_t*)a.dout + off);
 #pragma unroll
@@ -90,14 +95,16 @@ struct TileDma {
     static_assert(kBlocks % NW == 0, "tile must split evenly into 1 KiB blocks per wave");
     int goff[kPerWave];
     int row[kPerWave];
-    __device__ __forceinline__ void init(int wave, int lane, int stride) {
+    // dh: the tensor's row length (multiple of 8, at most D); slots past it
+    // receive the row's last valid chunk again
+    __device__ __forceinline__ void init(int wave, int lane, int stride, int dh) {
 #pragma unroll
         for (int i = 0; i < kPerWave; ++i) {
             const int bi = wave * kPerWave + i;
             const int r = bi * kRowsPerBlock + lane / CPR;
             const int slot = lane % CPR;
             row[i] = r;
-            goff[i] = r * stride + ((slot ^ swz<CPR>(r)) * 8);
+            goff[i] = r * stride + min(slot ^ swz<CPR>(r), dh / 8 - 1) * 8;
         }
     }
     // g: first row of the tile in global memory; last: last valid row index
@@ -149,12 +156,13 @@ void bwd_dq_kernel(BwdArgs a) {
     if (i0 >= s.len_q) return;
     const Mask mk{a.causal, a.left, a.right};
     const int hk = h / (a.heads / a.kv_heads);
-    const int64_t q_stride = (int64_t)a.heads * D;
-    const int kv_stride = a.kv_heads * D;
-    const uint16_t* qbase = (const uint16_t*)a.q + (s.q_start * a.heads + h) * D;
-    const uint16_t* dobase = (const uint16_t*)a.dout + (s.q_start * a.heads + h) * D;
-    const uint16_t* kbase = (const uint16_t*)a.k + (s.k_start * a.kv_heads + hk) * D;
-    const uint16_t* vbase = (const uint16_t*)a.v + (s.k_start * a.kv_heads + hk) * D;
+    const int dh = a.head_dim;
+    const int64_t q_stride = (int64_t)a.heads * dh;
+    const int kv_stride = a.kv_heads * dh;
+    const uint16_t* qbase = (const uint16_t*)a.q + (s.q_start * a.heads + h) * dh;
+    const uint16_t* dobase = (const uint16_t*)a.dout + (s.q_start * a.heads + h) * dh;
+    const uint16_t* kbase = (const uint16_t*)a.k + (s.k_start * a.kv_heads + hk) * dh;
+    const uint16_t* vbase = (const uint16_t*)a.v + (s.k_start * a.kv_heads + hk) * dh;
     const int64_t rowidx0 = a.cu_q ? (int64_t)h * a.cu_q[a.batch] + s.q_start
                                    : ((int64_t)b * a.heads + h) * a.seqlen_q;
 
@@ -176,15 +184,16 @@ void bwd_dq_kernel(BwdArgs a) {
     u32x4 qf[KS], dof[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-        qf[ks] = row_ok ? *(const u32x4*)(qbase + (int64_t)row * q_stride + ks * 16 + 8 * half) : u32x4{0, 0, 0, 0};
-        dof[ks] = row_ok ? *(const u32x4*)(dobase + (int64_t)row * q_stride + ks * 16 + 8 * half) : u32x4{0, 0, 0, 0};
+        const bool ok = row_ok && ks * 16 + 8 * half < dh;
+        qf[ks] = ok ? *(const u32x4*)(qbase + (int64_t)row * q_stride + ks * 16 + 8 * half) : u32x4{0, 0, 0, 0};
+        dof[ks] = ok ? *(const u32x4*)(dobase + (int64_t)row * q_stride + ks * 16 + 8 * half) : u32x4{0, 0, 0, 0};
     }
     const float lse2 = row_ok ? a.lse2[rowidx0 + row] : __builtin_inff();  // +inf: P = 0 on padding rows
     const float dsum = row_ok ? a.dsum[rowidx0 + row] : 0.f;
     const int row_lo = mk.lo_of(row, s), row_hi = mk.hi_of(row, s);
 
     Dma dma;
-    dma.init(wave, lane, kv_stride);
+    dma.init(wave, lane, kv_stride, dh);
     int k_rd[KS];  // A operand reads of the K / V tiles: row r32, chunk 2 ks + half
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) k_rd[ks] = r32 * D + (((2 * ks + half) ^ swz<CPR>(r32)) * 8);
@@ -283,15 +292,17 @@ void bwd_dq_kernel(BwdArgs a) {
         }
     }
     if (!row_ok) return;
-    uint16_t* dqrow = (uint16_t*)a.dq + ((s.q_start + row) * a.heads + h) * D;
+    uint16_t* dqrow = (uint16_t*)a.dq + ((s.q_start + row) * a.heads + h) * dh;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
+            const int col = db * 32 + 8 * gq + 4 * half;  // four columns, all below dh or none
+            if (col >= dh) continue;
             u32x2 w;
             w.x = pack2<BF16>(dq[db][4 * gq] * a.scale, dq[db][4 * gq + 1] * a.scale);
             w.y = pack2<BF16>(dq[db][4 * gq + 2] * a.scale, dq[db][4 * gq + 3] * a.scale);
-            *(u32x2*)(dqrow + db * 32 + 8 * gq + 4 * half) = w;
+            *(u32x2*)(dqrow + col) = w;
         }
 }
 
@@ -336,9 +347,10 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const Mask mk{a.causal, a.left, a.right};
     const int j1 = min(j0 + kKvBN, s.len_k) - 1;
 
-    const int q_stride = a.heads * D, kv_stride = a.kv_heads * D;
-    const uint16_t* kbase = (const uint16_t*)a.k + (s.k_start * a.kv_heads + hk) * D;
-    const uint16_t* vbase = (const uint16_t*)a.v + (s.k_start * a.kv_heads + hk) * D;
+    const int dh = a.head_dim;
+    const int q_stride = a.heads * dh, kv_stride = a.kv_heads * dh;
+    const uint16_t* kbase = (const uint16_t*)a.k + (s.k_start * a.kv_heads + hk) * dh;
+    const uint16_t* vbase = (const uint16_t*)a.v + (s.k_start * a.kv_heads + hk) * dh;
     const int64_t total_q = a.cu_q ? (int64_t)a.cu_q[a.batch] : 0;
 
     // Query rows that see any key of this tile.
@@ -363,7 +375,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
     u32x4 kf[KS], vf[KS];  // K^T, V^T B operands: lane column = key
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-        const bool ok = key < s.len_k;
+        const bool ok = key < s.len_k && ks * 16 + 8 * half < dh;
         kf[ks] = ok ? *(const u32x4*)(kbase + (int64_t)key * kv_stride + ks * 16 + 8 * half) : u32x4{0, 0, 0, 0};
         vf[ks] = ok ? *(const u32x4*)(vbase + (int64_t)key * kv_stride + ks * 16 + 8 * half) : u32x4{0, 0, 0, 0};
     }
@@ -373,7 +385,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const float c = a.scale_log2;
 
     Dma dma;
-    dma.init(wave, lane, q_stride);
+    dma.init(wave, lane, q_stride, dh);
     int q_rd[KS];  // A operand reads of the Q / dO tiles: row r32 (+32 qb), chunk 2 ks + half
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) q_rd[ks] = r32 * D + (((2 * ks + half) ^ swz<CPR>(r32)) * 8);
@@ -389,7 +401,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
         const int row0 = (it_lo + n % nt) * kKvBM;
         const bool tail = row0 + kKvBM > s.len_q;
         const int last = s.len_q - 1 - row0;
-        const int64_t hoff = (s.q_start * a.heads + h) * D + (int64_t)row0 * q_stride;
+        const int64_t hoff = (s.q_start * a.heads + h) * dh + (int64_t)row0 * q_stride;
         uint16_t* qt = q_lds(buf);
         dma.issue((const uint16_t*)a.q + hoff, qt, wave, q_stride, tail, last);
         dma.issue((const uint16_t*)a.dout + hoff, qt + C::tileElems, wave, q_stride, tail, last);
@@ -579,13 +591,14 @@ void bwd_dkdv_kernel(BwdArgs a) {
 
     // store dK = scale * dK^T, dV = dV^T (lane column = key, registers = d)
     if (!wave_live || key >= s.len_k) return;
-    uint16_t* dkrow = (uint16_t*)a.dk + ((s.k_start + key) * a.kv_heads + hk) * D;
-    uint16_t* dvrow = (uint16_t*)a.dv + ((s.k_start + key) * a.kv_heads + hk) * D;
+    uint16_t* dkrow = (uint16_t*)a.dk + ((s.k_start + key) * a.kv_heads + hk) * dh;
+    uint16_t* dvrow = (uint16_t*)a.dv + ((s.k_start + key) * a.kv_heads + hk) * dh;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-            const int col = db * 32 + 8 * gq + 4 * half;
+            const int col = db * 32 + 8 * gq + 4 * half;  // four columns, all below dh or none
+            if (col >= dh) continue;
             u32x2 wk, wv;
             wk.x = pack2<BF16>(dk[db][4 * gq] * a.scale, dk[db][4 * gq + 1] * a.scale);
             wk.y = pack2<BF16>(dk[db][4 * gq + 2] * a.scale, dk[db][4 * gq + 3] * a.scale);
@@ -637,9 +650,10 @@ int launch_bwd_t(const BwdArgs& a, int stage, hipStream_t stream) {
 }  // namespace
 
 int launch_bwd(const BwdArgs& a, int stage, hipStream_t stream) {
+    // tile width: the smallest of 64, 128 holding head_dim
     if (a.bf16)
-        return a.head_dim == 128 ? launch_bwd_t<true, 128>(a, stage, stream) : launch_bwd_t<true, 64>(a, stage, stream);
-    return a.head_dim == 128 ? launch_bwd_t<false, 128>(a, stage, stream) : launch_bwd_t<false, 64>(a, stage, stream);
+        return a.head_dim > 64 ? launch_bwd_t<true, 128>(a, stage, stream) : launch_bwd_t<true, 64>(a, stage, stream);
+    return a.head_dim > 64 ? launch_bwd_t<false, 128>(a, stage, stream) : launch_bwd_t<false, 64>(a, stage, stream);
 }
 
 }  // namespace fa

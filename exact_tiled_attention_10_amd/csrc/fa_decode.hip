@@ -29,6 +29,9 @@
 //     column (lazy rescale, as in the forward kernel), O^T += V^T P^T;
 //   * a second kernel merges, for every output row, the pieces of its
 //     segment: LSE = log sum_p e^{LSE_p}, O = sum_p e^{LSE_p - LSE} O_p.
+// Head dimension as in the forward: tiles D = 64 or 128 wide run any head_dim
+// dh that is a multiple of 8 up to D (q zero past dh, cache loads repeat the
+// row's last valid chunk past dh, columns past dh not stored).
 // Masking, alignment and empty-row conventions are those of the forward
 // (bottom-right causal alignment, inclusive windows, O = 0 and LSE = -inf
 // for a row without visible keys).
@@ -166,11 +169,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecArgs a) {
     const int nq = a.seqlen_q;
     const int rows = g * nq;
     const Mask mk{a.causal, a.left, a.right};
-    const int kv_stride = a.kv_heads * D;
+    const int dh = a.head_dim;  // multiple of 8, at most D
+    const int kv_stride = a.kv_heads * dh;
     const float c = a.scale_log2;
     // load i of a tile: lane reads chunk lane % CPR of row i * kRowsPerLd + lane / CPR
     // and later writes it to that row's swizzled slot in LDS
     const int ld_r = lane / C::CPR, ld_c = lane % C::CPR;
+    const int ld_cg = min(ld_c, dh / 8 - 1);  // chunk read from the global row
     int st_off[C::kLd];
 #pragma unroll
     for (int i = 0; i < C::kLd; ++i) {
@@ -207,13 +212,14 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecArgs a) {
 
         u32x4 qf[KS];
         {
-            const uint16_t* qrow = (const uint16_t*)a.q + ((s.q_start + t) * a.heads + hq) * D;
+            const uint16_t* qrow = (const uint16_t*)a.q + ((s.q_start + t) * a.heads + hq) * dh;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                qf[ks] = live ? *(const u32x4*)(qrow + ks * 16 + 8 * half) : u32x4{0, 0, 0, 0};
+                qf[ks] = live && ks * 16 + 8 * half < dh ? *(const u32x4*)(qrow + ks * 16 + 8 * half)
+                                                         : u32x4{0, 0, 0, 0};
         }
-        const uint16_t* kbase = (const uint16_t*)a.kc + (s.k_start * a.kv_heads + hk) * D;
-        const uint16_t* vbase = (const uint16_t*)a.vc + (s.k_start * a.kv_heads + hk) * D;
+        const uint16_t* kbase = (const uint16_t*)a.kc + (s.k_start * a.kv_heads + hk) * dh;
+        const uint16_t* vbase = (const uint16_t*)a.vc + (s.k_start * a.kv_heads + hk) * dh;
 
         f32x16 acc[DB];
 #pragma unroll
@@ -228,7 +234,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecArgs a) {
             for (int i = 0; i < C::kLd; ++i) {
                 // rows past the end (the look-ahead of the last steps) re-read the last row
                 const int row = min(key0 + i * C::kRowsPerLd + ld_r, len_k - 1);
-                const int64_t o = (int64_t)row * kv_stride + ld_c * 8;
+                const int64_t o = (int64_t)row * kv_stride + ld_cg * 8;
                 kx[i] = *(const u32x4*)(kbase + o);
                 vx[i] = *(const u32x4*)(vbase + o);
             }
@@ -408,13 +414,15 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecArgs a) {
             lse = mx + __logf(wsum);
         }
     }
-    uint16_t* out = (uint16_t*)a.o + (((int64_t)b * nq + t) * a.heads + hq) * D;
-    if constexpr (BF16) {
-        const __bf16 hv = (__bf16)o;
-        out[d] = __builtin_bit_cast(uint16_t, hv);
-    } else {
-        const _Float16 hv = (_Float16)o;
-        out[d] = __builtin_bit_cast(uint16_t, hv);
+    uint16_t* out = (uint16_t*)a.o + (((int64_t)b * nq + t) * a.heads + hq) * a.head_dim;
+    if (d < a.head_dim) {
+        if constexpr (BF16) {
+            const __bf16 hv = (__bf16)o;
+            out[d] = __builtin_bit_cast(uint16_t, hv);
+        } else {
+            const _Float16 hv = (_Float16)o;
+            out[d] = __builtin_bit_cast(uint16_t, hv);
+        }
     }
     if (d == 0) a.lse[row] = lse;
 }
@@ -433,8 +441,8 @@ int launch_decode_t(const DecArgs& a, hipStream_t stream) {
 
 int launch_decode(const DecArgs& a, hipStream_t stream) {
     if (a.bf16)
-        return a.head_dim == 128 ? launch_decode_t<true, 128>(a, stream) : launch_decode_t<true, 64>(a, stream);
-    return a.head_dim == 128 ? launch_decode_t<false, 128>(a, stream) : launch_decode_t<false, 64>(a, stream);
+        return a.head_dim > 64 ? launch_decode_t<true, 128>(a, stream) : launch_decode_t<true, 64>(a, stream);
+    return a.head_dim > 64 ? launch_decode_t<false, 128>(a, stream) : launch_decode_t<false, 64>(a, stream);
 }
 
 }  // namespace fa

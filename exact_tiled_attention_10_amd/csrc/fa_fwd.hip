@@ -31,6 +31,13 @@
 // every probability, and the kept ones are scaled by 256 / T in the epilogue,
 // so O = (P o M) V * 256 / T and LSE is that of the undropped softmax.
 //
+// Head dimension: the kernels are built for tile widths D = 64 and 128 and
+// run any head_dim dh that is a multiple of 8 up to D.  Global rows are dh
+// long; the resident Q^T fragments hold zeros past dh, and the direct loads
+// of K and V fill the columns past dh with a copy of the row's last valid
+// chunk (finite values that only ever meet those zeros in S, and only reach
+// the columns of O past dh, which are not stored).
+//
 // Masked scores are set to -inf before the exponent; the host clamps
 // scale*log2(e) to at least the smallest normal float, so -inf * c stays -inf
 // and exp2 gives an exact 0 even for softmax_scale == 0 (where every finite
@@ -89,12 +96,13 @@ void fwd_kernel(FwdArgs a) {
     const Mask mk{a.causal, a.left, a.right};
     const int hk = h / (a.heads / a.kv_heads);
 
-    const int64_t q_row_stride = (int64_t)a.heads * D;
-    const int kv_row_stride = a.kv_heads * D;
-    const uint16_t* qbase = (const uint16_t*)a.q + (s.q_start * a.heads + h) * D;
-    const uint16_t* kbase = (const uint16_t*)a.k + (s.k_start * a.kv_heads + hk) * D;
-    const uint16_t* vbase = (const uint16_t*)a.v + (s.k_start * a.kv_heads + hk) * D;
-    uint16_t* obase = (uint16_t*)a.o + (s.q_start * a.heads + h) * D;
+    const int dh = a.head_dim;  // multiple of 8, at most D
+    const int64_t q_row_stride = (int64_t)a.heads * dh;
+    const int kv_row_stride = a.kv_heads * dh;
+    const uint16_t* qbase = (const uint16_t*)a.q + (s.q_start * a.heads + h) * dh;
+    const uint16_t* kbase = (const uint16_t*)a.k + (s.k_start * a.kv_heads + hk) * dh;
+    const uint16_t* vbase = (const uint16_t*)a.v + (s.k_start * a.kv_heads + hk) * dh;
+    uint16_t* obase = (uint16_t*)a.o + (s.q_start * a.heads + h) * dh;
     float* lsebase = a.cu_q ? a.lse + (int64_t)h * a.cu_q[a.batch] + s.q_start
                             : a.lse + ((int64_t)b * a.heads + h) * a.seqlen_q;
 
@@ -122,7 +130,7 @@ void fwd_kernel(FwdArgs a) {
         const int row = wq0 + 32 * qb + r32;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            qf[qb][ks] = row < s.len_q
+            qf[qb][ks] = row < s.len_q && ks * 16 + 8 * half < dh
                              ? *(const u32x4*)(qbase + (int64_t)row * q_row_stride + ks * 16 + 8 * half)
                              : u32x4{0, 0, 0, 0};
     }
@@ -138,7 +146,8 @@ void fwd_kernel(FwdArgs a) {
         const int row = bi * C::kRowsPerBlock + lane / C::CPR;
         const int slot = lane % C::CPR;
         dma_row[i] = row;
-        dma_goff[i] = row * kv_row_stride + ((slot ^ swz<C::CPR>(row)) * 8);
+        const int chunk = min(slot ^ swz<C::CPR>(row), dh / 8 - 1);  // columns past dh: last chunk again
+        dma_goff[i] = row * kv_row_stride + chunk * 8;
     }
     // S^T operand reads of K: lane (r32, half) reads row kb*32 + r32, chunk 2 ks + half.
     int k_rd[KS];
@@ -325,10 +334,12 @@ void fwd_kernel(FwdArgs a) {
             for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
+                    const int col = db * 32 + 8 * g + 4 * half;  // four columns, all below dh or none
+                    if (col >= dh) continue;
                     u32x2 w;
                     w.x = pack2<BF16>(acc[db][qb][4 * g] * inv, acc[db][qb][4 * g + 1] * inv);
                     w.y = pack2<BF16>(acc[db][qb][4 * g + 2] * inv, acc[db][qb][4 * g + 3] * inv);
-                    *(u32x2*)(orow + db * 32 + 8 * g + 4 * half) = w;
+                    *(u32x2*)(orow + col) = w;
                 }
             if (half == 0)
                 lsebase[row] = l > 0.f ? m_run[qb] * a.scale + logf(l) : kNegInf;
@@ -374,11 +385,12 @@ int launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
 int launch_fwd(const FwdArgs& a, hipStream_t stream) {
     constexpr int NW = FA_FWD_NW, QB = FA_FWD_QB, W = FA_FWD_WPE;
     constexpr int B1 = FA_FWD_BN128, B2 = FA_FWD_BN64;
+    // tile width: the smallest of 64, 128 holding head_dim
     if (a.bf16)
-        return a.head_dim == 128 ? launch_fwd_t<true, 128, NW, QB, B1, W>(a, stream)
-                                 : launch_fwd_t<true, 64, NW, QB, B2, W>(a, stream);
-    return a.head_dim == 128 ? launch_fwd_t<false, 128, NW, QB, B1, W>(a, stream)
-                             : launch_fwd_t<false, 64, NW, QB, B2, W>(a, stream);
+        return a.head_dim > 64 ? launch_fwd_t<true, 128, NW, QB, B1, W>(a, stream)
+                               : launch_fwd_t<true, 64, NW, QB, B2, W>(a, stream);
+    return a.head_dim > 64 ? launch_fwd_t<false, 128, NW, QB, B1, W>(a, stream)
+                           : launch_fwd_t<false, 64, NW, QB, B2, W>(a, stream);
 }
 
 }  // namespace fa

@@ -60,7 +60,7 @@ struct DecArgs {
     const int32_t* cache_lens;  // [batch] valid cache rows, or null (all seqlen_k)
     // workspace: one slot of 32 rows per piece and kv head
     // ((groups + segments) * kv_heads slots)
-    float* ws_o;         // [slots, 32, D] partial O, normalised
+    float* ws_o;         // [slots, 32, D] partial O, normalised (D: the tile width)
     float* ws_lse;       // [slots, 32] partial LSE
     int64_t* prefix;     // [batch + 1] prefix sums of the per-sequence step counts
     int batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim;

@@ -12,7 +12,8 @@
  * section 4.2 (question 4) the causal upper-triangular mask.  The install
  * guide page (yfxerp.com/news/195771, section 1) names the sliding window
  * (window_size) and the backward that recomputes the scores instead of
- * storing them; its section 3.3 gives the head_dim contract.  The same
+ * storing them; its section 3.3 gives the head_dim contract (a multiple of 8,
+ * not too small).  The same
  * overview page's section 3.2 names packed variable-length batches.
  *
  * Conventions shared by every entry point
@@ -89,7 +90,7 @@ extern "C" {
 enum fa_status {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, bad scale   */
-    FA_ERR_UNSUPPORTED = 2, /* head_dim not 64/128, or dtype not fp16/bf16        */
+    FA_ERR_UNSUPPORTED = 2, /* head_dim not a multiple of 8 in [8, 128], or dtype  */
     FA_ERR_ARCH = 3,        /* no HIP device, or the current device is not gfx950 */
     FA_ERR_WORKSPACE = 4,   /* workspace smaller than the *_workspace_size() call */
     FA_ERR_LAUNCH = 5       /* a kernel launch was rejected by the runtime        */
@@ -106,7 +107,9 @@ enum fa_dtype { FA_DTYPE_F16 = 0, FA_DTYPE_BF16 = 1 };
  *   lse            out: float32, see layout above
  *   cu_seqlens_q/k in : both NULL (fixed length) or both device int32[batch+1]
  *   batch >= 0, heads >= 1, kv_heads >= 1 with heads % kv_heads == 0,
- *   seqlen_q >= 0, seqlen_k >= 0, head_dim in {64, 128},
+ *   seqlen_q >= 0, seqlen_k >= 0, head_dim a multiple of 8 from 8 to 128
+ *   (run in tiles 64 or 128 wide; a head_dim below the tile width costs the
+ *   tile width's arithmetic),
  *   causal in {0, 1}, window_left >= -1, window_right >= -1 (-1 = unbounded),
  *   softmax_scale finite and >= 0 (callers wanting the default pass
  *   1/sqrt(head_dim)), dtype one of fa_dtype.

@@ -89,7 +89,8 @@ BAD_FWD = [
     (dict(scale=-0.5), INVALID), (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
     (dict(cu_q=FAKE[10]), INVALID),                      # only one of the pair
     (dict(drop=-0.1), INVALID), (dict(drop=1.0), INVALID), (dict(drop=float("nan")), INVALID),
-    (dict(head_dim=96), UNSUPPORTED), (dict(head_dim=256), UNSUPPORTED), (dict(head_dim=0), UNSUPPORTED),
+    (dict(head_dim=100), UNSUPPORTED), (dict(head_dim=256), UNSUPPORTED), (dict(head_dim=0), UNSUPPORTED),
+    (dict(head_dim=136), UNSUPPORTED), (dict(head_dim=4), UNSUPPORTED), (dict(head_dim=-8), UNSUPPORTED),
     (dict(dtype=2), UNSUPPORTED), (dict(dtype=-1), UNSUPPORTED),
 ]
 
@@ -103,7 +104,7 @@ BAD_BWD = [
     (dict(do=None), INVALID), (dict(dq=None), INVALID), (dict(dk=None), INVALID),
     (dict(dv=None), INVALID), (dict(ws=None), INVALID),
     (dict(dv=ctypes.c_void_p(0x10004)), INVALID),
-    (dict(heads=3, kv_heads=2), INVALID), (dict(head_dim=32), UNSUPPORTED),
+    (dict(heads=3, kv_heads=2), INVALID), (dict(head_dim=36), UNSUPPORTED),
     (dict(wsb=2 * 4 * 4 * 128 - 4), WORKSPACE), (dict(wsb=0), WORKSPACE),
     (dict(drop=1.5), INVALID), (dict(drop=float("inf")), INVALID),
 ]
@@ -133,7 +134,8 @@ def test_workspace_size(L):
     assert f(2, 8, 1000, 128, 1) == 2 * (2 * 8 * 1000 * 4)
     assert f(1, 4, 128, 64, 0) == 2 * (4 * 128 * 4)
     assert f(0, 4, 128, 64, 0) == 4  # never zero for valid sizes
-    assert f(1, 4, 128, 96, 0) == 0 and f(1, 0, 128, 64, 0) == 0 and f(1, 4, 128, 64, 7) == 0
+    assert f(1, 4, 128, 96, 0) == 2 * (4 * 128 * 4) and f(1, 4, 128, 8, 1) == 2 * (4 * 128 * 4)
+    assert f(1, 4, 128, 100, 0) == 0 and f(1, 0, 128, 64, 0) == 0 and f(1, 4, 128, 64, 7) == 0
 
 
 @no_gpu
@@ -185,7 +187,7 @@ BAD_DEC = [
     (dict(kc=ctypes.c_void_p(0x10008)), INVALID),
     (dict(heads=6, kv_heads=4), INVALID), (dict(seqlen_q=-1), INVALID), (dict(causal=3), INVALID),
     (dict(scale=float("nan")), INVALID), (dict(left=-7), INVALID),
-    (dict(head_dim=80), UNSUPPORTED), (dict(dtype=5), UNSUPPORTED),
+    (dict(head_dim=84), UNSUPPORTED), (dict(head_dim=144), UNSUPPORTED), (dict(dtype=5), UNSUPPORTED),
     (dict(batch=1 << 16, seqlen_k=1 << 20), INVALID),      # 2^16 x 2^15 steps: beyond 32 bits
     (dict(batch=1 << 20, heads=2048, kv_heads=2048), INVALID),  # 2^31 output rows
     (dict(wsb=16), WORKSPACE),
@@ -212,15 +214,17 @@ def test_kvcache_split_plan(L):
     assert splits(2, 16, 2, 8, 4096, 128, 3) == 3 * 2 * 2 * 2  # 64 rows per kv head: 2 row blocks
     assert splits(2, 8, 2, 1, 4096, 128, 5000) == 2 * 2 * 128  # one step per wave at most
     assert splits(64, 8, 8, 1, 1 << 20, 128, 5000) == 65536
-    assert splits(1, 3, 2, 1, 64, 128, 0) == 0 and splits(1, 4, 2, 1, 64, 96, 0) == 0  # invalid
-    # workspace: (groups + sequences x row blocks) x kv_heads slots of 32 rows x (head_dim + 1)
-    # floats, then batch + 1 int64
+    assert splits(1, 3, 2, 1, 64, 128, 0) == 0 and splits(1, 4, 2, 1, 64, 100, 0) == 0  # invalid
+    # workspace: (groups + sequences x row blocks) x kv_heads slots of 32 rows x (tile width + 1)
+    # floats, then batch + 1 int64; the tile width is 64 or 128, the smallest holding head_dim
     for b, h, hk, nq, nk, d, ns in [(8, 32, 8, 1, 32768, 128, 0), (2, 16, 2, 8, 1000, 64, 3),
-                                    (1, 4, 1, 16, 33, 128, 0), (3, 4, 2, 2, 64, 64, 7)]:
+                                    (1, 4, 1, 16, 33, 128, 0), (3, 4, 2, 2, 64, 64, 7),
+                                    (2, 8, 2, 1, 500, 96, 0), (2, 8, 2, 1, 500, 40, 2)]:
         w = splits(b, h, hk, nq, nk, d, ns)
         seg = b * hk * ((h // hk * nq + 31) // 32)
-        assert size(b, h, hk, nq, nk, d, ns) == (w + seg) * 32 * (d + 1) * 4 + (b + 1) * 8
-    assert size(1, 4, 2, 1, 100, 96, 0) == 0 and size(1, 4, 3, 1, 100, 64, 0) == 0
+        tw = 64 if d <= 64 else 128
+        assert size(b, h, hk, nq, nk, d, ns) == (w + seg) * 32 * (tw + 1) * 4 + (b + 1) * 8
+    assert size(1, 4, 2, 1, 100, 100, 0) == 0 and size(1, 4, 3, 1, 100, 64, 0) == 0
 
 
 @no_gpu

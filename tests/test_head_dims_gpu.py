@@ -1,0 +1,122 @@
+"""Head dimensions other than the two tile widths: any multiple of 8 up to
+128 (the contract on the install guide page, yfxerp.com/news/195771, section
+3.3: a multiple of 8, not too small), run in tiles 64 or 128 wide.  Forward,
+backward, decode and dropout against the fp64 oracle, element by element,
+with the same tolerances as the tile widths themselves (O max-abs 4e-3 fp16 /
+2e-2 bf16, LSE 1e-3, dQ/dK/dV relative L2 2e-2); guard bands check that no
+column past head_dim is written.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = {"fp16": 4e-3, "bf16": 2e-2}
+LSE_TOL = 1e-3
+GRAD_TOL = 2e-2
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def fa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_tiled_attention_10_amd as m
+    m.lib()
+    return m
+
+
+def rel_l2(a, b):
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
+
+
+CASES = [
+    (8, "bf16", dict(batch=2, heads=2, kv_heads=2, seqlen=200, causal=True)),
+    (32, "fp16", dict(batch=2, heads=4, kv_heads=2, seqlen=300, causal=True)),
+    (40, "bf16", dict(batch=1, heads=3, kv_heads=1, seqlen=257, causal=False)),
+    (72, "fp16", dict(batch=1, heads=2, kv_heads=2, seqlen=333, causal=True, window=(50, 0))),
+    (96, "bf16", dict(batch=2, heads=4, kv_heads=4, seqlen=530, causal=True)),
+    (120, "fp16", dict(batch=1, heads=4, kv_heads=2, seqlen=150, seqlen_k=290, causal=True)),
+]
+
+
+@pytest.mark.parametrize("d,dtype,kw", CASES, ids=[f"d{c[0]}_{c[1]}" for c in CASES])
+def test_forward_backward(fa, oracle_mod, d, dtype, kw):
+    say(f"[head dim] d={d} {dtype} {kw}")
+    p = synth.make_problem(dtype=dtype, head_dim=d, seed=21, **kw)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (t.to(dev) for t in (p.q, p.k, p.v, p.do))
+    args = dict(causal=p.causal, window_size=(p.window_left, p.window_right), softmax_scale=p.scale)
+    # outputs inside guard bands: nothing past the tensor may change
+    pad = 1024
+    def padded(like):
+        buf = torch.full((like.numel() + 2 * pad,), 5.0, dtype=like.dtype, device=dev)
+        return buf, buf[pad:pad + like.numel()].view(like.shape)
+    ob, o = padded(q)
+    o, lse = fa.forward(q, k, v, out=o, **args)
+    dqb, dq = padded(q)
+    dkb, dk = padded(k)
+    dvb, dv = padded(v)
+    fa.backward(do, q, k, v, o, lse, dq=dq, dk=dk, dv=dv, **args)
+    torch.cuda.synchronize()
+    for buf in (ob, dqb, dkb, dvb):
+        assert torch.all(buf[:pad] == 5.0) and torch.all(buf[-pad:] == 5.0)
+    g = lambda t: t.float().cpu().double().numpy()
+    rdq, rdk, rdv, ro, rlse = oracle_mod.attention_bwd(p.q, p.k, p.v, p.do, scale=p.scale, causal=p.causal,
+                                                       window=(p.window_left, p.window_right))
+    eo = float(np.abs(g(o) - ro).max())
+    fin = np.isfinite(rlse)
+    el = float(np.abs(g(lse)[fin] - rlse[fin]).max())
+    errs = [rel_l2(g(dq), rdq), rel_l2(g(dk), rdk), rel_l2(g(dv), rdv)]
+    say(f"  O {eo:.2e} LSE {el:.2e} dq/dk/dv " + " ".join(f"{e:.2e}" for e in errs))
+    assert eo <= O_TOL[dtype] and el <= LSE_TOL and max(errs) <= GRAD_TOL
+
+
+@pytest.mark.parametrize("d", [24, 96])
+def test_dropout_with_odd_head_dim(fa, oracle_mod, d):
+    p = synth.make_problem(dtype="bf16", batch=1, heads=4, kv_heads=2, seqlen=260, head_dim=d, causal=True,
+                           seed=22)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (t.to(dev) for t in (p.q, p.k, p.v, p.do))
+    args = dict(causal=True, softmax_scale=p.scale, dropout_p=0.3, dropout_seed=4242)
+    o, lse = fa.forward(q, k, v, **args)
+    dq, dk, dv = fa.backward(do, q, k, v, o, lse, **args)
+    torch.cuda.synchronize()
+    g = lambda t: t.float().cpu().double().numpy()
+    rdq, rdk, rdv, ro, _ = oracle_mod.attention_bwd(p.q, p.k, p.v, p.do, scale=p.scale, causal=True,
+                                                    dropout_p=0.3, seed=4242)
+    eo = float(np.abs(g(o) - ro).max())
+    errs = [rel_l2(g(dq), rdq), rel_l2(g(dk), rdk), rel_l2(g(dv), rdv)]
+    say(f"[head dim dropout] d={d} O {eo:.2e} dq/dk/dv " + " ".join(f"{e:.2e}" for e in errs))
+    assert eo <= O_TOL["bf16"] and max(errs) <= GRAD_TOL
+
+
+@pytest.mark.parametrize("d,dtype", [(32, "fp16"), (80, "bf16"), (112, "bf16")])
+def test_decode(fa, oracle_mod, d, dtype):
+    p = synth.make_decode(dtype=dtype, batch=3, heads=8, kv_heads=2, seqlen_q=2, capacity=700, head_dim=d,
+                          causal=True, cache_lens=[1, 350, 700], seed=23)
+    dev = torch.device("cuda:0")
+    o, lse = fa.forward_kvcache(p.q.to(dev), p.k_cache.to(dev), p.v_cache.to(dev), p.cache_seqlens().to(dev),
+                                causal=True, softmax_scale=p.scale)
+    torch.cuda.synchronize()
+    go, gl = o.float().cpu().double().numpy(), lse.cpu().double().numpy()
+    eo = el = 0.0
+    for b in range(p.batch):
+        n = p.cache_lens[b]
+        ro, rl = oracle_mod.attention_fwd(p.q[b:b + 1], p.k_cache[b:b + 1, :n], p.v_cache[b:b + 1, :n],
+                                          scale=p.scale, causal=True)
+        eo = max(eo, float(np.abs(go[b] - ro[0]).max()))
+        fin = np.isfinite(rl[0])
+        if fin.any():
+            el = max(el, float(np.abs(gl[b][fin] - rl[0][fin]).max()))
+    say(f"[head dim decode] d={d} {dtype} O {eo:.2e} LSE {el:.2e}")
+    assert eo <= O_TOL[dtype] and el <= LSE_TOL
