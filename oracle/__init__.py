@@ -79,35 +79,41 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
-def _geometry(q, k, heads_hint, cu):
+def _geometry(q, k, heads_hint, cu, cu_k=None):
     if cu is None:
         b, nq, h, d = q.shape
         _, nk, hk, _ = k.shape
         return b, h, hk, nq, nk, d
+    cu_k = cu if cu_k is None else cu_k
+    if len(cu_k) != len(cu):
+        raise ValueError("cu_seqlens and cu_seqlens_k must describe the same number of sequences")
     _, h, d = q.shape
     _, hk, _ = k.shape
-    lens = np.diff(cu)
-    m = int(lens.max()) if len(lens) else 0
-    return len(cu) - 1, h, hk, m, m, d
+    lq, lk = np.diff(cu), np.diff(cu_k)
+    mq = int(lq.max()) if len(lq) else 0
+    mk = int(lk.max()) if len(lk) else 0
+    return len(cu) - 1, h, hk, mq, mk, d
 
 
 def attention_fwd(q, k, v, *, scale, causal=False, window=(-1, -1),
                   cu_seqlens=None, rows=None, heads=None, threads=0,
-                  dropout_p=0.0, seed=0):
+                  dropout_p=0.0, seed=0, cu_seqlens_k=None):
     """O and LSE of exact attention.  q: (B, Nq, H, d) or packed (T, H, d);
     k, v: (B, Nk, Hkv, d) or (T, Hkv, d).  ``cu_seqlens`` (B+1 prefix sums)
-    marks a packed batch, used for both queries and keys.  ``rows`` /
+    marks a packed batch, used for both queries and keys unless
+    ``cu_seqlens_k`` gives the keys' own.  ``rows`` /
     ``heads`` restrict the computed query rows (positions within each
     sequence) / query heads; the rest stays NaN.  ``dropout_p`` / ``seed``:
     dropout with the Philox4x32-10 keep decisions (see the C++ header)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     cu = _i32(cu_seqlens)
-    B, H, HK, NQ, NK, D = _geometry(q, k, None, cu)
+    cuk = cu if cu_seqlens_k is None or cu is None else _i32(cu_seqlens_k)
+    B, H, HK, NQ, NK, D = _geometry(q, k, None, cu, cuk)
     o = np.full(q.shape, np.nan)
     lse = np.full((B, H, NQ) if cu is None else (H, q.shape[0]), np.nan)
     rs, hs = _i32(rows), _i32(heads)
     rc = _load().oracle_attention_fwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu), _ptr(cu),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu), _ptr(cuk),
         B, H, HK, NQ, NK, D, int(bool(causal)), int(window[0]), int(window[1]),
         float(scale), _ptr(rs), 0 if rs is None else len(rs),
         _ptr(hs), 0 if hs is None else len(hs), int(threads),
@@ -119,14 +125,16 @@ def attention_fwd(q, k, v, *, scale, causal=False, window=(-1, -1),
 
 def attention_bwd(q, k, v, dout, *, scale, causal=False, window=(-1, -1),
                   cu_seqlens=None, q_rows=None, k_rows=None, kv_heads=None,
-                  threads=0, dropout_p=0.0, seed=0):
+                  threads=0, dropout_p=0.0, seed=0, cu_seqlens_k=None):
     """dQ, dK, dV (and the oracle's own O, LSE on the rows it needed) of exact
-    attention for upstream gradient ``dout``.  ``q_rows`` restricts dQ rows,
+    attention for upstream gradient ``dout``.  ``cu_seqlens_k`` as in
+    attention_fwd.  ``q_rows`` restricts dQ rows,
     ``k_rows`` the dK/dV rows, ``kv_heads`` the kv heads (with all query
     heads of their groups); unselected entries stay NaN."""
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
     cu = _i32(cu_seqlens)
-    B, H, HK, NQ, NK, D = _geometry(q, k, None, cu)
+    cuk = cu if cu_seqlens_k is None or cu is None else _i32(cu_seqlens_k)
+    B, H, HK, NQ, NK, D = _geometry(q, k, None, cu, cuk)
     dq = np.full(q.shape, np.nan)
     dk = np.full(k.shape, np.nan)
     dv = np.full(k.shape, np.nan)
@@ -135,7 +143,7 @@ def attention_bwd(q, k, v, dout, *, scale, causal=False, window=(-1, -1),
     qr, kr, kh = _i32(q_rows), _i32(k_rows), _i32(kv_heads)
     rc = _load().oracle_attention_bwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
-        _ptr(o), _ptr(lse), _ptr(cu), _ptr(cu),
+        _ptr(o), _ptr(lse), _ptr(cu), _ptr(cuk),
         B, H, HK, NQ, NK, D, int(bool(causal)), int(window[0]), int(window[1]),
         float(scale), _ptr(qr), 0 if qr is None else len(qr),
         _ptr(kr), 0 if kr is None else len(kr),

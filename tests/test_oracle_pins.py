@@ -313,6 +313,30 @@ def test_packed_batch_equals_independent_calls(oracle_mod):
         assert np.allclose(lse[:, s], r[4][0], atol=1e-14)
 
 
+def test_packed_batch_with_own_key_lengths_equals_independent_calls(oracle_mod):
+    """Packed queries and keys with lengths of their own (cu_seqlens_k):
+    sequence b is the fixed-layout call on its Lq queries and Lk keys,
+    bottom-right aligned, empty sequences included."""
+    lq, lk = [5, 0, 9, 3, 1], [11, 4, 9, 2, 0]
+    cq = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    ck = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    q, do = rnd((cq[-1], 4, 8), 74), rnd((cq[-1], 4, 8), 77)
+    k, v = rnd((ck[-1], 2, 8), 75), rnd((ck[-1], 2, 8), 76)
+    kw = dict(scale=0.45, causal=True, window=(4, 0))
+    dq, dk, dv, o, lse = oracle_mod.attention_bwd(q, k, v, do, cu_seqlens=cq, cu_seqlens_k=ck, **kw)
+    for b in range(len(lq)):
+        sq, sk = slice(cq[b], cq[b + 1]), slice(ck[b], ck[b + 1])
+        if lq[b] == 0:
+            assert np.all(dk[sk] == 0) and np.all(dv[sk] == 0)
+            continue
+        r = oracle_mod.attention_bwd(q[None, sq], k[None, sk], v[None, sk], do[None, sq], **kw)
+        o1, l1 = oracle_mod.attention_fwd(q[None, sq], k[None, sk], v[None, sk], **kw)
+        assert np.allclose(dq[sq], r[0][0], atol=1e-14)
+        assert np.allclose(dk[sk], r[1][0], atol=1e-14) and np.allclose(dv[sk], r[2][0], atol=1e-14)
+        assert np.allclose(o[sq], o1[0], atol=1e-14, equal_nan=True)
+        assert np.allclose(lse[:, sq], l1[0], atol=1e-14, equal_nan=True)
+
+
 def test_wide_window_equals_plain_causal(oracle_mod):
     q, k, v = rnd((1, 23, 2, 8), 80), rnd((1, 23, 2, 8), 81), rnd((1, 23, 2, 8), 82)
     o1, l1 = oracle_mod.attention_fwd(q, k, v, scale=0.5, causal=True)
