@@ -52,13 +52,13 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     U64 = ctypes.c_uint64
-    L.fa_fwd.argtypes = [P] * 7 + [I] * 9 + [F, F, U64, I, P]
+    L.fa_fwd.argtypes = [P] * 9 + [I] * 9 + [F, F, U64, I, P]
     L.fa_fwd.restype = I
     L.fa_bwd_workspace_size.argtypes = [I] * 5
     L.fa_bwd_workspace_size.restype = S
-    L.fa_bwd.argtypes = [P] * 10 + [S] + [P] * 2 + [I] * 9 + [F, F, U64, I, P]
+    L.fa_bwd.argtypes = [P] * 10 + [S] + [P] * 4 + [I] * 9 + [F, F, U64, I, P]
     L.fa_bwd.restype = I
-    L.fa_bwd_stage.argtypes = [I] + [P] * 10 + [S] + [P] * 2 + [I] * 9 + [F, F, U64, I, P]
+    L.fa_bwd_stage.argtypes = [I] + [P] * 10 + [S] + [P] * 4 + [I] * 9 + [F, F, U64, I, P]
     L.fa_bwd_stage.restype = I
     L.fa_fwd_kvcache_workspace_size.argtypes = [I] * 7
     L.fa_fwd_kvcache_workspace_size.restype = S
@@ -151,9 +151,17 @@ def new_dropout_seed() -> int:
     return int(torch.randint(0, 2**62, (1,), dtype=torch.int64).item())
 
 
+def _check_used(used, name, batch, device):
+    if used is None:
+        return
+    _check(used, name, torch.int32, device)
+    if used.shape != (batch,):
+        raise ValueError(f"{name} must hold one int32 per sequence")
+
+
 def forward(q, k, v, *, causal=False, window_size=(-1, -1), softmax_scale=None,
             cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
-            out=None, lse=None, dropout_p=0.0, dropout_seed=0):
+            out=None, lse=None, dropout_p=0.0, dropout_seed=0, seqused_q=None, seqused_k=None):
     """O and LSE of exact attention (see include/fa.h for the definition,
     dropout included).  Returns (out, lse); lse is float32 (batch, heads,
     seqlen_q) or (heads, total_q) for packed batches."""
@@ -166,6 +174,8 @@ def forward(q, k, v, *, causal=False, window_size=(-1, -1), softmax_scale=None,
         _check(cu_seqlens_q, "cu_seqlens_q", torch.int32, q.device)
         _check(cu_seqlens_k, "cu_seqlens_k", torch.int32, q.device)
     g = _Geom(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    _check_used(seqused_q, "seqused_q", g.batch, q.device)
+    _check_used(seqused_k, "seqused_k", g.batch, q.device)
     if out is None:
         out = torch.empty_like(q)
     else:
@@ -175,7 +185,7 @@ def forward(q, k, v, *, causal=False, window_size=(-1, -1), softmax_scale=None,
     else:
         _check(lse, "lse", torch.float32, q.device)
     rc = L.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
-                  _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                  _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(seqused_q), _ptr(seqused_k),
                   g.batch, g.heads, g.kv_heads, g.seqlen_q, g.seqlen_k, g.d,
                   int(bool(causal)), int(window_size[0]), int(window_size[1]),
                   _default_scale(g.d, softmax_scale), float(dropout_p), _seed(dropout_seed),
@@ -193,7 +203,7 @@ def workspace_size(batch, heads, seqlen_q, head_dim, dtype) -> int:
 def backward(dout, q, k, v, out, lse, *, causal=False, window_size=(-1, -1),
              softmax_scale=None, cu_seqlens_q=None, cu_seqlens_k=None,
              max_seqlen_q=None, max_seqlen_k=None, dq=None, dk=None, dv=None,
-             workspace=None, dropout_p=0.0, dropout_seed=0):
+             workspace=None, dropout_p=0.0, dropout_seed=0, seqused_q=None, seqused_k=None):
     """dQ, dK, dV of exact attention for upstream gradient ``dout``, from the
     forward's ``out`` and ``lse`` (recomputing the scores)."""
     L = lib()
@@ -205,6 +215,8 @@ def backward(dout, q, k, v, out, lse, *, causal=False, window_size=(-1, -1),
         _check(cu_seqlens_q, "cu_seqlens_q", torch.int32, q.device)
         _check(cu_seqlens_k, "cu_seqlens_k", torch.int32, q.device)
     g = _Geom(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    _check_used(seqused_q, "seqused_q", g.batch, q.device)
+    _check_used(seqused_k, "seqused_k", g.batch, q.device)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
@@ -217,7 +229,7 @@ def backward(dout, q, k, v, out, lse, *, causal=False, window_size=(-1, -1),
         workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
     rc = L.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
                   _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                  _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                  _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(seqused_q), _ptr(seqused_k),
                   g.batch, g.heads, g.kv_heads, g.seqlen_q, g.seqlen_k, g.d,
                   int(bool(causal)), int(window_size[0]), int(window_size[1]),
                   _default_scale(g.d, softmax_scale), float(dropout_p), _seed(dropout_seed),
@@ -235,11 +247,13 @@ class Plan:
 
     def __init__(self, q, k, v, dout=None, *, causal=False, window_size=(-1, -1), softmax_scale=None,
                  cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, stream=None,
-                 dropout_p=0.0, dropout_seed=0):
+                 dropout_p=0.0, dropout_seed=0, seqused_q=None, seqused_k=None):
         L = lib()
         dt = q.dtype
         _check(q, "q"); _check(k, "k", dt, q.device); _check(v, "v", dt, q.device)
         g = _Geom(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+        _check_used(seqused_q, "seqused_q", g.batch, q.device)
+        _check_used(seqused_k, "seqused_k", g.batch, q.device)
         self.geom = g
         self.q, self.k, self.v, self.dout = q, k, v, dout
         self.out = torch.empty_like(q)
@@ -252,8 +266,9 @@ class Plan:
                   int(bool(causal)), int(window_size[0]), int(window_size[1]),
                   _default_scale(g.d, softmax_scale), float(dropout_p), _seed(dropout_seed),
                   _dtype_code(q), sp]
+        self._used = (seqused_q, seqused_k)
         self._fwd = [_ptr(q), _ptr(k), _ptr(v), _ptr(self.out), _ptr(self.lse),
-                     _ptr(cu_seqlens_q), _ptr(cu_seqlens_k)] + common
+                     _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(seqused_q), _ptr(seqused_k)] + common
         if dout is not None:
             _check(dout, "dout", dt, q.device)
             self.dq, self.dk, self.dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -261,7 +276,8 @@ class Plan:
             self.workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
             self._bwd = [_ptr(q), _ptr(k), _ptr(v), _ptr(self.out), _ptr(self.lse), _ptr(dout),
                          _ptr(self.dq), _ptr(self.dk), _ptr(self.dv), _ptr(self.workspace),
-                         self.workspace.numel(), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k)] + common
+                         self.workspace.numel(), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                         _ptr(seqused_q), _ptr(seqused_k)] + common
         self._L = L
 
     def fwd(self):
@@ -283,37 +299,39 @@ class Plan:
 class _FlashAttn(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, softmax_scale, causal, window_size, cu_q, cu_k, max_q, max_k,
-                dropout_p, dropout_seed):
+                dropout_p, dropout_seed, used_q, used_k):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
         out, lse = forward(q, k, v, causal=causal, window_size=window_size,
                            softmax_scale=softmax_scale, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k,
                            max_seqlen_q=max_q, max_seqlen_k=max_k,
-                           dropout_p=dropout_p, dropout_seed=dropout_seed)
-        ctx.save_for_backward(q, k, v, out, lse, cu_q, cu_k)
+                           dropout_p=dropout_p, dropout_seed=dropout_seed, seqused_q=used_q, seqused_k=used_k)
+        ctx.save_for_backward(q, k, v, out, lse, cu_q, cu_k, used_q, used_k)
         ctx.args = (softmax_scale, causal, window_size, max_q, max_k, dropout_p, dropout_seed)
         return out
 
     @staticmethod
     def backward(ctx, dout):
-        q, k, v, out, lse, cu_q, cu_k = ctx.saved_tensors
+        q, k, v, out, lse, cu_q, cu_k, used_q, used_k = ctx.saved_tensors
         softmax_scale, causal, window_size, max_q, max_k, dropout_p, dropout_seed = ctx.args
         dq, dk, dv = backward(dout.contiguous(), q, k, v, out, lse, causal=causal,
                               window_size=window_size, softmax_scale=softmax_scale,
                               cu_seqlens_q=cu_q, cu_seqlens_k=cu_k,
                               max_seqlen_q=max_q, max_seqlen_k=max_k,
-                              dropout_p=dropout_p, dropout_seed=dropout_seed)
-        return dq, dk, dv, None, None, None, None, None, None, None, None, None
+                              dropout_p=dropout_p, dropout_seed=dropout_seed, seqused_q=used_q, seqused_k=used_k)
+        return dq, dk, dv, None, None, None, None, None, None, None, None, None, None, None
 
 
 def flash_attn_func(q, k, v, dropout_p=0.0, softmax_scale=None, causal=False,
-                    window_size=(-1, -1), dropout_seed=None):
+                    window_size=(-1, -1), dropout_seed=None, seqused_q=None, seqused_k=None):
     """Autograd entry with the call shape the pages use.  With dropout_p > 0
     and no dropout_seed, a seed is drawn from torch's default generator; the
-    backward reuses the forward's seed."""
+    backward reuses the forward's seed.  seqused_q / seqused_k (int32 per
+    sequence) make a padded batch: only the first rows of each sequence
+    count, the rest of the output and gradients is zero."""
     if dropout_p > 0.0 and dropout_seed is None:
         dropout_seed = new_dropout_seed()
     return _FlashAttn.apply(q, k, v, softmax_scale, causal, tuple(window_size), None, None, None, None,
-                            float(dropout_p), 0 if dropout_seed is None else dropout_seed)
+                            float(dropout_p), 0 if dropout_seed is None else dropout_seed, seqused_q, seqused_k)
 
 
 def flash_attn_varlen_func(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
@@ -325,7 +343,7 @@ def flash_attn_varlen_func(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, ma
         dropout_seed = new_dropout_seed()
     return _FlashAttn.apply(q, k, v, softmax_scale, causal, tuple(window_size),
                             cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
-                            float(dropout_p), 0 if dropout_seed is None else dropout_seed)
+                            float(dropout_p), 0 if dropout_seed is None else dropout_seed, None, None)
 
 
 # ---------------------------------------------------------------------------

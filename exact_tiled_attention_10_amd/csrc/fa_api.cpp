@@ -73,6 +73,13 @@ float log2e_scaled(float s) {
     return c < 1.17549435e-38f ? 1.17549435e-38f : c;
 }
 
+// Padded-batch lengths: device int32[batch] arrays, only with the fixed
+// layout (not together with cu_seqlens).
+bool seqused_ok(const int32_t* used_q, const int32_t* used_k, const int32_t* cu_q) {
+    if ((used_q || used_k) && cu_q) return false;
+    return aligned(used_q, 4) && aligned(used_k, 4);
+}
+
 // Dropout threshold T (elements kept iff their 8-bit draw is below T) and
 // the scale of kept probabilities, 256 / T (0 when T = 0).  p must lie in
 // [0, 1).
@@ -91,6 +98,7 @@ extern "C" {
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+           const int32_t* seqused_q, const int32_t* seqused_k,
            int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
            int head_dim, int causal, int window_left, int window_right,
            float softmax_scale, float dropout_p, uint64_t dropout_seed, int dtype, void* stream) {
@@ -100,6 +108,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
     uint32_t drop_t;
     float drop_scale;
     if (!dropout_params(dropout_p, drop_t, drop_scale)) return FA_ERR_INVALID_ARG;
+    if (!seqused_ok(seqused_q, seqused_k, cu_seqlens_q)) return FA_ERR_INVALID_ARG;
     const bool has_q = (long long)batch * seqlen_q > 0, has_k = (long long)batch * seqlen_k > 0;
     if ((has_q && (!q || !o || !lse)) || (has_k && (!k || !v))) return FA_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
@@ -109,6 +118,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
     fa::FwdArgs a;
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
     a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
+    a.used_q = seqused_q; a.used_k = seqused_k;
     a.batch = batch; a.heads = heads; a.kv_heads = kv_heads;
     a.seqlen_q = seqlen_q; a.seqlen_k = seqlen_k; a.head_dim = head_dim;
     a.causal = causal; a.left = window_left; a.right = window_right;
@@ -116,7 +126,11 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
     a.bf16 = dtype == FA_DTYPE_BF16;
     a.drop_t = drop_t; a.drop_scale = drop_scale;
     a.seed_lo = (uint32_t)dropout_seed; a.seed_hi = (uint32_t)(dropout_seed >> 32);
-    return fa::launch_fwd(a, (hipStream_t)stream) == 0 ? FA_OK : FA_ERR_LAUNCH;
+    if (fa::launch_fwd(a, (hipStream_t)stream) != 0) return FA_ERR_LAUNCH;
+    if (seqused_q && fa::launch_pad_fill(o, lse, seqused_q, batch, seqlen_q, heads, head_dim,
+                                         (hipStream_t)stream) != 0)
+        return FA_ERR_LAUNCH;
+    return FA_OK;
 }
 
 size_t fa_bwd_workspace_size(int batch, int heads, int seqlen_q, int head_dim, int dtype) {
@@ -137,6 +151,7 @@ int bwd_common(int stage_lo, int stage_hi,
                const float* lse, const void* dout, void* dq, void* dk, void* dv,
                void* workspace, size_t workspace_bytes,
                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+               const int32_t* seqused_q, const int32_t* seqused_k,
                int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
                int head_dim, int causal, int window_left, int window_right,
                float softmax_scale, float dropout_p, uint64_t dropout_seed, int dtype, void* stream) {
@@ -146,6 +161,7 @@ int bwd_common(int stage_lo, int stage_hi,
     uint32_t drop_t;
     float drop_scale;
     if (!dropout_params(dropout_p, drop_t, drop_scale)) return FA_ERR_INVALID_ARG;
+    if (!seqused_ok(seqused_q, seqused_k, cu_seqlens_q)) return FA_ERR_INVALID_ARG;
     const bool has_q = (long long)batch * seqlen_q > 0, has_k = (long long)batch * seqlen_k > 0;
     if ((has_q && (!q || !o || !lse || !dout || !dq)) || (has_k && (!k || !v || !dk || !dv)) || !workspace)
         return FA_ERR_INVALID_ARG;
@@ -162,6 +178,7 @@ int bwd_common(int stage_lo, int stage_hi,
     a.dq = dq; a.dk = dk; a.dv = dv; a.dsum = (float*)workspace;
     a.lse2 = a.dsum + (size_t)batch * (size_t)heads * (size_t)seqlen_q;
     a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
+    a.used_q = seqused_q; a.used_k = seqused_k;
     a.batch = batch; a.heads = heads; a.kv_heads = kv_heads;
     a.seqlen_q = seqlen_q; a.seqlen_k = seqlen_k; a.head_dim = head_dim;
     a.causal = causal; a.left = window_left; a.right = window_right;
@@ -169,8 +186,18 @@ int bwd_common(int stage_lo, int stage_hi,
     a.bf16 = dtype == FA_DTYPE_BF16;
     a.drop_t = drop_t; a.drop_scale = drop_scale;
     a.seed_lo = (uint32_t)dropout_seed; a.seed_hi = (uint32_t)(dropout_seed >> 32);
-    for (int st = stage_lo; st <= stage_hi; ++st)
-        if (fa::launch_bwd(a, st, (hipStream_t)stream) != 0) return FA_ERR_LAUNCH;
+    hipStream_t st_ = (hipStream_t)stream;
+    for (int st = stage_lo; st <= stage_hi; ++st) {
+        if (fa::launch_bwd(a, st, st_) != 0) return FA_ERR_LAUNCH;
+        // padded rows of the stage's outputs
+        if (st == 1 && seqused_k &&
+            (fa::launch_pad_fill(dk, nullptr, seqused_k, batch, seqlen_k, kv_heads, head_dim, st_) != 0 ||
+             fa::launch_pad_fill(dv, nullptr, seqused_k, batch, seqlen_k, kv_heads, head_dim, st_) != 0))
+            return FA_ERR_LAUNCH;
+        if (st == 2 && seqused_q &&
+            fa::launch_pad_fill(dq, nullptr, seqused_q, batch, seqlen_q, heads, head_dim, st_) != 0)
+            return FA_ERR_LAUNCH;
+    }
     return FA_OK;
 }
 
@@ -182,11 +209,12 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const float* lse, const void* dout, void* dq, void* dk, void* dv,
            void* workspace, size_t workspace_bytes,
            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+           const int32_t* seqused_q, const int32_t* seqused_k,
            int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
            int head_dim, int causal, int window_left, int window_right,
            float softmax_scale, float dropout_p, uint64_t dropout_seed, int dtype, void* stream) {
     return bwd_common(0, 2, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes,
-                      cu_seqlens_q, cu_seqlens_k, batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim,
+                      cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k, batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim,
                       causal, window_left, window_right, softmax_scale, dropout_p, dropout_seed, dtype,
                       stream);
 }
@@ -195,12 +223,13 @@ int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const v
                  const float* lse, const void* dout, void* dq, void* dk, void* dv,
                  void* workspace, size_t workspace_bytes,
                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                 const int32_t* seqused_q, const int32_t* seqused_k,
                  int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
                  int head_dim, int causal, int window_left, int window_right,
                  float softmax_scale, float dropout_p, uint64_t dropout_seed, int dtype, void* stream) {
     if (stage < 0 || stage > 2) return FA_ERR_INVALID_ARG;
     return bwd_common(stage, stage, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes,
-                      cu_seqlens_q, cu_seqlens_k, batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim,
+                      cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k, batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim,
                       causal, window_left, window_right, softmax_scale, dropout_p, dropout_seed, dtype,
                       stream);
 }

@@ -151,7 +151,7 @@ void bwd_dq_kernel(BwdArgs a) {
     const int b = blockIdx.x / a.heads, h = blockIdx.x % a.heads;
     const int ntiles = gridDim.y;
     const int qt = a.causal ? (ntiles - 1 - (int)blockIdx.y) : (int)blockIdx.y;
-    const Seq s = seq_of(b, a.cu_q, a.cu_k, a.seqlen_q, a.seqlen_k);
+    const Seq s = seq_of(b, a.cu_q, a.cu_k, a.used_q, a.used_k, a.seqlen_q, a.seqlen_k);
     const int i0 = qt * BM;
     if (i0 >= s.len_q) return;
     const Mask mk{a.causal, a.left, a.right};
@@ -341,7 +341,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const int r32 = lane & 31, half = lane >> 5;
     const int g = a.heads / a.kv_heads;
     const int b = blockIdx.x / a.kv_heads, hk = blockIdx.x % a.kv_heads;
-    const Seq s = seq_of(b, a.cu_q, a.cu_k, a.seqlen_q, a.seqlen_k);
+    const Seq s = seq_of(b, a.cu_q, a.cu_k, a.used_q, a.used_k, a.seqlen_q, a.seqlen_k);
     const int j0 = blockIdx.y * kKvBN;
     if (j0 >= s.len_k) return;
     const Mask mk{a.causal, a.left, a.right};

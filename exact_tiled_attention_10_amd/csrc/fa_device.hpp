@@ -256,22 +256,25 @@ __device__ __forceinline__ bool keep_byte(uint32_t w, int e, uint32_t thresh) {
     return ((w >> (8 * e)) & 0xFFu) < thresh;
 }
 
-// Geometry of one (batch, head) problem slice, resolved from cu_seqlens.
+// Geometry of one (batch, head) problem slice: packed (cu_seqlens), fixed
+// length, or fixed layout with fewer valid rows (used_q / used_k: padded
+// batches, lengths clamped to the layout).
 struct Seq {
-    int64_t q_start, k_start;  // first packed row of the sequence
-    int len_q, len_k;
+    int64_t q_start, k_start;  // first row of the sequence in the tensor
+    int len_q, len_k;          // valid rows
     int off;                   // len_k - len_q: bottom-right alignment
 };
 
-__device__ __forceinline__ Seq seq_of(int b, const int32_t* cu_q, const int32_t* cu_k,
-                                      int seqlen_q, int seqlen_k) {
+__device__ __forceinline__ Seq seq_of(int b, const int32_t* cu_q, const int32_t* cu_k, const int32_t* used_q,
+                                      const int32_t* used_k, int seqlen_q, int seqlen_k) {
     Seq s;
     if (cu_q) {
         const int q0 = cu_q[b], q1 = cu_q[b + 1], k0 = cu_k[b], k1 = cu_k[b + 1];
         s.q_start = q0; s.k_start = k0; s.len_q = q1 - q0; s.len_k = k1 - k0;
     } else {
         s.q_start = (int64_t)b * seqlen_q; s.k_start = (int64_t)b * seqlen_k;
-        s.len_q = seqlen_q; s.len_k = seqlen_k;
+        s.len_q = used_q ? min(max(used_q[b], 0), seqlen_q) : seqlen_q;
+        s.len_k = used_k ? min(max(used_k[b], 0), seqlen_k) : seqlen_k;
     }
     s.off = s.len_k - s.len_q;
     return s;

@@ -90,7 +90,7 @@ void fwd_kernel(FwdArgs a) {
     const int b = hb / a.heads, h = hb % a.heads;
     const int ntiles = gridDim.y;
     const int qt = a.causal ? (ntiles - 1 - (int)blockIdx.y) : (int)blockIdx.y;
-    const Seq s = seq_of(b, a.cu_q, a.cu_k, a.seqlen_q, a.seqlen_k);
+    const Seq s = seq_of(b, a.cu_q, a.cu_k, a.used_q, a.used_k, a.seqlen_q, a.seqlen_k);
     const int i0 = qt * BM;
     if (i0 >= s.len_q) return;
     const Mask mk{a.causal, a.left, a.right};

@@ -15,6 +15,8 @@ struct FwdArgs {
     float* lse;
     const int32_t* cu_q;
     const int32_t* cu_k;
+    const int32_t* used_q;  // padded batches: valid rows per sequence, or null
+    const int32_t* used_k;
     int batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim;
     int causal, left, right;
     float scale;       // softmax scale
@@ -41,6 +43,8 @@ struct BwdArgs {
     float* lse2;  // workspace: LSE_i * log2(e), laid out like lse
     const int32_t* cu_q;
     const int32_t* cu_k;
+    const int32_t* used_q;  // as in FwdArgs
+    const int32_t* used_k;
     int batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim;
     int causal, left, right;
     float scale;
@@ -78,5 +82,11 @@ struct DecArgs {
 int launch_fwd(const FwdArgs& a, hipStream_t stream);
 int launch_bwd(const BwdArgs& a, int stage, hipStream_t stream);
 int launch_decode(const DecArgs& a, hipStream_t stream);
+
+// Padded batches: for each sequence b and row r with used[b] <= r < seqlen of
+// a [batch, seqlen, heads, dh] 16-bit tensor, zero the row of every head and,
+// when lse is given ([batch, heads, seqlen] float32), set its LSE to -inf.
+int launch_pad_fill(void* t, float* lse, const int32_t* used, int batch, int seqlen, int heads, int dh,
+                    hipStream_t stream);
 
 }  // namespace fa

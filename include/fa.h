@@ -30,6 +30,14 @@
  * and seqlen_q / seqlen_k give the longest sequence of each.  cu_seqlens_*
  * are device arrays of batch+1 non-decreasing int32 prefix sums starting at
  * 0 (not checked on the device).
+ * Padded batches (fixed layout, seqused_q and/or seqused_k non-null; the
+ * padded-batch test the overview page names in section 3.2): sequence b uses
+ * only its first seqused_q[b] query rows and seqused_k[b] key rows (device
+ * int32[batch], clamped to 0 .. seqlen) and is computed exactly as that
+ * shorter sequence, bottom-right alignment included.  The rows past them are
+ * written as a sequence without them defines them: O = 0 and LSE = -inf
+ * (fa_fwd), dQ = 0, dK = dV = 0 (fa_bwd).  Not combined with cu_seqlens
+ * (FA_ERR_INVALID_ARG).
  *
  * Visible keys of query row i in a sequence of Lq queries and Lk keys, with
  * p = i + Lk - Lq (bottom-right alignment; p = i when Lq = Lk):
@@ -106,6 +114,7 @@ enum fa_dtype { FA_DTYPE_F16 = 0, FA_DTYPE_BF16 = 1 };
  *   o              out: like q
  *   lse            out: float32, see layout above
  *   cu_seqlens_q/k in : both NULL (fixed length) or both device int32[batch+1]
+ *   seqused_q/k    in : NULL, or device int32[batch] (padded batches, above)
  *   batch >= 0, heads >= 1, kv_heads >= 1 with heads % kv_heads == 0,
  *   seqlen_q >= 0, seqlen_k >= 0, head_dim a multiple of 8 from 8 to 128
  *   (run in tiles 64 or 128 wide; a head_dim below the tile width costs the
@@ -118,6 +127,7 @@ enum fa_dtype { FA_DTYPE_F16 = 0, FA_DTYPE_BF16 = 1 };
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+           const int32_t* seqused_q, const int32_t* seqused_k,
            int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
            int head_dim, int causal, int window_left, int window_right,
            float softmax_scale, float dropout_p, uint64_t dropout_seed, int dtype, void* stream);
@@ -148,6 +158,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const float* lse, const void* dout, void* dq, void* dk, void* dv,
            void* workspace, size_t workspace_bytes,
            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+           const int32_t* seqused_q, const int32_t* seqused_k,
            int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
            int head_dim, int causal, int window_left, int window_right,
            float softmax_scale, float dropout_p, uint64_t dropout_seed, int dtype, void* stream);
@@ -164,6 +175,7 @@ int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const v
                  const float* lse, const void* dout, void* dq, void* dk, void* dv,
                  void* workspace, size_t workspace_bytes,
                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                 const int32_t* seqused_q, const int32_t* seqused_k,
                  int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
                  int head_dim, int causal, int window_left, int window_right,
                  float softmax_scale, float dropout_p, uint64_t dropout_seed, int dtype, void* stream);

@@ -57,11 +57,11 @@ def test_strerror_and_version(L):
 
 def fwd(L, **over):
     args = dict(q=FAKE[0], k=FAKE[1], v=FAKE[2], o=FAKE[3], lse=FAKE[4], cu_q=None, cu_k=None,
-                batch=1, heads=4, kv_heads=2, seqlen_q=128, seqlen_k=128, head_dim=128,
+                used_q=None, used_k=None, batch=1, heads=4, kv_heads=2, seqlen_q=128, seqlen_k=128, head_dim=128,
                 causal=1, left=-1, right=-1, scale=0.125, drop=0.0, seed=0, dtype=1, stream=None)
     args.update(over)
     return L.fa_fwd(args["q"], args["k"], args["v"], args["o"], args["lse"], args["cu_q"], args["cu_k"],
-                    args["batch"], args["heads"], args["kv_heads"], args["seqlen_q"], args["seqlen_k"],
+                    args["used_q"], args["used_k"], args["batch"], args["heads"], args["kv_heads"], args["seqlen_q"], args["seqlen_k"],
                     args["head_dim"], args["causal"], args["left"], args["right"], args["scale"],
                     args["drop"], args["seed"], args["dtype"], args["stream"])
 
@@ -69,12 +69,12 @@ def fwd(L, **over):
 def bwd(L, **over):
     args = dict(q=FAKE[0], k=FAKE[1], v=FAKE[2], o=FAKE[3], lse=FAKE[4], do=FAKE[5], dq=FAKE[6],
                 dk=FAKE[7], dv=FAKE[8], ws=FAKE[9], wsb=1 << 20, cu_q=None, cu_k=None,
-                batch=1, heads=4, kv_heads=2, seqlen_q=128, seqlen_k=128, head_dim=128,
+                used_q=None, used_k=None, batch=1, heads=4, kv_heads=2, seqlen_q=128, seqlen_k=128, head_dim=128,
                 causal=1, left=-1, right=-1, scale=0.125, drop=0.0, seed=0, dtype=1, stream=None)
     args.update(over)
     return L.fa_bwd(args["q"], args["k"], args["v"], args["o"], args["lse"], args["do"], args["dq"],
                     args["dk"], args["dv"], args["ws"], args["wsb"], args["cu_q"], args["cu_k"],
-                    args["batch"], args["heads"], args["kv_heads"], args["seqlen_q"], args["seqlen_k"],
+                    args["used_q"], args["used_k"], args["batch"], args["heads"], args["kv_heads"], args["seqlen_q"], args["seqlen_k"],
                     args["head_dim"], args["causal"], args["left"], args["right"], args["scale"],
                     args["drop"], args["seed"], args["dtype"], args["stream"])
 
@@ -89,6 +89,8 @@ BAD_FWD = [
     (dict(scale=-0.5), INVALID), (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
     (dict(cu_q=FAKE[10]), INVALID),                      # only one of the pair
     (dict(drop=-0.1), INVALID), (dict(drop=1.0), INVALID), (dict(drop=float("nan")), INVALID),
+    (dict(used_q=FAKE[11], cu_q=FAKE[10], cu_k=FAKE[9]), INVALID),   # padded lengths with a packed batch
+    (dict(used_k=ctypes.c_void_p(0x10002)), INVALID),                # misaligned
     (dict(head_dim=100), UNSUPPORTED), (dict(head_dim=256), UNSUPPORTED), (dict(head_dim=0), UNSUPPORTED),
     (dict(head_dim=136), UNSUPPORTED), (dict(head_dim=4), UNSUPPORTED), (dict(head_dim=-8), UNSUPPORTED),
     (dict(dtype=2), UNSUPPORTED), (dict(dtype=-1), UNSUPPORTED),
@@ -117,14 +119,14 @@ def test_bwd_rejects_bad_arguments(L, over, code):
 
 @pytest.mark.parametrize("stage", [-1, 3, 100])
 def test_bwd_stage_rejects_unknown_stage(L, stage):
-    args = [FAKE[i] for i in range(10)] + [1 << 20, None, None, 1, 4, 2, 128, 128, 128, 1, -1, -1, 0.125, 0.0, 0,
-                                           1, None]
+    args = [FAKE[i] for i in range(10)] + [1 << 20, None, None, None, None, 1, 4, 2, 128, 128, 128, 1, -1, -1,
+                                           0.125, 0.0, 0, 1, None]
     assert L.fa_bwd_stage(stage, *args) == INVALID
 
 
 def test_bwd_stage_validates_like_fa_bwd(L):
-    args = [FAKE[i] for i in range(10)] + [16, None, None, 1, 4, 2, 128, 128, 128, 1, -1, -1, 0.125, 0.1, 7,
-                                           1, None]
+    args = [FAKE[i] for i in range(10)] + [16, None, None, None, None, 1, 4, 2, 128, 128, 128, 1, -1, -1,
+                                           0.125, 0.1, 7, 1, None]
     for stage in range(3):
         assert L.fa_bwd_stage(stage, *args) == WORKSPACE
 
@@ -143,6 +145,7 @@ def test_valid_call_without_gfx950_reports_arch(L):
     assert fwd(L) == ARCH
     assert bwd(L) == ARCH
     assert fwd(L, drop=0.1, seed=2**64 - 1) == ARCH and bwd(L, drop=0.999, seed=3) == ARCH
+    assert fwd(L, used_q=FAKE[10], used_k=FAKE[11]) == ARCH and bwd(L, used_k=FAKE[11]) == ARCH
     # empty tensors may be NULL: no keys, no queries, empty batch
     assert fwd(L, k=None, v=None, seqlen_k=0) == ARCH
     assert fwd(L, q=None, o=None, lse=None, seqlen_q=0) == ARCH
