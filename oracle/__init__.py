@@ -183,3 +183,38 @@ def dropout_mask(batch, heads, lq, lk, p, seed):
     _load().oracle_dropout_mask(int(batch), int(heads), int(lq), int(lk), float(p),
                                 int(seed) & (2**64 - 1), _ptr(out))
     return out
+
+
+def _u8(x):
+    """FP8 codes as a uint8 numpy array (accepts torch float8 / uint8 tensors)."""
+    if hasattr(x, "detach"):
+        import torch
+        x = x.detach().cpu()
+        if x.dtype != torch.uint8:
+            x = x.view(torch.uint8)
+        x = x.numpy()
+    return np.ascontiguousarray(x, dtype=np.uint8)
+
+
+def fp8_e4m3_decode(codes):
+    """Values of FP8 E4M3 codes as float64, from the format's definition (OCP
+    8-bit floating point specification, E4M3 without infinities): sign bit,
+    4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 holds the
+    subnormals m * 2^-9; S.1111.111 is NaN, so the largest value is
+    1.75 * 2^8 = 448."""
+    c = _u8(codes)
+    e = ((c >> 3) & 0xF).astype(np.int64)
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(c & 0x80, -mag, mag)
+
+
+def attention_fwd_fp8(q8, k8, v8, descale_q, descale_k, descale_v, **kw):
+    """Exact attention (attention_fwd) of dequantised FP8 inputs: each tensor
+    is descale * E4M3(code), per tensor.  The scores are those of the
+    dequantised Q and K, so softmax_scale applies on top of the descales."""
+    q = fp8_e4m3_decode(q8) * float(descale_q)
+    k = fp8_e4m3_decode(k8) * float(descale_k)
+    v = fp8_e4m3_decode(v8) * float(descale_v)
+    return attention_fwd(q, k, v, **kw)

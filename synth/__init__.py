@@ -12,7 +12,10 @@ on numpy/torch versions or on the chunking used to produce them:
 * normals: Box-Muller on consecutive output pairs (2m, 2m+1), giving the
   cosine branch at even and the sine branch at odd element indices, in float64;
 * rounding: float64 -> float32 (round to nearest even) -> the 16-bit input
-  dtype (round to nearest even).
+  dtype (round to nearest even);
+* FP8 inputs ("fp8"): per-tensor scale amax / 448, then float64 / scale ->
+  float32 -> FP8 E4M3 (torch.float8_e4m3fn, round to nearest even); the
+  problem carries the descales (the scales themselves).
 
 Streams for one seed: Q = 16*seed + 0, K = +1, V = +2, dO = +3, lengths = +4.
 Tensors are laid out (batch, seqlen, heads, head_dim) with the last dimension
@@ -122,6 +125,23 @@ def tensor(seed: int, stream: int, shape, dtype: str, factor: float = 1.0):
     return _to_dtype(x, dtype).reshape(tuple(shape))
 
 
+FP8_MAX = 448.0  # largest finite FP8 E4M3 value
+
+
+def tensor_fp8(seed: int, stream: int, shape, factor: float = 1.0):
+    """One seeded FP8 E4M3 tensor (torch.float8_e4m3fn, CPU) and its descale:
+    the normals of the stream, divided by amax / 448 and rounded to E4M3."""
+    import torch
+    n = int(np.prod(shape))
+    x = normals_f64(16 * seed + stream, n)
+    if factor != 1.0:
+        x *= factor
+    amax = float(np.abs(x).max()) if n else 0.0
+    descale = amax / FP8_MAX if amax > 0 else 1.0
+    t = torch.from_numpy((x / descale).astype(np.float32)).to(torch.float8_e4m3fn)
+    return t.reshape(tuple(shape)), descale
+
+
 @dataclass
 class Problem:
     """One attention problem: shapes, mask and the seeded tensors (CPU)."""
@@ -142,6 +162,9 @@ class Problem:
     v: object = None
     do: object = None
     meta: dict = field(default_factory=dict)
+    descale_q: float = 1.0  # FP8 problems: value = descale * E4M3(code)
+    descale_k: float = 1.0
+    descale_v: float = 1.0
 
     @property
     def varlen(self) -> bool:
@@ -190,6 +213,12 @@ def make_problem(*, dtype: str, batch: int, heads: int, kv_heads: int,
                 seqlen_q=seqlen, seqlen_k=seqlen_k, head_dim=head_dim,
                 causal=causal, window_left=window[0], window_right=window[1],
                 scale=scale, seqlens=lens)
+    if dtype == "fp8":
+        p.q, p.descale_q = tensor_fp8(seed, STREAM_Q, qshape, factor)
+        p.k, p.descale_k = tensor_fp8(seed, STREAM_K, kshape, factor)
+        p.v, p.descale_v = tensor_fp8(seed, STREAM_V, kshape, factor)
+        p.meta = dict(seed=seed, factor=factor)
+        return p  # forward only: no dO
     p.q = tensor(seed, STREAM_Q, qshape, dtype, factor)
     p.k = tensor(seed, STREAM_K, kshape, dtype, factor)
     p.v = tensor(seed, STREAM_V, kshape, dtype, factor)
@@ -212,6 +241,10 @@ WORKLOADS = {
         causal=True, scale=1.0 / math.sqrt(128.0), factor=0.5),
     "bf16_causal_gqa_b1_h32kv8_n32768_d128": dict(
         dtype="bf16", batch=1, heads=32, kv_heads=8, seqlen=32768, head_dim=128,
+        causal=True, scale=1.0 / math.sqrt(128.0), factor=0.5),
+    # FP8 forward on the 8K shape: E4M3 inputs with per-tensor scales
+    "fp8_causal_b1_h32_n8192_d128": dict(
+        dtype="fp8", batch=1, heads=32, kv_heads=32, seqlen=8192, head_dim=128,
         causal=True, scale=1.0 / math.sqrt(128.0), factor=0.5),
     "fp16_causal_window4096_varlen_b2_h16_d128": dict(
         dtype="fp16", batch=2, heads=16, kv_heads=16, seqlen=16384, head_dim=128,
