@@ -24,6 +24,10 @@ workload (one new token per sequence, GQA 32/8 heads, ragged caches of
 16K-32K tokens, d 128, bf16): bytes of the valid K/V cache rows read (plus
 q, o and lse) per call / call time, against the 8 TB/s HBM peak.
 
+An object "fp8" times the FP8 forward (fa_fwd_fp8: E4M3 Q, K, V with
+per-tensor scales, P rounded to E4M3, bf16 O) on the 8K shape, against the
+dense fp8 matrix-core peak.
+
 Prints ONE JSON line.  Only one GPU: --gpus above 1 exits with a message.
 """
 from __future__ import annotations
@@ -42,6 +46,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 4096 dense bf16 FLOP/clk/CU x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
+PEAK_FP8_TFLOPS = 5033.2    # 256 CUs x 8192 dense fp8 FLOP/clk/CU x 2.4 GHz
+FP8_WORKLOAD = "fp8_causal_b1_h32_n8192_d128"
 WORKLOAD = "bf16_causal_b1_h32_n8192_d128"
 METRIC = "attention fwd+bwd TFLOP/s and % MFMA bf16 peak, seq 8192 d128 causal, 1 GPU"
 def visible_pairs(p) -> int:
@@ -62,7 +68,7 @@ def visible_pairs(p) -> int:
     return total
 
 
-CPU_SAMPLE_HEADS = 4
+CPU_SAMPLE_HEADS = 8
 DECODE_WORKLOAD = "bf16_decode_gqa_b8_h32kv8_q1_cache32768_d128"
 
 
@@ -98,6 +104,29 @@ def bench_decode(fa, synth, torch, steps: int, warmup: int, measured_traffic):
             "bytes_per_call": int(decode_bytes(p)),
             "traffic": measured_traffic("decode", DECODE_WORKLOAD),
             "tokens_per_s": round(p.batch * p.seqlen_q / (ms / 1e3), 1)}
+
+
+def bench_fp8(fa, synth, torch, steps: int, warmup: int, measured_traffic):
+    dev = torch.device("cuda:0")
+    p = synth.workload(FP8_WORKLOAD)
+    q, k, v = p.q.to(dev), p.k.to(dev), p.v.to(dev)
+    plan = fa.Fp8Plan(q, k, v, p.descale_q, p.descale_k, p.descale_v, causal=p.causal,
+                      window_size=(p.window_left, p.window_right), softmax_scale=p.scale)
+    for _ in range(warmup):
+        plan.run()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(plan.stream)
+    for i in range(steps):
+        plan.run()
+        ev[i + 1].record(plan.stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]))
+    flops = 4.0 * p.head_dim * visible_pairs(p) * p.heads
+    tf = flops / (ms / 1e3) / 1e12
+    return {"workload": FP8_WORKLOAD, "ms": round(ms, 4), "bound": "mfma", "achieved": round(tf, 2),
+            "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4),
+            "traffic": measured_traffic("fwd_fp8", FP8_WORKLOAD)}
 
 
 def cpu_baseline(p, threads: int):
@@ -153,6 +182,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the KV-cache decode measurement")
     ap.add_argument("--no-dropout", action="store_true", help="skip the dropout step measurement")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 forward measurement")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (default min(16, cores))")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -261,10 +291,13 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
         "dropout": None,
+        "fp8": None,
         "decode": None,
     }
     if not args.no_dropout:
         out["dropout"] = bench_dropout(fa, p, q, k, v, do, K, args.warmup, fwd_flops + bwd_flops, torch)
+    if not args.no_fp8:
+        out["fp8"] = bench_fp8(fa, synth, torch, max(K, 20), max(args.warmup, 3), measured_traffic)
     if not args.no_decode:
         out["decode"] = bench_decode(fa, synth, torch, max(K, 20), max(args.warmup, 3), measured_traffic)
     if not args.no_cpu_baseline:

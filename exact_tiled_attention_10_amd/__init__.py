@@ -24,7 +24,7 @@ __all__ = [
     "FaError", "lib", "forward", "backward", "Plan", "flash_attn_func",
     "flash_attn_varlen_func", "workspace_size", "FA_DTYPE_F16", "FA_DTYPE_BF16",
     "forward_kvcache", "kvcache_workspace_size", "kvcache_splits", "DecodePlan",
-    "flash_attn_with_kvcache", "new_dropout_seed",
+    "flash_attn_with_kvcache", "new_dropout_seed", "forward_fp8", "Fp8Plan",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd.restype = I
     L.fa_bwd_stage.argtypes = [I] + [P] * 10 + [S] + [P] * 4 + [I] * 9 + [F, F, U64, I, P]
     L.fa_bwd_stage.restype = I
+    L.fa_fwd_fp8.argtypes = [P] * 9 + [I] * 9 + [F, F, F, F, I, P]
+    L.fa_fwd_fp8.restype = I
     L.fa_fwd_kvcache_workspace_size.argtypes = [I] * 7
     L.fa_fwd_kvcache_workspace_size.restype = S
     L.fa_fwd_kvcache.argtypes = [P] * 7 + [S] + [I] * 9 + [F, I, I, P]
@@ -193,6 +195,85 @@ def forward(q, k, v, *, causal=False, window_size=(-1, -1), softmax_scale=None,
     if rc != 0:
         raise FaError(rc, "fa_fwd")
     return out, lse
+
+
+_FP8_TYPES = (torch.float8_e4m3fn, torch.uint8)
+
+
+def _fp8_args(q, k, v, descale_q, descale_k, descale_v, causal, window_size, softmax_scale,
+              cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, out, lse, out_dtype,
+              seqused_q, seqused_k):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, None, q.device)
+        if t.dtype not in _FP8_TYPES:
+            raise TypeError(f"{name} must hold E4M3 codes (torch.float8_e4m3fn or uint8), got {t.dtype}")
+    if k.shape != v.shape:
+        raise ValueError("k and v shapes differ")
+    if cu_seqlens_q is not None:
+        _check(cu_seqlens_q, "cu_seqlens_q", torch.int32, q.device)
+        _check(cu_seqlens_k, "cu_seqlens_k", torch.int32, q.device)
+    g = _Geom(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    _check_used(seqused_q, "seqused_q", g.batch, q.device)
+    _check_used(seqused_k, "seqused_k", g.batch, q.device)
+    if out_dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("out_dtype must be torch.bfloat16 or torch.float16")
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    else:
+        _check(out, "out", out_dtype, q.device)
+        if out.shape != q.shape:
+            raise ValueError("out must have the shape of q")
+    if lse is None:
+        lse = torch.empty(g.lse_shape, dtype=torch.float32, device=q.device)
+    else:
+        _check(lse, "lse", torch.float32, q.device)
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+            _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(seqused_q), _ptr(seqused_k),
+            g.batch, g.heads, g.kv_heads, g.seqlen_q, g.seqlen_k, g.d,
+            int(bool(causal)), int(window_size[0]), int(window_size[1]),
+            _default_scale(g.d, softmax_scale), float(descale_q), float(descale_k), float(descale_v),
+            FA_DTYPE_BF16 if out_dtype == torch.bfloat16 else FA_DTYPE_F16]
+    return args, out, lse
+
+
+def forward_fp8(q, k, v, descale_q=1.0, descale_k=1.0, descale_v=1.0, *, causal=False, window_size=(-1, -1),
+                softmax_scale=None, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
+                max_seqlen_k=None, out=None, lse=None, out_dtype=torch.bfloat16, seqused_q=None,
+                seqused_k=None):
+    """FP8 forward: q, k, v hold E4M3 codes (torch.float8_e4m3fn, or their
+    bytes as uint8), each tensor's values being its descale times the code's
+    value.  Returns (out, lse): O in ``out_dtype`` (bf16 or fp16), LSE float32,
+    of the attention of the dequantised inputs with P rounded to E4M3 before
+    P.V (include/fa.h).  head_dim 64 or 128."""
+    L = lib()
+    args, out, lse = _fp8_args(q, k, v, descale_q, descale_k, descale_v, causal, window_size, softmax_scale,
+                               cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, out, lse, out_dtype,
+                               seqused_q, seqused_k)
+    rc = L.fa_fwd_fp8(*args, _stream(q.device))
+    if rc != 0:
+        raise FaError(rc, "fa_fwd_fp8")
+    return out, lse
+
+
+class Fp8Plan:
+    """Pre-resolved arguments of fa_fwd_fp8 on fixed buffers (benchmark
+    loop); ``run()`` enqueues one call on ``stream`` (default: q's current
+    torch stream)."""
+
+    def __init__(self, q, k, v, descale_q=1.0, descale_k=1.0, descale_v=1.0, *, causal=False,
+                 window_size=(-1, -1), softmax_scale=None, out_dtype=torch.bfloat16, stream=None):
+        self._L = lib()
+        self.q, self.k, self.v = q, k, v
+        args, self.out, self.lse = _fp8_args(q, k, v, descale_q, descale_k, descale_v, causal, window_size,
+                                             softmax_scale, None, None, None, None, None, None, out_dtype,
+                                             None, None)
+        self.stream = stream if stream is not None else torch.cuda.current_stream(q.device)
+        self._args = args + [ctypes.c_void_p(self.stream.cuda_stream)]
+
+    def run(self):
+        rc = self._L.fa_fwd_fp8(*self._args)
+        if rc != 0:
+            raise FaError(rc, "fa_fwd_fp8")
 
 
 def workspace_size(batch, heads, seqlen_q, head_dim, dtype) -> int:

@@ -16,7 +16,7 @@ CALIB_OUT = os.path.join(HERE, "libfacalib.so")
 CALIB_SOURCE = "fa_calib.hip"
 BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip", "fa_pad.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip", "fa_pad.hip", "fa_fwd_fp8.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 ALU forms stay off: plain fp32 code only

@@ -133,6 +133,46 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
     return FA_OK;
 }
 
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+               const int32_t* seqused_q, const int32_t* seqused_k,
+               int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
+               int head_dim, int causal, int window_left, int window_right, float softmax_scale,
+               float descale_q, float descale_k, float descale_v, int out_dtype, void* stream) {
+    for (float d : {descale_q, descale_k, descale_v})
+        if (!std::isfinite(d) || d < 0.f) return FA_ERR_INVALID_ARG;
+    if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return FA_ERR_INVALID_ARG;
+    const float sc = softmax_scale * descale_q * descale_k;  // scale of the raw E4M3 dot products
+    int rc = check_common(batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim, causal, window_left,
+                          window_right, sc, out_dtype, cu_seqlens_q, cu_seqlens_k);
+    if (rc != FA_OK) return rc;
+    if (head_dim != 64 && head_dim != 128) return FA_ERR_UNSUPPORTED;
+    if (!seqused_ok(seqused_q, seqused_k, cu_seqlens_q)) return FA_ERR_INVALID_ARG;
+    const bool has_q = (long long)batch * seqlen_q > 0, has_k = (long long)batch * seqlen_k > 0;
+    if ((has_q && (!q || !o || !lse)) || (has_k && (!k || !v))) return FA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+        return FA_ERR_INVALID_ARG;
+    rc = check_arch();
+    if (rc != FA_OK) return rc;
+    fa::Fp8Args a8;
+    fa::FwdArgs& a = a8.f;
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
+    a.used_q = seqused_q; a.used_k = seqused_k;
+    a.batch = batch; a.heads = heads; a.kv_heads = kv_heads;
+    a.seqlen_q = seqlen_q; a.seqlen_k = seqlen_k; a.head_dim = head_dim;
+    a.causal = causal; a.left = window_left; a.right = window_right;
+    a.scale = sc; a.scale_log2 = log2e_scaled(sc);
+    a.bf16 = out_dtype == FA_DTYPE_BF16;
+    a.drop_t = 256; a.drop_scale = 1.f; a.seed_lo = 0; a.seed_hi = 0;
+    a8.v_scale = descale_v;
+    if (fa::launch_fwd_fp8(a8, (hipStream_t)stream) != 0) return FA_ERR_LAUNCH;
+    if (seqused_q && fa::launch_pad_fill(o, lse, seqused_q, batch, seqlen_q, heads, head_dim,
+                                         (hipStream_t)stream) != 0)
+        return FA_ERR_LAUNCH;
+    return FA_OK;
+}
+
 size_t fa_bwd_workspace_size(int batch, int heads, int seqlen_q, int head_dim, int dtype) {
     if (batch < 0 || heads < 1 || seqlen_q < 0) return 0;
     if (!head_dim_ok(head_dim)) return 0;

@@ -29,6 +29,11 @@ struct FwdArgs {
     uint32_t seed_lo, seed_hi;
 };
 
+struct Fp8Args {
+    FwdArgs f;
+    float v_scale;  // descale of V: O = v_scale * sum_j p_j v_j / l
+};
+
 struct BwdArgs {
     const void* q;
     const void* k;
@@ -80,6 +85,9 @@ struct DecArgs {
 // Each returns 0 when every launch was accepted, 1 otherwise.  Backward
 // stages: 0 = D_i = dO_i . O_i, 1 = dK/dV pass, 2 = dQ pass.
 int launch_fwd(const FwdArgs& a, hipStream_t stream);
+// FP8 forward: f.q/k/v hold E4M3 bytes, f.scale = softmax_scale * dq * dk
+// (f.scale_log2 likewise), f.o is bf16 or fp16 (f.bf16); no dropout.
+int launch_fwd_fp8(const Fp8Args& a, hipStream_t stream);
 int launch_bwd(const BwdArgs& a, int stage, hipStream_t stream);
 int launch_decode(const DecArgs& a, hipStream_t stream);
 

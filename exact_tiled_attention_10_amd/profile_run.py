@@ -2,7 +2,7 @@
 
 Subcommands (run from anywhere; the repository root is found from this file):
 
-  run     --workload W --kernel {fwd,rowdot,dkdv,dq,decode} [--iters N]
+  run     --workload W --kernel {fwd,rowdot,dkdv,dq,decode,fwd_fp8} [--iters N]
           Run one kernel of the library N times on a named synthetic workload
           (after one untimed call of each earlier stage to produce its inputs;
           `decode` runs the KV-cache decode call, split pass and merge, on a
@@ -47,10 +47,11 @@ KERNEL_SOURCES = {
     "dkdv": ["fa_bwd.hip", "fa_device.hpp"],
     "dq": ["fa_bwd.hip", "fa_device.hpp"],
     "decode": ["fa_decode.hip", "fa_device.hpp"],
+    "fwd_fp8": ["fa_fwd_fp8.hip", "fa_device.hpp"],
 }
 # Kernel-name substrings in rocprofv3 output.
 KERNEL_NAMES = {"fwd": "fwd_kernel", "rowdot": "bwd_rowdot_kernel", "dkdv": "bwd_dkdv_kernel",
-                "dq": "bwd_dq_kernel", "decode": "decode_split_kernel"}
+                "dq": "bwd_dq_kernel", "decode": "decode_split_kernel", "fwd_fp8": "fwd_fp8_kernel"}
 COPY_NAME = "calib_copy_kernel"
 CALIB_LIB = os.path.join(HERE, "libfacalib.so")
 
@@ -102,6 +103,16 @@ def _run(args):
             plan.run()
         torch.cuda.synchronize()
         print(f"ran decode x{args.iters} on {args.workload}", flush=True)
+        return
+    if args.kernel == "fwd_fp8":
+        p = synth.workload(args.workload)
+        plan = fa.Fp8Plan(p.q.to(dev), p.k.to(dev), p.v.to(dev), p.descale_q, p.descale_k, p.descale_v,
+                          causal=p.causal, window_size=(p.window_left, p.window_right), softmax_scale=p.scale)
+        torch.cuda.synchronize()
+        for _ in range(args.iters):
+            plan.run()
+        torch.cuda.synchronize()
+        print(f"ran fwd_fp8 x{args.iters} on {args.workload}", flush=True)
         return
     p = synth.workload(args.workload)
     q, k, v, do = (t.to(dev) for t in (p.q, p.k, p.v, p.do))

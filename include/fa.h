@@ -98,7 +98,8 @@ extern "C" {
 enum fa_status {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, bad scale   */
-    FA_ERR_UNSUPPORTED = 2, /* head_dim not a multiple of 8 in [8, 128], or dtype  */
+    FA_ERR_UNSUPPORTED = 2, /* head_dim not a multiple of 8 in [8, 128] (FP8: not
+                               64 or 128), or dtype                                */
     FA_ERR_ARCH = 3,        /* no HIP device, or the current device is not gfx950 */
     FA_ERR_WORKSPACE = 4,   /* workspace smaller than the *_workspace_size() call */
     FA_ERR_LAUNCH = 5       /* a kernel launch was rejected by the runtime        */
@@ -131,6 +132,36 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
            int head_dim, int causal, int window_left, int window_right,
            float softmax_scale, float dropout_p, uint64_t dropout_seed, int dtype, void* stream);
+
+/*
+ * FP8 forward (overview page, section 5.2: attention on FP8 matrix cores with
+ * float8_e4m3fn inputs).  q, k, v hold one byte per element, codes of the
+ * 8-bit E4M3 format (OCP 8-bit floating point, E4M3 without infinities:
+ * bias 7, largest value 448, 0x7F / 0xFF NaN), in the layouts above; the
+ * value of an element is its tensor's descale times the code's value.
+ * Computes the attention of those dequantised tensors:
+ *   scores      softmax_scale * descale_q * descale_k * (q8 . k8), fp32
+ *               (the matrix cores' FP8 dot products: not exactly rounded,
+ *               observed within 2^-14 of the sum of the products' magnitudes)
+ *   LSE         natural log of the sum of exp(score) over visible keys
+ *   O           descale_v * sum_j P_ij v8_j / l_i, with the probabilities P
+ *               rounded to E4M3 (nearest even) before the product and l_i
+ *               their unrounded fp32 sum; stored as out_dtype (fa_dtype)
+ * The rounding of P is the one approximation: each rounded P_ij lies within
+ * 2^-4 P_ij + 2^-14 of P_ij (P relative to the row's largest probability),
+ * so |O_ic - exact| <= (2^-4 sum_j P_ij |v_jc| + 2^-14 sum_j |v_jc| / L_i) / l_i
+ * plus the score error and the output rounding, L_i being the row's sum of
+ * exp(score - max score).
+ *   head_dim 64 or 128 (FA_ERR_UNSUPPORTED otherwise); descales finite and
+ *   >= 0; no dropout, no backward.  Everything else as for fa_fwd (masks,
+ *   GQA, packed and padded batches, empty rows, alignment, errors).
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+               const int32_t* seqused_q, const int32_t* seqused_k,
+               int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
+               int head_dim, int causal, int window_left, int window_right, float softmax_scale,
+               float descale_q, float descale_k, float descale_v, int out_dtype, void* stream);
 
 /*
  * Bytes of device workspace fa_bwd needs for these sizes: two float32

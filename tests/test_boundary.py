@@ -38,7 +38,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_fwd",
-                                    "fa_fwd_kvcache", "fa_fwd_kvcache_splits",
+                                    "fa_fwd_fp8", "fa_fwd_kvcache", "fa_fwd_kvcache_splits",
                                     "fa_fwd_kvcache_workspace_size", "fa_strerror", "fa_version"]
 
 
@@ -102,6 +102,34 @@ def test_fwd_rejects_bad_arguments(L, over, code):
     assert fwd(L, **over) == code
 
 
+def fwd8(L, **over):
+    args = dict(q=FAKE[0], k=FAKE[1], v=FAKE[2], o=FAKE[3], lse=FAKE[4], cu_q=None, cu_k=None,
+                used_q=None, used_k=None, batch=1, heads=4, kv_heads=2, seqlen_q=128, seqlen_k=128, head_dim=128,
+                causal=1, left=-1, right=-1, scale=0.125, dq=0.01, dk=0.02, dv=0.5, dtype=1, stream=None)
+    args.update(over)
+    return L.fa_fwd_fp8(args["q"], args["k"], args["v"], args["o"], args["lse"], args["cu_q"], args["cu_k"],
+                        args["used_q"], args["used_k"], args["batch"], args["heads"], args["kv_heads"],
+                        args["seqlen_q"], args["seqlen_k"], args["head_dim"], args["causal"], args["left"],
+                        args["right"], args["scale"], args["dq"], args["dk"], args["dv"], args["dtype"],
+                        args["stream"])
+
+
+BAD_FWD8 = [
+    (dict(q=None), INVALID), (dict(v=None), INVALID), (dict(o=ctypes.c_void_p(0x10008)), INVALID),
+    (dict(dq=-1.0), INVALID), (dict(dk=float("nan")), INVALID), (dict(dv=float("inf")), INVALID),
+    (dict(scale=-1.0), INVALID), (dict(scale=1e30, dq=1e30, dk=1e30), INVALID),   # product overflows
+    (dict(heads=6, kv_heads=4), INVALID), (dict(causal=3), INVALID), (dict(cu_k=FAKE[10]), INVALID),
+    (dict(used_q=FAKE[11], cu_q=FAKE[10], cu_k=FAKE[9]), INVALID),
+    (dict(head_dim=96), UNSUPPORTED), (dict(head_dim=32), UNSUPPORTED), (dict(head_dim=256), UNSUPPORTED),
+    (dict(dtype=2), UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("over,code", BAD_FWD8)
+def test_fwd_fp8_rejects_bad_arguments(L, over, code):
+    assert fwd8(L, **over) == code
+
+
 BAD_BWD = [
     (dict(do=None), INVALID), (dict(dq=None), INVALID), (dict(dk=None), INVALID),
     (dict(dv=None), INVALID), (dict(ws=None), INVALID),
@@ -146,6 +174,7 @@ def test_valid_call_without_gfx950_reports_arch(L):
     assert bwd(L) == ARCH
     assert fwd(L, drop=0.1, seed=2**64 - 1) == ARCH and bwd(L, drop=0.999, seed=3) == ARCH
     assert fwd(L, used_q=FAKE[10], used_k=FAKE[11]) == ARCH and bwd(L, used_k=FAKE[11]) == ARCH
+    assert fwd8(L) == ARCH and fwd8(L, head_dim=64, dtype=0, dq=0.0) == ARCH
     # empty tensors may be NULL: no keys, no queries, empty batch
     assert fwd(L, k=None, v=None, seqlen_k=0) == ARCH
     assert fwd(L, q=None, o=None, lse=None, seqlen_q=0) == ARCH
