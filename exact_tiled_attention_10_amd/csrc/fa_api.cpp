@@ -21,10 +21,10 @@ std::atomic<int> g_arch_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
-// Supported head dimensions: multiples of 8 (16-byte rows) up to 128; the
-// kernels run them in tiles 64 or 128 wide.
-bool head_dim_ok(int d) { return d >= 8 && d <= 128 && d % 8 == 0; }
-int tile_width(int d) { return d > 64 ? 128 : 64; }
+// Supported head dimensions: multiples of 8 (16-byte rows) up to 256; the
+// kernels run them in tiles 64, 128 or 256 wide.
+bool head_dim_ok(int d) { return d >= 8 && d <= 256 && d % 8 == 0; }
+int tile_width(int d) { return d > 128 ? 256 : (d > 64 ? 128 : 64); }
 
 int check_common(int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k, int head_dim,
                  int causal, int window_left, int window_right, float softmax_scale, int dtype,

@@ -133,8 +133,8 @@ struct DqCfg {
     static constexpr int stageElems = 2 * tileElems;  // K then V
 };
 
-template <bool BF16, int D, int NW, int BN, bool DROP>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
+template <bool BF16, int D, int NW, int BN, bool DROP, int WPE>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(WPE, WPE)))
 void bwd_dq_kernel(BwdArgs a) {
     using C = DqCfg<D, NW, BN>;
     using Dma = TileDma<D, BN, NW>;
@@ -319,19 +319,26 @@ constexpr int kKvBN = 32 * kKvWaves;  // keys per workgroup
 constexpr int kKvBM = 128;            // query rows per streamed tile
 constexpr int kKvQB = kKvBM / 32;     // 32-row blocks per tile
 
-template <int D>
+template <int D, int BMR>
 struct DkdvCfg {
-    static constexpr int tileElems = kKvBM * D;
-    // per stage: Q tile, dO tile (16-bit), then lse2[kKvBM], D[kKvBM] (fp32)
-    static constexpr int stageBytes = 2 * tileElems * 2 + 2 * kKvBM * 4;
+    static constexpr int tileElems = BMR * D;
+    // per stage: Q tile, dO tile (16-bit), then lse2[BMR], D[BMR] (fp32)
+    static constexpr int stageBytes = 2 * tileElems * 2 + 2 * BMR * 4;
 };
 
-template <bool BF16, int D, bool DROP>
+// D: tile width of the contraction over head_dim (S, dP); DO: the dK / dV
+// columns one workgroup accumulates, columns DO * blockIdx.z .. + DO - 1
+// (DO = D, except at width 256, where the accumulators of all 256 columns and
+// the resident K^T / V^T do not fit the register file together: two
+// workgroups per key tile, each recomputing S and dP); BMR: query rows per
+// streamed tile (64 at width 256, so that two stages fit in LDS).
+template <bool BF16, int D, bool DROP, int DO, int BMR>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdArgs a) {
-    using C = DkdvCfg<D>;
-    using Dma = TileDma<D, kKvBM, kKvWaves>;
-    constexpr int KS = D / 16, DB = D / 32, CPR = D / 8;
+    using C = DkdvCfg<D, BMR>;
+    using Dma = TileDma<D, BMR, kKvWaves>;
+    constexpr int KS = D / 16, DB = DO / 32, CPR = D / 8;
+    const int c0 = (int)blockIdx.z * DO;  // first dK / dV column of this workgroup
     // separate objects per stage (no waits on the other stage's direct loads)
     __shared__ __attribute__((aligned(16))) uint8_t lds0[C::stageBytes];
     __shared__ __attribute__((aligned(16))) uint8_t lds1[C::stageBytes];
@@ -358,8 +365,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
     if (a.causal) i_lo = max(i_lo, j0 - s.off);
     if (a.right >= 0) i_lo = max(i_lo, j0 - s.off - a.right);
     if (a.left >= 0) i_hi = min(i_hi, j1 - s.off + a.left);
-    const int it_lo = i_lo / kKvBM;
-    const int it_hi = i_hi >= i_lo ? i_hi / kKvBM + 1 : it_lo;
+    const int it_lo = i_lo / BMR;
+    const int it_hi = i_hi >= i_lo ? i_hi / BMR + 1 : it_lo;
     const int nt = it_hi - it_lo;  // tiles per head
 
     // This wave's keys and, per lane, the query rows that see its key.
@@ -389,8 +396,12 @@ void bwd_dkdv_kernel(BwdArgs a) {
     int q_rd[KS];  // A operand reads of the Q / dO tiles: row r32 (+32 qb), chunk 2 ks + half
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) q_rd[ks] = r32 * D + (((2 * ks + half) ^ swz<CPR>(r32)) * 8);
-    int t_rd[2][DB];  // Q^T / dO^T operands (transposing reads)
+    int t_rd[2][DB];  // Q^T / dO^T operands (transposing reads) of columns c0 ..
     tr_offsets<D, DB>(lane, t_rd);
+#pragma unroll
+    for (int inst = 0; inst < 2; ++inst)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) t_rd[inst][db] += c0;  // c0 / 8 is a multiple of 16: above the swizzle
 
     auto q_lds = [&](int buf) { return (uint16_t*)(buf ? lds1 : lds0); };
     auto lse_lds = [&](int buf) { return (float*)((buf ? lds1 : lds0) + 2 * C::tileElems * 2); };
@@ -398,25 +409,25 @@ void bwd_dkdv_kernel(BwdArgs a) {
     // Flattened (query head in group, query tile) sequence n = 0 .. g*nt-1.
     auto issue_step = [&](int n, int buf) {
         const int h = hk * g + n / nt;
-        const int row0 = (it_lo + n % nt) * kKvBM;
-        const bool tail = row0 + kKvBM > s.len_q;
+        const int row0 = (it_lo + n % nt) * BMR;
+        const bool tail = row0 + BMR > s.len_q;
         const int last = s.len_q - 1 - row0;
         const int64_t hoff = (s.q_start * a.heads + h) * dh + (int64_t)row0 * q_stride;
         uint16_t* qt = q_lds(buf);
         dma.issue((const uint16_t*)a.q + hoff, qt, wave, q_stride, tail, last);
         dma.issue((const uint16_t*)a.dout + hoff, qt + C::tileElems, wave, q_stride, tail, last);
-        constexpr int kRowLoads = kKvBM / 64;  // 4-byte direct loads (64 rows each) per array
+        constexpr int kRowLoads = BMR / 64;  // 4-byte direct loads (64 rows each) per array
         static_assert(2 * kRowLoads <= kKvWaves, "one row-term load per wave");
         if (wave < 2 * kRowLoads) {  // lse2 rows, then D rows
             const int arr = wave / kRowLoads, part = wave % kRowLoads;
             const int64_t idx0 = a.cu_q ? (int64_t)h * total_q + s.q_start + row0
                                         : ((int64_t)b * a.heads + h) * a.seqlen_q + row0;
             const float* src = (arr == 0 ? a.lse2 : a.dsum) + idx0 + min(64 * part + lane, last);
-            dma4(src, lse_lds(buf) + arr * kKvBM + 64 * part);
+            dma4(src, lse_lds(buf) + arr * BMR + 64 * part);
         }
     };
 
-    // One step covers a kKvBM-row query tile as kKvQB blocks of 32 rows,
+    // One step covers a BMR-row query tile as (BMR / 32) blocks of 32 rows,
     // software-pipelined over the blocks: phase ph multiplies S, dP of block
     // ph and dV, dK of block ph-2 beside the softmax arithmetic (P, dS) of
     // block ph-1, so the matrix cores and the vector ALU work side by side and
@@ -429,16 +440,17 @@ void bwd_dkdv_kernel(BwdArgs a) {
     // branch that touches nothing but those words.  Masked entries of rows
     // without any visible key give inf or NaN before the AND, never after.
     auto compute = [&](int n, int buf, bool full) {
-        constexpr int QBS = kKvQB;
+        constexpr int QBS = (BMR / 32);
         constexpr int kPf = 2;          // k-steps of operand reads ahead of their MFMAs
         constexpr int NJ = 4 * DB;      // dV, dK products per block
         constexpr int JPS = NJ / KS;    // dV, dK products per k-step
-        constexpr int MPS = 8 / KS;     // softmax register pairs per k-step
-        const int row0 = (it_lo + n % nt) * kKvBM;
+        constexpr int KPM = KS > 8 ? KS / 8 : 1;  // k-steps per softmax slot
+        constexpr int MPS = KS >= 8 ? 1 : 8 / KS;  // softmax register pairs per slot
+        const int row0 = (it_lo + n % nt) * BMR;
         const uint16_t* qt = q_lds(buf);
         const uint16_t* dot = qt + C::tileElems;
         const float* lses = lse_lds(buf);
-        const float* dss = lses + kKvBM;
+        const float* dss = lses + BMR;
         const int lo = q_lo - row0, hi = q_hi - row0;
 
         const int hq = hk * g + n / nt;  // query head of this step
@@ -542,10 +554,13 @@ void bwd_dkdv_kernel(BwdArgs a) {
                 }
                 // row terms of the softmax block: group gq serves pairs 2 gq, 2 gq + 1,
                 // read one group ahead of its first use
-                if (hv && (ks * MPS) % 2 == 0 && (ks * MPS) / 2 + 1 < 4) load_rows(bv, (ks * MPS) / 2 + 1);
-                if (hv) {
+                if (ks % KPM == 0) {
+                    const int m0 = (ks / KPM) * MPS;  // first pair of this slot
+                    if (hv && m0 % 2 == 0 && m0 / 2 + 1 < 4) load_rows(bv, m0 / 2 + 1);
+                    if (hv) {
 #pragma unroll
-                    for (int m = ks * MPS; m < (ks + 1) * MPS; ++m) softmax_pair(bv, m);
+                        for (int m = m0; m < m0 + MPS; ++m) softmax_pair(bv, m);
+                    }
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -567,13 +582,13 @@ void bwd_dkdv_kernel(BwdArgs a) {
     auto step = [&](int n, int buf) {
         const bool has_next = n + 1 < total;
         if (has_next) issue_step(n + 1, buf ^ 1);
-        const int row0 = (it_lo + n % nt) * kKvBM;
-        const int row1 = min(row0 + kKvBM, s.len_q) - 1;
+        const int row0 = (it_lo + n % nt) * BMR;
+        const int row1 = min(row0 + BMR, s.len_q) - 1;
         // any visible pair between rows [row0, row1] and keys [kw0, kw1]?  (uniform)
         if (wave_live && mk.hi_of(row1, s) >= kw0 && mk.lo_of(row0, s) <= kw1) {
             // all visible: the first row sees the last key and the last row the first key
-            const bool full = row0 + kKvBM <= s.len_q && kw0 + 31 < s.len_k &&
-                              mk.hi_of(row0, s) >= kw0 + 31 && mk.lo_of(row0 + kKvBM - 1, s) <= kw0;
+            const bool full = row0 + BMR <= s.len_q && kw0 + 31 < s.len_k &&
+                              mk.hi_of(row0, s) >= kw0 + 31 && mk.lo_of(row0 + BMR - 1, s) <= kw0;
             compute(n, buf, full);
         }
         wait_vmcnt<0>();
@@ -597,7 +612,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-            const int col = db * 32 + 8 * gq + 4 * half;  // four columns, all below dh or none
+            const int col = c0 + db * 32 + 8 * gq + 4 * half;  // four columns, all below dh or none
             if (col >= dh) continue;
             u32x2 wk, wv;
             wk.x = pack2<BF16>(dk[db][4 * gq] * a.scale, dk[db][4 * gq + 1] * a.scale);
@@ -627,20 +642,25 @@ int launch_bwd_t(const BwdArgs& a, int stage, hipStream_t stream) {
         return 0;
     }
     if (stage == 1) {  // dK, dV
+        constexpr int DO = D > 128 ? 128 : D, BMR = D > 128 ? 64 : kKvBM;
         const int ntiles = (a.seqlen_k + kKvBN - 1) / kKvBN;
         if (ntiles > 0 && a.batch > 0) {
-            auto kern = a.drop_t < 256 ? bwd_dkdv_kernel<BF16, D, true> : bwd_dkdv_kernel<BF16, D, false>;
-            hipLaunchKernelGGL(kern, dim3(a.batch * a.kv_heads, ntiles), dim3(256), 0, stream, a);
+            auto kern = a.drop_t < 256 ? bwd_dkdv_kernel<BF16, D, true, DO, BMR>
+                                       : bwd_dkdv_kernel<BF16, D, false, DO, BMR>;
+            hipLaunchKernelGGL(kern, dim3(a.batch * a.kv_heads, ntiles, D / DO), dim3(256), 0, stream, a);
             if (hipGetLastError() != hipSuccess) return 1;
         }
         return 0;
     }
-    // stage 2: dQ
-    constexpr int NW = FA_DQ_NW, BN = D == 128 ? 64 : 128;
+    // stage 2: dQ (at width 256: 4 waves at one per SIMD, 32-key tiles; the
+    // resident Q, dO and the dQ accumulators take 256 registers per lane)
+    constexpr int NW = D > 128 ? 4 : FA_DQ_NW, BN = D > 128 ? 32 : (D == 128 ? 64 : 128);
+    constexpr int WPE = D > 128 ? 1 : 2;
     constexpr int BM = 32 * NW;
     const int ntiles = (a.seqlen_q + BM - 1) / BM;
     if (ntiles > 0 && a.batch > 0) {
-        auto kern = a.drop_t < 256 ? bwd_dq_kernel<BF16, D, NW, BN, true> : bwd_dq_kernel<BF16, D, NW, BN, false>;
+        auto kern = a.drop_t < 256 ? bwd_dq_kernel<BF16, D, NW, BN, true, WPE>
+                                   : bwd_dq_kernel<BF16, D, NW, BN, false, WPE>;
         hipLaunchKernelGGL(kern, dim3(a.batch * a.heads, ntiles), dim3(64 * NW), 0, stream, a);
         if (hipGetLastError() != hipSuccess) return 1;
     }
@@ -650,7 +670,9 @@ int launch_bwd_t(const BwdArgs& a, int stage, hipStream_t stream) {
 }  // namespace
 
 int launch_bwd(const BwdArgs& a, int stage, hipStream_t stream) {
-    // tile width: the smallest of 64, 128 holding head_dim
+    // tile width: the smallest of 64, 128, 256 holding head_dim
+    if (a.head_dim > 128)
+        return a.bf16 ? launch_bwd_t<true, 256>(a, stage, stream) : launch_bwd_t<false, 256>(a, stage, stream);
     if (a.bf16)
         return a.head_dim > 64 ? launch_bwd_t<true, 128>(a, stage, stream) : launch_bwd_t<true, 64>(a, stage, stream);
     return a.head_dim > 64 ? launch_bwd_t<false, 128>(a, stage, stream) : launch_bwd_t<false, 64>(a, stage, stream);

@@ -19,7 +19,7 @@
 //     result (O normalised, LSE) per piece.  Piece (group j, segment s) of
 //     kv head hk goes to slot (j + s) * kv_heads + hk: groups and segments
 //     both advance along the same axis, so no two pieces share a slot;
-//   * inside a piece the loads of K and V run kDecAhead steps ahead into
+//   * inside a piece the loads of K and V run kDecAhead steps (one at width 256) ahead into
 //     registers (coalesced 16-byte loads; the register file is far larger
 //     than LDS, so many bytes are in flight per CU); at its turn a step is
 //     written to the wave's own LDS tiles, from which the matrix-core
@@ -55,6 +55,9 @@ struct DecCfg {
     static constexpr int tileElems = kDecBK * D;       // one K or V tile
     static constexpr int kLd = tileElems * 2 / 1024;   // 16-byte loads per lane per tile
     static constexpr int kRowsPerLd = 1024 / (2 * D);  // cache rows per wave load
+    // steps in flight: at width 256 one step's K and V already take 128
+    // registers per lane
+    static constexpr int kAhead = D > 128 ? 1 : kDecAhead;
 };
 
 // Valid keys of sequence b.
@@ -227,7 +230,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecArgs a) {
         float m_run = kNegInf, l_part = 0.f;
 
         // registers of the steps in flight
-        u32x4 kr[kDecAhead][C::kLd], vr[kDecAhead][C::kLd];
+        u32x4 kr[C::kAhead][C::kLd], vr[C::kAhead][C::kLd];
         auto load = [&](int st, u32x4 (&kx)[C::kLd], u32x4 (&vx)[C::kLd]) {
             const int key0 = st * kDecBK;
 #pragma unroll
@@ -292,21 +295,21 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecArgs a) {
 
         const int sa = st_lo + off, se = sa + cnt;
 #pragma unroll
-        for (int j = 0; j < kDecAhead; ++j) load(sa + j, kr[j], vr[j]);
-        // Whole groups of kDecAhead steps (each step's registers fixed, one
-        // exit), then the last < kDecAhead steps, which load nothing more.
+        for (int j = 0; j < C::kAhead; ++j) load(sa + j, kr[j], vr[j]);
+        // Whole groups of C::kAhead steps (each step's registers fixed, one
+        // exit), then the last < C::kAhead steps, which load nothing more.
         int st = sa;
-        const int groups = cnt / kDecAhead;
-        for (int it = 0; it < groups; ++it, st += kDecAhead) {
+        const int groups = cnt / C::kAhead;
+        for (int it = 0; it < groups; ++it, st += C::kAhead) {
 #pragma unroll
-            for (int j = 0; j < kDecAhead; ++j) {
+            for (int j = 0; j < C::kAhead; ++j) {
                 stage(kr[j], vr[j]);
-                load(st + j + kDecAhead, kr[j], vr[j]);
+                load(st + j + C::kAhead, kr[j], vr[j]);
                 compute(st + j);
             }
         }
 #pragma unroll
-        for (int j = 0; j < kDecAhead - 1; ++j) {
+        for (int j = 0; j < C::kAhead - 1; ++j) {
             if (st + j < se) {
                 stage(kr[j], vr[j]);
                 compute(st + j);
@@ -440,6 +443,7 @@ int launch_decode_t(const DecArgs& a, hipStream_t stream) {
 }  // namespace
 
 int launch_decode(const DecArgs& a, hipStream_t stream) {
+    if (a.head_dim > 128) return a.bf16 ? launch_decode_t<true, 256>(a, stream) : launch_decode_t<false, 256>(a, stream);
     if (a.bf16)
         return a.head_dim > 64 ? launch_decode_t<true, 128>(a, stream) : launch_decode_t<true, 64>(a, stream);
     return a.head_dim > 64 ? launch_decode_t<false, 128>(a, stream) : launch_decode_t<false, 64>(a, stream);

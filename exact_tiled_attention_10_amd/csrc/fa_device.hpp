@@ -117,7 +117,9 @@ __device__ __forceinline__ void transpose4x8(const u32x4& r0, const u32x4& r1, c
 // ---------------------------------------------------------------------------
 template <int CPR>
 __device__ __forceinline__ int swz(int row) {
-    if constexpr (CPR == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+    // 32 chunks (512-byte rows): the same 4-bit permutation as for 16, on
+    // the chunk's low bits (its high bit is kept)
+    if constexpr (CPR == 16 || CPR == 32) return ((row & 3) << 2) | ((row >> 2) & 3);
     else return ((row & 3) << 1) | ((row >> 2) & 1);
 }
 

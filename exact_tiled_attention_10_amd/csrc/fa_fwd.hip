@@ -385,7 +385,13 @@ int launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
 int launch_fwd(const FwdArgs& a, hipStream_t stream) {
     constexpr int NW = FA_FWD_NW, QB = FA_FWD_QB, W = FA_FWD_WPE;
     constexpr int B1 = FA_FWD_BN128, B2 = FA_FWD_BN64;
-    // tile width: the smallest of 64, 128 holding head_dim
+    // tile width: the smallest of 64, 128, 256 holding head_dim.  At 256 the
+    // O accumulators (128 per lane) and the resident Q^T (64) need more than
+    // half the register file: 4 waves at one per SIMD, 64-key tiles (two
+    // 64 KiB LDS stages).
+    if (a.head_dim > 128)
+        return a.bf16 ? launch_fwd_t<true, 256, 4, 1, 32, 1>(a, stream)
+                      : launch_fwd_t<false, 256, 4, 1, 32, 1>(a, stream);
     if (a.bf16)
         return a.head_dim > 64 ? launch_fwd_t<true, 128, NW, QB, B1, W>(a, stream)
                                : launch_fwd_t<true, 64, NW, QB, B2, W>(a, stream);

@@ -98,7 +98,7 @@ extern "C" {
 enum fa_status {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, bad scale   */
-    FA_ERR_UNSUPPORTED = 2, /* head_dim not a multiple of 8 in [8, 128] (FP8: not
+    FA_ERR_UNSUPPORTED = 2, /* head_dim not a multiple of 8 in [8, 256] (FP8: not
                                64 or 128), or dtype                                */
     FA_ERR_ARCH = 3,        /* no HIP device, or the current device is not gfx950 */
     FA_ERR_WORKSPACE = 4,   /* workspace smaller than the *_workspace_size() call */
@@ -117,8 +117,8 @@ enum fa_dtype { FA_DTYPE_F16 = 0, FA_DTYPE_BF16 = 1 };
  *   cu_seqlens_q/k in : both NULL (fixed length) or both device int32[batch+1]
  *   seqused_q/k    in : NULL, or device int32[batch] (padded batches, above)
  *   batch >= 0, heads >= 1, kv_heads >= 1 with heads % kv_heads == 0,
- *   seqlen_q >= 0, seqlen_k >= 0, head_dim a multiple of 8 from 8 to 128
- *   (run in tiles 64 or 128 wide; a head_dim below the tile width costs the
+ *   seqlen_q >= 0, seqlen_k >= 0, head_dim a multiple of 8 from 8 to 256
+ *   (run in tiles 64, 128 or 256 wide; a head_dim below the tile width costs the
  *   tile width's arithmetic),
  *   causal in {0, 1}, window_left >= -1, window_right >= -1 (-1 = unbounded),
  *   softmax_scale finite and >= 0 (callers wanting the default pass

@@ -91,8 +91,9 @@ BAD_FWD = [
     (dict(drop=-0.1), INVALID), (dict(drop=1.0), INVALID), (dict(drop=float("nan")), INVALID),
     (dict(used_q=FAKE[11], cu_q=FAKE[10], cu_k=FAKE[9]), INVALID),   # padded lengths with a packed batch
     (dict(used_k=ctypes.c_void_p(0x10002)), INVALID),                # misaligned
-    (dict(head_dim=100), UNSUPPORTED), (dict(head_dim=256), UNSUPPORTED), (dict(head_dim=0), UNSUPPORTED),
-    (dict(head_dim=136), UNSUPPORTED), (dict(head_dim=4), UNSUPPORTED), (dict(head_dim=-8), UNSUPPORTED),
+    (dict(head_dim=100), UNSUPPORTED), (dict(head_dim=264), UNSUPPORTED), (dict(head_dim=0), UNSUPPORTED),
+    (dict(head_dim=252), UNSUPPORTED), (dict(head_dim=4), UNSUPPORTED), (dict(head_dim=-8), UNSUPPORTED),
+    (dict(head_dim=512), UNSUPPORTED),
     (dict(dtype=2), UNSUPPORTED), (dict(dtype=-1), UNSUPPORTED),
 ]
 
@@ -219,7 +220,7 @@ BAD_DEC = [
     (dict(kc=ctypes.c_void_p(0x10008)), INVALID),
     (dict(heads=6, kv_heads=4), INVALID), (dict(seqlen_q=-1), INVALID), (dict(causal=3), INVALID),
     (dict(scale=float("nan")), INVALID), (dict(left=-7), INVALID),
-    (dict(head_dim=84), UNSUPPORTED), (dict(head_dim=144), UNSUPPORTED), (dict(dtype=5), UNSUPPORTED),
+    (dict(head_dim=84), UNSUPPORTED), (dict(head_dim=264), UNSUPPORTED), (dict(dtype=5), UNSUPPORTED),
     (dict(batch=1 << 16, seqlen_k=1 << 20), INVALID),      # 2^16 x 2^15 steps: beyond 32 bits
     (dict(batch=1 << 20, heads=2048, kv_heads=2048), INVALID),  # 2^31 output rows
     (dict(wsb=16), WORKSPACE),

@@ -1,6 +1,8 @@
-"""Head dimensions other than the two tile widths: any multiple of 8 up to
-128 (the contract on the install guide page, yfxerp.com/news/195771, section
-3.3: a multiple of 8, not too small), run in tiles 64 or 128 wide.  Forward,
+"""Head dimensions other than the tile widths: any multiple of 8 up to 256
+(the contract on the install guide page, yfxerp.com/news/195771, section
+3.3: a multiple of 8, not too small), run in tiles 64, 128 or 256 wide; 256
+itself and the widths between 128 and 256 take the widest tiles (dK / dV in
+two column halves).  Forward,
 backward, decode and dropout against the fp64 oracle, element by element,
 with the same tolerances as the tile widths themselves (O max-abs 4e-3 fp16 /
 2e-2 bf16, LSE 1e-3, dQ/dK/dV relative L2 2e-2); guard bands check that no
@@ -46,6 +48,11 @@ CASES = [
     (72, "fp16", dict(batch=1, heads=2, kv_heads=2, seqlen=333, causal=True, window=(50, 0))),
     (96, "bf16", dict(batch=2, heads=4, kv_heads=4, seqlen=530, causal=True)),
     (120, "fp16", dict(batch=1, heads=4, kv_heads=2, seqlen=150, seqlen_k=290, causal=True)),
+    (136, "bf16", dict(batch=2, heads=2, kv_heads=1, seqlen=270, causal=True)),
+    (192, "fp16", dict(batch=1, heads=4, kv_heads=2, seqlen=333, causal=True, window=(80, 0))),
+    (256, "bf16", dict(batch=2, heads=4, kv_heads=2, seqlen=300, causal=True)),
+    (256, "fp16", dict(batch=1, heads=2, kv_heads=2, seqlen=140, seqlen_k=397, causal=False)),
+    (248, "bf16", dict(batch=1, heads=3, kv_heads=3, seqlen=129, seqlen_k=77, causal=True)),
 ]
 
 
@@ -81,7 +88,7 @@ def test_forward_backward(fa, oracle_mod, d, dtype, kw):
     assert eo <= O_TOL[dtype] and el <= LSE_TOL and max(errs) <= GRAD_TOL
 
 
-@pytest.mark.parametrize("d", [24, 96])
+@pytest.mark.parametrize("d", [24, 96, 256])
 def test_dropout_with_odd_head_dim(fa, oracle_mod, d):
     p = synth.make_problem(dtype="bf16", batch=1, heads=4, kv_heads=2, seqlen=260, head_dim=d, causal=True,
                            seed=22)
@@ -100,7 +107,7 @@ def test_dropout_with_odd_head_dim(fa, oracle_mod, d):
     assert eo <= O_TOL["bf16"] and max(errs) <= GRAD_TOL
 
 
-@pytest.mark.parametrize("d,dtype", [(32, "fp16"), (80, "bf16"), (112, "bf16")])
+@pytest.mark.parametrize("d,dtype", [(32, "fp16"), (80, "bf16"), (112, "bf16"), (200, "fp16"), (256, "bf16")])
 def test_decode(fa, oracle_mod, d, dtype):
     p = synth.make_decode(dtype=dtype, batch=3, heads=8, kv_heads=2, seqlen_q=2, capacity=700, head_dim=d,
                           causal=True, cache_lens=[1, 350, 700], seed=23)
@@ -120,3 +127,36 @@ def test_decode(fa, oracle_mod, d, dtype):
             el = max(el, float(np.abs(gl[b][fin] - rl[0][fin]).max()))
     say(f"[head dim decode] d={d} {dtype} O {eo:.2e} LSE {el:.2e}")
     assert eo <= O_TOL[dtype] and el <= LSE_TOL
+
+
+def test_width_256_varlen_and_padded(fa, oracle_mod):
+    """Packed varlen (empty and one-token sequences) and a padded batch at
+    head_dim 256, against the oracle on each valid sequence."""
+    p = synth.make_problem(dtype="bf16", batch=0, heads=4, kv_heads=2, seqlen=0, head_dim=256, causal=True,
+                           seqlens=[1, 200, 0, 131], seed=24)
+    dev = torch.device("cuda:0")
+    cu = p.cu_seqlens().to(dev)
+    q, k, v, do = (t.to(dev) for t in (p.q, p.k, p.v, p.do))
+    kw = dict(causal=True, softmax_scale=p.scale, cu_seqlens_q=cu, cu_seqlens_k=cu,
+              max_seqlen_q=p.seqlen_q, max_seqlen_k=p.seqlen_k)
+    o, lse = fa.forward(q, k, v, **kw)
+    dq, dk, dv = fa.backward(do, q, k, v, o, lse, **kw)
+    torch.cuda.synchronize()
+    g = lambda t: t.float().cpu().double().numpy()
+    rdq, rdk, rdv, ro, rlse = oracle_mod.attention_bwd(p.q, p.k, p.v, p.do, scale=p.scale, causal=True,
+                                                       cu_seqlens=p.cu_seqlens().numpy())
+    eo = float(np.abs(g(o) - ro).max())
+    errs = [rel_l2(g(dq), rdq), rel_l2(g(dk), rdk), rel_l2(g(dv), rdv)]
+    say(f"[head dim 256 varlen] O {eo:.2e} dq/dk/dv " + " ".join(f"{e:.2e}" for e in errs))
+    assert eo <= O_TOL["bf16"] and max(errs) <= GRAD_TOL
+    # padded: rows past seqused are zero, LSE -inf
+    p2 = synth.make_problem(dtype="bf16", batch=2, heads=2, kv_heads=1, seqlen=150, head_dim=256, causal=True,
+                            seed=25)
+    used = torch.tensor([150, 70], dtype=torch.int32, device=dev)
+    q2, k2, v2 = (t.to(dev) for t in (p2.q, p2.k, p2.v))
+    o2, l2 = fa.forward(q2, k2, v2, causal=True, softmax_scale=p2.scale, seqused_q=used, seqused_k=used)
+    torch.cuda.synchronize()
+    go2, gl2 = g(o2), l2.cpu().double().numpy()
+    assert np.all(go2[1, 70:] == 0) and np.all(np.isneginf(gl2[1, :, 70:]))
+    ro2, _ = oracle_mod.attention_fwd(p2.q[1:2, :70], p2.k[1:2, :70], p2.v[1:2, :70], scale=p2.scale, causal=True)
+    assert float(np.abs(go2[1:2, :70] - ro2).max()) <= O_TOL["bf16"]
