@@ -237,6 +237,8 @@ def _trace(args):
                        "kernels_ms": {k: v["ms"] for k, v in d["kernels"].items()}}
             if d.get("decode"):
                 summary["decode"] = {k: d["decode"][k] for k in ("workload", "ms_per_call", "achieved", "unit")}
+            if d.get("fp8"):
+                summary["fp8"] = {k: d["fp8"][k] for k in ("workload", "ms", "achieved", "unit")}
             out += ["", "bench.py line of the same run (HIP-event kernel times, ms):", "", "```",
                     json.dumps(summary), "```"]
     print("\n".join(out))
