@@ -261,6 +261,30 @@ __device__ __forceinline__ bool keep_byte(uint32_t w, int e, uint32_t thresh) {
 // Geometry of one (batch, head) problem slice: packed (cu_seqlens), fixed
 // length, or fixed layout with fewer valid rows (used_q / used_k: padded
 // batches, lengths clamped to the layout).
+#ifndef FA_XCD_GROUPS
+#define FA_XCD_GROUPS 1
+#endif
+// (batch, query head) of workgroup column x in a grid over batch * heads.
+// The GPU hands workgroups to its 8 XCDs (each with its own L2) in turn, so
+// columns x and x + 8 run on the same XCD.  When the g = heads / kv_heads
+// query heads reading one kv head can all share an XCD (g > 1 and the
+// batch * kv_heads groups a multiple of 8), group G goes to XCD G % 8 and
+// its heads to columns G % 8 + 8 ((G / 8) g + r), r = 0 .. g-1: the group's
+// K and V are then fetched into one L2.  Otherwise x = b * heads + h.  A
+// bijection either way.
+__device__ __forceinline__ void xcd_head(int x, int batch, int heads, int kv_heads, int& b, int& h) {
+    const int g = heads / kv_heads, groups = batch * kv_heads;
+    if (FA_XCD_GROUPS && g > 1 && (groups & 7) == 0) {
+        const int xcd = x & 7, p = x >> 3;
+        const int grp = (p / g) * 8 + xcd;
+        b = grp / kv_heads;
+        h = (grp % kv_heads) * g + p % g;
+    } else {
+        b = x / heads;
+        h = x % heads;
+    }
+}
+
 struct Seq {
     int64_t q_start, k_start;  // first row of the sequence in the tensor
     int len_q, len_k;          // valid rows

@@ -86,8 +86,8 @@ void fwd_kernel(FwdArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches below
     const int r32 = lane & 31, half = lane >> 5;
-    const int hb = blockIdx.x;
-    const int b = hb / a.heads, h = hb % a.heads;
+    int b, h;
+    xcd_head(blockIdx.x, a.batch, a.heads, a.kv_heads, b, h);
     const int ntiles = gridDim.y;
     const int qt = a.causal ? (ntiles - 1 - (int)blockIdx.y) : (int)blockIdx.y;
     const Seq s = seq_of(b, a.cu_q, a.cu_k, a.used_q, a.used_k, a.seqlen_q, a.seqlen_k);
