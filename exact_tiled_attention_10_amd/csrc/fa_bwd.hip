@@ -93,19 +93,17 @@ struct TileDma {
     static constexpr int kPerWave = kBlocks / NW;
     static constexpr int kRowsPerBlock = 1024 / (D * 2);
     static_assert(kBlocks % NW == 0, "tile must split evenly into 1 KiB blocks per wave");
-    int goff[kPerWave];
-    int row[kPerWave];
+    // The lane's row in block i is row0 + i * kRowsPerBlock; its offsets are
+    // recomputed at each issue (a few integer operations) rather than kept in
+    // registers for the whole kernel.
+    int row0, slot, last_chunk;
     // dh: the tensor's row length (multiple of 8, at most D); slots past it
     // receive the row's last valid chunk again
     __device__ __forceinline__ void init(int wave, int lane, int stride, int dh) {
-#pragma unroll
-        for (int i = 0; i < kPerWave; ++i) {
-            const int bi = wave * kPerWave + i;
-            const int r = bi * kRowsPerBlock + lane / CPR;
-            const int slot = lane % CPR;
-            row[i] = r;
-            goff[i] = r * stride + min(slot ^ swz<CPR>(r), dh / 8 - 1) * 8;
-        }
+        row0 = wave * kPerWave * kRowsPerBlock + lane / CPR;
+        slot = lane % CPR;
+        last_chunk = dh / 8 - 1;
+        (void)stride;
     }
     // g: first row of the tile in global memory; last: last valid row index
     // relative to g (rows beyond are clamped); tail: whether clamping applies.
@@ -113,8 +111,9 @@ struct TileDma {
                                           bool tail, int last) const {
 #pragma unroll
         for (int i = 0; i < kPerWave; ++i) {
-            int off = goff[i];
-            if (tail && row[i] > last) off += (last - row[i]) * stride;
+            const int r = row0 + i * kRowsPerBlock;
+            const int rg = tail && r > last ? last : r;
+            const int off = rg * stride + min(slot ^ swz<CPR>(r), last_chunk) * 8;
             dma16(g + off, tile + (wave * kPerWave + i) * 512);
         }
     }
@@ -216,63 +215,85 @@ void bwd_dq_kernel(BwdArgs a) {
         dma.issue(vbase + toff, st + C::tileElems, wave, kv_stride, tail, last);
     };
 
+    // One key tile, as KB blocks of 32 keys in a three-stage pipeline of
+    // phases: phase ph multiplies S^T, dP^T of block ph, computes P^T, dS^T of
+    // block ph-1 and accumulates dQ^T += K^T dS^T of block ph-2, one k-step at a
+    // time (each k-step: one S/dP product pair, one dQ product, and a slice of
+    // the exponentials), so the matrix cores and the vector ALU of one wave
+    // work side by side.  Operands are read one k-step ahead of their products.
     auto compute = [&](int t, int buf) {
         const int key0 = t * BN;
         if (!(wave_live && key0 <= w_key_hi && key0 + BN - 1 >= w_key_lo)) return;
         const uint16_t* kt = stage(buf);
         const uint16_t* vt = kt + C::tileElems;
-        f32x16 sacc[KB], dpacc[KB];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) { sacc[kb] = f32x16{0}; dpacc[kb] = f32x16{0}; }
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            u32x4 ka[KB], va[KB];
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                ka[kb] = *(const u32x4*)(kt + kb * 32 * D + k_rd[ks]);
-                va[kb] = *(const u32x4*)(vt + kb * 32 * D + k_rd[ks]);
-            }
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                sacc[kb] = mfma32<BF16>(ka[kb], qf[ks], sacc[kb]);
-                dpacc[kb] = mfma32<BF16>(va[kb], dof[ks], dpacc[kb]);
-            }
-        }
         // lane column = query row; register i = key key0 + kb*32 + 8(i/4) + 4 half + i%4
         const bool masked = key0 < w_full_lo || key0 + BN - 1 > w_full_hi;  // uniform
         const int lo = row_lo - key0, hi = row_hi - key0;
+        constexpr int KPM = KS > 8 ? KS / 8 : 1;   // k-steps per slot of exponentials
+        constexpr int MPS = KS >= 8 ? 1 : 8 / KS;  // register pairs per slot
+        static_assert(2 * DB == KS, "one dQ product per k-step");
+        f32x16 sacc[KB], dpacc[KB];
         uint32_t dsp[KB][8];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            u32x4 kw;  // dropout keep words of this lane's query row, as in the forward
+        u32x4 ka[2], va[2], tq[2];  // S / dP operands and dQ operands, double-buffered
+        u32x4 kw;                   // dropout keep words of the block in the exponential stage
+        auto load_sd = [&](int kb, int ks, int slot) {
+            ka[slot] = *(const u32x4*)(kt + kb * 32 * D + k_rd[ks]);
+            va[slot] = *(const u32x4*)(vt + kb * 32 * D + k_rd[ks]);
+        };
+        // dQ product j of block kb: key k-step 2 kb + j / DB, output block j % DB
+        auto load_q = [&](int kb, int j, int slot) {
+            tq[slot] = read_tr<D, DB>(kt, 2 * kb + j / DB, j % DB, kt_rd);
+        };
+        auto pair = [&](int kb, int m) {  // P, dS of registers 2m, 2m + 1 of block kb
+            const int i = 2 * m;
+            float p0 = fast_exp2(__builtin_fmaf(sacc[kb][i], c, -lse2));
+            float p1 = fast_exp2(__builtin_fmaf(sacc[kb][i + 1], c, -lse2));
+            if (masked) {
+                const int k0 = kb * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+                p0 = (k0 < lo || k0 > hi) ? 0.f : p0;
+                p1 = (k0 + 1 < lo || k0 + 1 > hi) ? 0.f : p1;
+            }
+            float dp0 = dpacc[kb][i], dp1 = dpacc[kb][i + 1];
             if constexpr (DROP) {
-                const uint32_t jq = (uint32_t)(key0 + 32 * kb) / 4 + 2 * (r32 & 3) + half;
-                kw = quad_transpose(philox4x32_10(jq, (uint32_t)row / 4, h, b, a.seed_lo, a.seed_hi));
+                dp0 = keep_byte(kw[i / 4], i % 4, a.drop_t) ? dp0 * a.drop_scale : 0.f;
+                dp1 = keep_byte(kw[i / 4], (i + 1) % 4, a.drop_t) ? dp1 * a.drop_scale : 0.f;
             }
+            dsp[kb][m] = pack2<BF16>(p0 * (dp0 - dsum), p1 * (dp1 - dsum));
+        };
 #pragma unroll
-            for (int i = 0; i < 16; i += 2) {
-                float p0 = fast_exp2(__builtin_fmaf(sacc[kb][i], c, -lse2));
-                float p1 = fast_exp2(__builtin_fmaf(sacc[kb][i + 1], c, -lse2));
-                if (masked) {
-                    const int k0 = kb * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-                    p0 = (k0 < lo || k0 > hi) ? 0.f : p0;
-                    p1 = (k0 + 1 < lo || k0 + 1 > hi) ? 0.f : p1;
+        for (int ph = 0; ph <= KB + 1; ++ph) {
+            const int bs = ph, bv = ph - 1, bp = ph - 2;  // S/dP, exponential and dQ blocks
+            const bool hs = bs < KB, hv = bv >= 0 && bv < KB, hp = bp >= 0;
+            if constexpr (DROP) {
+                if (hv) {  // keep words of this lane's query row, as in the forward
+                    const uint32_t jq = (uint32_t)(key0 + 32 * bv) / 4 + 2 * (r32 & 3) + half;
+                    kw = quad_transpose(philox4x32_10(jq, (uint32_t)row / 4, h, b, a.seed_lo, a.seed_hi));
                 }
-                float dp0 = dpacc[kb][i], dp1 = dpacc[kb][i + 1];
-                if constexpr (DROP) {
-                    dp0 = keep_byte(kw[i / 4], i % 4, a.drop_t) ? dp0 * a.drop_scale : 0.f;
-                    dp1 = keep_byte(kw[i / 4], (i + 1) % 4, a.drop_t) ? dp1 * a.drop_scale : 0.f;
-                }
-                dsp[kb][i / 2] = pack2<BF16>(p0 * (dp0 - dsum), p1 * (dp1 - dsum));
             }
-        }
-        // dQ^T += K^T dS^T over the BN keys (k-steps of 16)
+            if (hs) load_sd(bs, 0, 0);
+            if (hp) load_q(bp, 0, 0);
 #pragma unroll
-        for (int kk = 0; kk < BN / 16; ++kk) {
-            const int kb = kk / 2, hs = kk % 2;
-            const u32x4 sb = u32x4{dsp[kb][4 * hs], dsp[kb][4 * hs + 1], dsp[kb][4 * hs + 2], dsp[kb][4 * hs + 3]};
+            for (int ks = 0; ks < KS; ++ks) {
+                if (hs && ks + 1 < KS) load_sd(bs, ks + 1, (ks + 1) & 1);
+                if (hp && ks + 1 < KS) load_q(bp, ks + 1, (ks + 1) & 1);
+                __builtin_amdgcn_sched_barrier(0);
+                if (hs) {
+                    sacc[bs] = mfma32<BF16>(ka[ks & 1], qf[ks], ks ? sacc[bs] : f32x16{0});
+                    dpacc[bs] = mfma32<BF16>(va[ks & 1], dof[ks], ks ? dpacc[bs] : f32x16{0});
+                }
+                if (hp) {
+                    const int j = ks, hsel = j / DB, db = j % DB;
+                    const u32x4 sb = u32x4{dsp[bp][4 * hsel], dsp[bp][4 * hsel + 1], dsp[bp][4 * hsel + 2],
+                                           dsp[bp][4 * hsel + 3]};
+                    dq[db] = mfma32<BF16>(tq[ks & 1], sb, dq[db]);
+                }
+                if (hv && ks % KPM == 0) {
+                    const int m0 = (ks / KPM) * MPS;
 #pragma unroll
-            for (int db = 0; db < DB; ++db) dq[db] = mfma32<BF16>(read_tr<D, DB>(kt, kk, db, kt_rd), sb, dq[db]);
+                    for (int m = m0; m < m0 + MPS; ++m) pair(bv, m);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     };
 
