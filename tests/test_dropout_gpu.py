@@ -104,6 +104,8 @@ SMALL = {
                                      seqlens=[1, 63, 65, 257, 0, 300]), 0.25),
     "q_shorter_than_k_bf16_d64": (dict(dtype="bf16", batch=2, heads=2, kv_heads=1, seqlen=150, seqlen_k=333,
                                        head_dim=64, causal=True), 0.4),
+    "gqa_groups_on_one_xcd_bf16_d128": (dict(dtype="bf16", batch=2, heads=12, kv_heads=4, seqlen=160, head_dim=128,
+                                             causal=True), 0.3),
 }
 
 

@@ -159,6 +159,8 @@ CASES = {
                                 seqlens=[1, 255, 0, 257, 600]), torch.bfloat16),
     "large_scores_d128": (dict(batch=1, heads=2, kv_heads=2, seqlen=300, head_dim=128, causal=True, scale=0.5,
                                factor=3.0), torch.bfloat16),
+    "gqa_groups_on_one_xcd_d128": (dict(batch=4, heads=8, kv_heads=2, seqlen=200, head_dim=128, causal=True),
+                                   torch.bfloat16),
 }
 
 

@@ -129,6 +129,11 @@ SMALL = {
     "single_token_bf16_d128": dict(dtype="bf16", batch=3, heads=2, kv_heads=1, seqlen=1, head_dim=128, causal=True),
     "zero_scale_causal_fp16_d64": dict(dtype="fp16", batch=1, heads=2, kv_heads=2, seqlen=200, head_dim=64, causal=True, scale=0.0),
     "large_scores_bf16_d128": dict(dtype="bf16", batch=1, heads=2, kv_heads=2, seqlen=260, head_dim=128, causal=True, scale=0.8),
+    # batch * kv_heads a multiple of 8: the grids place each GQA group's query heads on one XCD
+    "gqa_groups_on_one_xcd_bf16_d128": dict(dtype="bf16", batch=2, heads=16, kv_heads=4, seqlen=270, head_dim=128,
+                                            causal=True),
+    "gqa_groups_on_one_xcd_varlen_fp16_d64": dict(dtype="fp16", batch=0, heads=6, kv_heads=2, seqlen=0, head_dim=64,
+                                                  causal=False, seqlens=[40, 1, 130, 0]),
 }
 
 
