@@ -99,11 +99,10 @@ struct TileDma {
     int row0, slot, last_chunk;
     // dh: the tensor's row length (multiple of 8, at most D); slots past it
     // receive the row's last valid chunk again
-    __device__ __forceinline__ void init(int wave, int lane, int stride, int dh) {
+    __device__ __forceinline__ void init(int wave, int lane, int dh) {
         row0 = wave * kPerWave * kRowsPerBlock + lane / CPR;
         slot = lane % CPR;
         last_chunk = dh / 8 - 1;
-        (void)stride;
     }
     // g: first row of the tile in global memory; last: last valid row index
     // relative to g (rows beyond are clamped); tail: whether clamping applies.
@@ -193,7 +192,7 @@ void bwd_dq_kernel(BwdArgs a) {
     const int row_lo = mk.lo_of(row, s), row_hi = mk.hi_of(row, s);
 
     Dma dma;
-    dma.init(wave, lane, kv_stride, dh);
+    dma.init(wave, lane, dh);
     int k_rd[KS];  // A operand reads of the K / V tiles: row r32, chunk 2 ks + half
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) k_rd[ks] = r32 * D + (((2 * ks + half) ^ swz<CPR>(r32)) * 8);
@@ -414,7 +413,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const float c = a.scale_log2;
 
     Dma dma;
-    dma.init(wave, lane, q_stride, dh);
+    dma.init(wave, lane, dh);
     int q_rd[KS];  // A operand reads of the Q / dO tiles: row r32 (+32 qb), chunk 2 ks + half
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) q_rd[ks] = r32 * D + (((2 * ks + half) ^ swz<CPR>(r32)) * 8);

@@ -46,7 +46,6 @@ namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLazyLog2F8 = 4.0f;
 constexpr float kShiftLog2F8 = 4.0f;
