@@ -1,0 +1,127 @@
+"""Seeded random configurations on the GPU, forward and backward against the
+fp64 oracle element by element (O max-abs 4e-3 fp16 / 2e-2 bf16, LSE 1e-3,
+dQ/dK/dV relative L2 2e-2, the tolerances of the fixed cases).
+
+Each configuration draws, from its own seed: the 16-bit type, a head_dim
+among the multiples of 8 up to 256, a GQA ratio, query and key lengths
+(equal, or not for the fixed layout), causal or not, a window or none, the
+layout (fixed, packed variable-length or padded with seqused) and dropout or
+none.  The combinations the fixed cases do not list are where a wrong index
+or a missed mask shows.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = {"fp16": 4e-3, "bf16": 2e-2}
+LSE_TOL = 1e-3
+GRAD_TOL = 2e-2
+N_CONFIGS = 64
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def fa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_tiled_attention_10_amd as m
+    m.lib()
+    return m
+
+
+def draw(seed):
+    r = np.random.default_rng(1000 + seed)
+    d = int(r.choice([8, 16, 40, 64, 72, 96, 128, 136, 192, 248, 256]))
+    g = int(r.choice([1, 2, 4, 8]))
+    kv = int(r.integers(1, 3))
+    layout = str(r.choice(["fixed", "varlen", "padded"]))
+    cfg = dict(dtype=str(r.choice(["fp16", "bf16"])), head_dim=d, heads=g * kv, kv_heads=kv,
+               causal=bool(r.integers(0, 2)))
+    if r.random() < 0.4:
+        cfg["window"] = (int(r.integers(0, 200)), int(r.integers(0, 60)) if r.random() < 0.5 else -1)
+    if layout == "varlen":
+        n = int(r.integers(1, 5))
+        cfg.update(batch=0, seqlen=0, seqlens=[int(x) for x in r.integers(0, 300, n)])
+        if sum(cfg["seqlens"]) == 0:
+            cfg["seqlens"][0] = 5
+    else:
+        cfg.update(batch=int(r.integers(1, 4)), seqlen=int(r.integers(1, 320)))
+        if r.random() < 0.5:
+            cfg["seqlen_k"] = int(r.integers(1, 320))
+    drop = float(r.choice([0.0, 0.0, 0.25]))
+    used = None
+    if layout == "padded":
+        nq, nk = cfg["seqlen"], cfg.get("seqlen_k", cfg["seqlen"])
+        used = ([int(x) for x in r.integers(0, nq + 1, cfg["batch"])], [int(x) for x in r.integers(0, nk + 1, cfg["batch"])])
+    return cfg, layout, drop, used
+
+
+def rel_l2(a, b):
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
+
+
+@pytest.mark.parametrize("seed", range(N_CONFIGS))
+def test_random_config(fa, oracle_mod, seed):
+    cfg, layout, drop, used = draw(seed)
+    say(f"[random {seed}] {layout} drop={drop} used={used} {cfg}")
+    p = synth.make_problem(seed=50 + seed, **cfg)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (t.to(dev) for t in (p.q, p.k, p.v, p.do))
+    cu = p.cu_seqlens()
+    kw = dict(causal=p.causal, window_size=(p.window_left, p.window_right), softmax_scale=p.scale,
+              dropout_p=drop, dropout_seed=77 + seed)
+    if cu is not None:
+        cud = cu.to(dev)
+        kw.update(cu_seqlens_q=cud, cu_seqlens_k=cud, max_seqlen_q=p.seqlen_q, max_seqlen_k=p.seqlen_k)
+    if used is not None:
+        kw.update(seqused_q=torch.tensor(used[0], dtype=torch.int32, device=dev),
+                  seqused_k=torch.tensor(used[1], dtype=torch.int32, device=dev))
+    o, lse = fa.forward(q, k, v, **kw)
+    dq, dk, dv = fa.backward(do, q, k, v, o, lse, **kw)
+    torch.cuda.synchronize()
+    g = lambda t: t.float().cpu().double().numpy()
+    got = dict(o=g(o), lse=lse.cpu().double().numpy(), dq=g(dq), dk=g(dk), dv=g(dv))
+    okw = dict(scale=p.scale, causal=p.causal, window=(p.window_left, p.window_right), dropout_p=drop,
+               seed=77 + seed, threads=16)
+    if used is None:
+        rdq, rdk, rdv, ro, rlse = oracle_mod.attention_bwd(p.q, p.k, p.v, p.do,
+                                                           cu_seqlens=None if cu is None else cu.numpy(), **okw)
+        ref = dict(o=ro, lse=rlse, dq=rdq, dk=rdk, dv=rdv)
+    else:
+        # padded: the oracle on the valid prefixes, packed with their own prefix sums
+        uq, uk = used
+        cq = np.concatenate([[0], np.cumsum(uq)]).astype(np.int32)
+        ck = np.concatenate([[0], np.cumsum(uk)]).astype(np.int32)
+        cat = lambda x, u: np.concatenate([x[b, :u[b]].double().numpy() for b in range(p.batch)])
+        rdq, rdk, rdv, ro, rlse = oracle_mod.attention_bwd(cat(p.q, uq), cat(p.k, uk), cat(p.v, uk), cat(p.do, uq),
+                                                           cu_seqlens=cq, cu_seqlens_k=ck, **okw)
+        for b in range(p.batch):  # padded rows as the definition fixes them
+            assert np.all(got["o"][b, uq[b]:] == 0) and np.all(np.isneginf(got["lse"][b, :, uq[b]:]))
+            assert np.all(got["dq"][b, uq[b]:] == 0)
+            assert np.all(got["dk"][b, uk[b]:] == 0) and np.all(got["dv"][b, uk[b]:] == 0)
+        pk = lambda x, u: np.concatenate([x[b, :u[b]] for b in range(p.batch)])
+        got = dict(o=pk(got["o"], uq), lse=np.concatenate([got["lse"][b, :, :uq[b]] for b in range(p.batch)], axis=1),
+                   dq=pk(got["dq"], uq), dk=pk(got["dk"], uk), dv=pk(got["dv"], uk))
+        ref = dict(o=ro, lse=rlse, dq=rdq, dk=rdk, dv=rdv)
+    eo = float(np.abs(got["o"] - ref["o"]).max()) if ref["o"].size else 0.0
+    fin = np.isfinite(ref["lse"])
+    assert np.array_equal(np.isneginf(got["lse"]), np.isneginf(ref["lse"]))
+    el = float(np.abs(got["lse"][fin] - ref["lse"][fin]).max()) if fin.any() else 0.0
+    errs = {n: rel_l2(got[n], ref[n]) for n in ("dq", "dk", "dv") if np.linalg.norm(ref[n]) > 0}
+    say(f"  O {eo:.2e} LSE {el:.2e} " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()))
+    assert eo <= O_TOL[p.dtype] and el <= LSE_TOL
+    for n, e in errs.items():
+        assert e <= GRAD_TOL, n
+    for n in ("dq", "dk", "dv"):  # an all-zero reference (no visible pair) must come back zero
+        if np.linalg.norm(ref[n]) == 0:
+            assert np.all(got[n] == 0), n
