@@ -7,7 +7,9 @@ among the multiples of 8 up to 256, a GQA ratio, query and key lengths
 (equal, or not for the fixed layout), causal or not, a window or none, the
 layout (fixed, packed variable-length or padded with seqused) and dropout or
 none.  The combinations the fixed cases do not list are where a wrong index
-or a missed mask shows.
+or a missed mask shows.  The KV-cache decode gets the same treatment: GQA
+ratio, new tokens, cache lengths (empty included), head_dim, masks and the
+split count.
 """
 import sys
 
@@ -125,3 +127,43 @@ def test_random_config(fa, oracle_mod, seed):
     for n in ("dq", "dk", "dv"):  # an all-zero reference (no visible pair) must come back zero
         if np.linalg.norm(ref[n]) == 0:
             assert np.all(got[n] == 0), n
+
+
+def draw_decode(seed):
+    r = np.random.default_rng(5000 + seed)
+    kv = int(r.choice([1, 2, 4]))
+    g = int(r.choice([1, 2, 4, 8, 16]))
+    cap = int(r.integers(1, 2000))
+    batch = int(r.integers(1, 5))
+    cfg = dict(dtype=str(r.choice(["fp16", "bf16"])), batch=batch, heads=g * kv, kv_heads=kv,
+               seqlen_q=int(r.choice([1, 2, 5, 8, 16, 33])), capacity=cap,
+               head_dim=int(r.choice([8, 64, 80, 128, 200, 256])), causal=bool(r.integers(0, 2)),
+               cache_lens=[int(x) for x in r.integers(0, cap + 1, batch)])
+    if r.random() < 0.3:
+        cfg["window"] = (int(r.integers(0, 300)), int(r.integers(0, 10)) if r.random() < 0.5 else -1)
+    return cfg, int(r.choice([0, 0, 1, 3]))
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_decode(fa, oracle_mod, seed):
+    cfg, splits = draw_decode(seed)
+    say(f"[random decode {seed}] splits={splits} {cfg}")
+    p = synth.make_decode(seed=60 + seed, **cfg)
+    dev = torch.device("cuda:0")
+    o, lse = fa.forward_kvcache(p.q.to(dev), p.k_cache.to(dev), p.v_cache.to(dev), p.cache_seqlens().to(dev),
+                                causal=p.causal, window_size=(p.window_left, p.window_right),
+                                softmax_scale=p.scale, num_splits=splits)
+    torch.cuda.synchronize()
+    go, gl = o.float().cpu().double().numpy(), lse.cpu().double().numpy()
+    eo = el = 0.0
+    for b in range(p.batch):  # the new tokens against each sequence's valid prefix, bottom-right aligned
+        n = p.cache_lens[b]
+        ro, rl = oracle_mod.attention_fwd(p.q[b:b + 1], p.k_cache[b:b + 1, :n], p.v_cache[b:b + 1, :n],
+                                          scale=p.scale, causal=p.causal, window=(p.window_left, p.window_right))
+        assert np.array_equal(np.isneginf(gl[b]), np.isneginf(rl[0]))
+        eo = max(eo, float(np.abs(go[b] - ro[0]).max()))
+        fin = np.isfinite(rl[0])
+        if fin.any():
+            el = max(el, float(np.abs(gl[b][fin] - rl[0][fin]).max()))
+    say(f"  O {eo:.2e} LSE {el:.2e}")
+    assert eo <= O_TOL[p.dtype] and el <= LSE_TOL
