@@ -274,3 +274,19 @@ def test_kvcache_binding_fails_loudly_without_gpu_tensors():
     kc = torch.zeros(1, 16, 2, 64, dtype=torch.float16)
     with pytest.raises(ValueError, match="GPU"):
         fa.forward_kvcache(q, kc, kc)
+
+
+@no_gpu
+def test_header_compiles_as_c_and_a_c_client_runs(tmp_path, L):
+    """include/fa.h is plain C: a C11 program (gcc, -Wall -Werror) includes it,
+    links libfa.so and gets the documented codes from the argument checks."""
+    import subprocess
+    import exact_tiled_attention_10_amd as fa
+    src = os.path.join(ROOT, "tests", "c_abi", "check_abi.c")
+    exe = str(tmp_path / "check_abi")
+    libdir = os.path.dirname(fa.LIB_PATH)
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"), src,
+                    "-L", libdir, "-l:libfa.so", "-Wl,-rpath," + libdir, "-o", exe], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "all checks passed" in r.stdout
