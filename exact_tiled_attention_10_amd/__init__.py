@@ -244,7 +244,7 @@ def forward_fp8(q, k, v, descale_q=1.0, descale_k=1.0, descale_v=1.0, *, causal=
     bytes as uint8), each tensor's values being its descale times the code's
     value.  Returns (out, lse): O in ``out_dtype`` (bf16 or fp16), LSE float32,
     of the attention of the dequantised inputs with P rounded to E4M3 before
-    P.V (include/fa.h).  head_dim 64 or 128."""
+    P.V (include/fa.h).  head_dim a multiple of 16 up to 128."""
     L = lib()
     args, out, lse = _fp8_args(q, k, v, descale_q, descale_k, descale_v, causal, window_size, softmax_scale,
                                cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, out, lse, out_dtype,

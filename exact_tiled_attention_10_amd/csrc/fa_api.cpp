@@ -146,7 +146,7 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
     int rc = check_common(batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim, causal, window_left,
                           window_right, sc, out_dtype, cu_seqlens_q, cu_seqlens_k);
     if (rc != FA_OK) return rc;
-    if (head_dim != 64 && head_dim != 128) return FA_ERR_UNSUPPORTED;
+    if (head_dim % 16 != 0 || head_dim > 128) return FA_ERR_UNSUPPORTED;  // 16-byte chunks of E4M3 rows
     if (!seqused_ok(seqused_q, seqused_k, cu_seqlens_q)) return FA_ERR_INVALID_ARG;
     const bool has_q = (long long)batch * seqlen_q > 0, has_k = (long long)batch * seqlen_k > 0;
     if ((has_q && (!q || !o || !lse)) || (has_k && (!k || !v))) return FA_ERR_INVALID_ARG;

@@ -36,7 +36,12 @@
 //   the transposing V reads (8 B per lane, 8 rows per 16 lanes) each spread
 //   over distinct bank groups.
 //
-// head_dim is 64 or 128 (the tile width; no columns past it).
+// head_dim is any multiple of 16 up to 128, run in tiles 64 or 128 wide, as
+// the 16-bit forward runs its head dims: rows are head_dim bytes long, the
+// resident Q^T fragments hold zeros past head_dim, the direct loads of K and V
+// fill the chunks past it with a copy of the row's last valid chunk (finite
+// values that only meet those zeros in S and only reach columns of O past
+// head_dim, which are not stored).
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -118,12 +123,13 @@ void fwd_fp8_kernel(Fp8Args a8) {
     const Mask mk{a.causal, a.left, a.right};
     const int hk = h / (a.heads / a.kv_heads);
 
-    const int64_t q_row_stride = (int64_t)a.heads * D;  // bytes
-    const int kv_row_stride = a.kv_heads * D;
-    const uint8_t* qbase = (const uint8_t*)a.q + (s.q_start * a.heads + h) * D;
-    const uint8_t* kbase = (const uint8_t*)a.k + (s.k_start * a.kv_heads + hk) * D;
-    const uint8_t* vbase = (const uint8_t*)a.v + (s.k_start * a.kv_heads + hk) * D;
-    uint16_t* obase = (uint16_t*)a.o + (s.q_start * a.heads + h) * D;
+    const int dh = a.head_dim;  // multiple of 16, at most D
+    const int64_t q_row_stride = (int64_t)a.heads * dh;  // bytes
+    const int kv_row_stride = a.kv_heads * dh;
+    const uint8_t* qbase = (const uint8_t*)a.q + (s.q_start * a.heads + h) * dh;
+    const uint8_t* kbase = (const uint8_t*)a.k + (s.k_start * a.kv_heads + hk) * dh;
+    const uint8_t* vbase = (const uint8_t*)a.v + (s.k_start * a.kv_heads + hk) * dh;
+    uint16_t* obase = (uint16_t*)a.o + (s.q_start * a.heads + h) * dh;
     float* lsebase = a.cu_q ? a.lse + (int64_t)h * a.cu_q[a.batch] + s.q_start
                             : a.lse + ((int64_t)b * a.heads + h) * a.seqlen_q;
 
@@ -148,10 +154,11 @@ void fwd_fp8_kernel(Fp8Args a8) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             u32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+            const int c0 = 64 * ks + 32 * half;  // first byte of this lane's two 16-byte chunks
             if (row < s.len_q) {
-                const uint8_t* src = qbase + (int64_t)row * q_row_stride + 64 * ks + 32 * half;
-                lo = *(const u32x4*)src;
-                hi = *(const u32x4*)(src + 16);
+                const uint8_t* src = qbase + (int64_t)row * q_row_stride + c0;
+                if (c0 < dh) lo = *(const u32x4*)src;
+                if (c0 + 16 < dh) hi = *(const u32x4*)(src + 16);
             }
             qf[ks] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         }
@@ -166,8 +173,9 @@ void fwd_fp8_kernel(Fp8Args a8) {
         const int row = bi * C::kRowsPerBlock + lane / CPR;
         const int slot = lane % CPR;
         dma_row[i] = row;
-        dk_off[i] = row * kv_row_stride + (slot ^ swz_k<CPR>(row)) * 16;
-        dv_off[i] = row * kv_row_stride + (slot ^ swz_v<CPR>(row)) * 16;
+        // chunks past head_dim: the row's last valid chunk again
+        dk_off[i] = row * kv_row_stride + min(slot ^ swz_k<CPR>(row), dh / 16 - 1) * 16;
+        dv_off[i] = row * kv_row_stride + min(slot ^ swz_v<CPR>(row), dh / 16 - 1) * 16;
     }
     // K operand reads: lane (r32, half) reads row 32 kb + r32, chunks 4 ks + 2 half + e.
     int k_rd[KS][2];
@@ -341,7 +349,8 @@ void fwd_fp8_kernel(Fp8Args a8) {
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int col = db * 32 + 8 * g + 4 * half;
+                const int col = db * 32 + 8 * g + 4 * half;  // four columns, all below dh or none
+                if (col >= dh) continue;
                 u32x2 w;
                 w.x = pack2<BF16>(acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv);
                 w.y = pack2<BF16>(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
@@ -366,9 +375,9 @@ int launch_fp8_t(const Fp8Args& a8, hipStream_t stream) {
 
 int launch_fwd_fp8(const Fp8Args& a8, hipStream_t stream) {
     const bool bf16 = a8.f.bf16 != 0;
-    if (a8.f.head_dim == 128) return bf16 ? launch_fp8_t<true, 128>(a8, stream) : launch_fp8_t<false, 128>(a8, stream);
-    if (a8.f.head_dim == 64) return bf16 ? launch_fp8_t<true, 64>(a8, stream) : launch_fp8_t<false, 64>(a8, stream);
-    return 1;
+    // tile width: the smaller of 64, 128 holding head_dim
+    if (a8.f.head_dim > 64) return bf16 ? launch_fp8_t<true, 128>(a8, stream) : launch_fp8_t<false, 128>(a8, stream);
+    return bf16 ? launch_fp8_t<true, 64>(a8, stream) : launch_fp8_t<false, 64>(a8, stream);
 }
 
 }  // namespace fa

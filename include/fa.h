@@ -98,8 +98,8 @@ extern "C" {
 enum fa_status {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, bad scale   */
-    FA_ERR_UNSUPPORTED = 2, /* head_dim not a multiple of 8 in [8, 256] (FP8: not
-                               64 or 128), or dtype                                */
+    FA_ERR_UNSUPPORTED = 2, /* head_dim not a multiple of 8 in [8, 256] (FP8: of 16
+                               in [16, 128]), or dtype                             */
     FA_ERR_ARCH = 3,        /* no HIP device, or the current device is not gfx950 */
     FA_ERR_WORKSPACE = 4,   /* workspace smaller than the *_workspace_size() call */
     FA_ERR_LAUNCH = 5       /* a kernel launch was rejected by the runtime        */
@@ -152,7 +152,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * so |O_ic - exact| <= (2^-4 sum_j P_ij |v_jc| + 2^-14 sum_j |v_jc| / L_i) / l_i
  * plus the score error and the output rounding, L_i being the row's sum of
  * exp(score - max score).
- *   head_dim 64 or 128 (FA_ERR_UNSUPPORTED otherwise); descales finite and
+ *   head_dim a multiple of 16 from 16 to 128 (FA_ERR_UNSUPPORTED otherwise;
+ *   run in tiles 64 or 128 wide); descales finite and
  *   >= 0; no dropout, no backward.  Everything else as for fa_fwd (masks,
  *   GQA, packed and padded batches, empty rows, alignment, errors).
  */

@@ -33,8 +33,8 @@ int main(void) {
            fa_fwd(p, p, p, p, lse, NULL, NULL, NULL, NULL, 1, 4, 2, 128, 128, 128, 1, -1, -1, 0.125f, 1.0f, 0,
                   FA_DTYPE_BF16, NULL),
            FA_ERR_INVALID_ARG);
-    expect("fwd_fp8: head_dim 96",
-           fa_fwd_fp8(p, p, p, p, lse, NULL, NULL, NULL, NULL, 1, 4, 2, 128, 128, 96, 1, -1, -1, 0.125f, 1.0f, 1.0f,
+    expect("fwd_fp8: head_dim 40 (not a multiple of 16)",
+           fa_fwd_fp8(p, p, p, p, lse, NULL, NULL, NULL, NULL, 1, 4, 2, 128, 128, 40, 1, -1, -1, 0.125f, 1.0f, 1.0f,
                       1.0f, FA_DTYPE_BF16, NULL),
            FA_ERR_UNSUPPORTED);
     expect("bwd: workspace too small",

@@ -121,7 +121,8 @@ BAD_FWD8 = [
     (dict(scale=-1.0), INVALID), (dict(scale=1e30, dq=1e30, dk=1e30), INVALID),   # product overflows
     (dict(heads=6, kv_heads=4), INVALID), (dict(causal=3), INVALID), (dict(cu_k=FAKE[10]), INVALID),
     (dict(used_q=FAKE[11], cu_q=FAKE[10], cu_k=FAKE[9]), INVALID),
-    (dict(head_dim=96), UNSUPPORTED), (dict(head_dim=32), UNSUPPORTED), (dict(head_dim=256), UNSUPPORTED),
+    (dict(head_dim=40), UNSUPPORTED), (dict(head_dim=8), UNSUPPORTED), (dict(head_dim=256), UNSUPPORTED),
+    (dict(head_dim=144), UNSUPPORTED),
     (dict(dtype=2), UNSUPPORTED),
 ]
 
@@ -176,6 +177,7 @@ def test_valid_call_without_gfx950_reports_arch(L):
     assert fwd(L, drop=0.1, seed=2**64 - 1) == ARCH and bwd(L, drop=0.999, seed=3) == ARCH
     assert fwd(L, used_q=FAKE[10], used_k=FAKE[11]) == ARCH and bwd(L, used_k=FAKE[11]) == ARCH
     assert fwd8(L) == ARCH and fwd8(L, head_dim=64, dtype=0, dq=0.0) == ARCH
+    assert fwd8(L, head_dim=16) == ARCH and fwd8(L, head_dim=96) == ARCH and fwd8(L, head_dim=112) == ARCH
     # empty tensors may be NULL: no keys, no queries, empty batch
     assert fwd(L, k=None, v=None, seqlen_k=0) == ARCH
     assert fwd(L, q=None, o=None, lse=None, seqlen_q=0) == ARCH

@@ -129,7 +129,7 @@ def check(name, got_o, got_lse, o, lse, bound, lse_bound):
 
 
 @pytest.mark.parametrize("d,causal,heads,kv_heads", [(128, True, 4, 2), (128, False, 2, 2), (64, True, 2, 1),
-                                                     (64, False, 3, 3)])
+                                                     (64, False, 3, 3), (80, True, 2, 2), (32, False, 2, 1)])
 def test_identity_values_show_each_rounded_probability(fa, oracle_mod, d, causal, heads, kv_heads):
     """Nk = d keys and V = I: O_ic is key c's probability for query i."""
     say(f"[fp8 identity] d={d} causal={causal} heads={heads}/{kv_heads}")
@@ -161,6 +161,13 @@ CASES = {
                                factor=3.0), torch.bfloat16),
     "gqa_groups_on_one_xcd_d128": (dict(batch=4, heads=8, kv_heads=2, seqlen=200, head_dim=128, causal=True),
                                    torch.bfloat16),
+    # head dims between the tile widths: zero Q^T past head_dim, clamped tile loads, no stores past it
+    "d16_noncausal": (dict(batch=2, heads=2, kv_heads=1, seqlen=150, head_dim=16, causal=False), torch.bfloat16),
+    "d48_causal_gqa": (dict(batch=1, heads=4, kv_heads=2, seqlen=333, head_dim=48, causal=True), torch.float16),
+    "d96_window": (dict(batch=2, heads=2, kv_heads=2, seqlen=300, head_dim=96, causal=True, window=(90, 0)),
+                   torch.bfloat16),
+    "d112_q_shorter_than_k": (dict(batch=1, heads=3, kv_heads=1, seqlen=120, seqlen_k=290, head_dim=112,
+                                   causal=True), torch.bfloat16),
 }
 
 
@@ -210,13 +217,14 @@ def test_descales(fa):
     assert torch.equal(o4, o1) and torch.equal(l4, l1)
 
 
-def test_empty_and_guard_bands(fa):
+@pytest.mark.parametrize("d", [64, 48])
+def test_empty_and_guard_bands(fa, d):
     dev = torch.device("cuda:0")
-    e = torch.empty(1, 0, 2, 64, dtype=torch.float8_e4m3fn, device=dev)
+    e = torch.empty(1, 0, 2, d, dtype=torch.float8_e4m3fn, device=dev)
     o, lse = fa.forward_fp8(e, e, e, 1.0, 1.0, 1.0)
     torch.cuda.synchronize()
     assert o.numel() == 0 and lse.numel() == 0
-    p = synth.make_problem(dtype="fp8", batch=1, heads=3, kv_heads=1, seqlen=257, head_dim=64, causal=True, seed=45)
+    p = synth.make_problem(dtype="fp8", batch=1, heads=3, kv_heads=1, seqlen=257, head_dim=d, causal=True, seed=45)
     q, k, v = p.q.to(dev), p.k.to(dev), p.v.to(dev)
     pad = 4096
     buf = torch.full((q.numel() + 2 * pad,), 5.0, dtype=torch.bfloat16, device=dev)
