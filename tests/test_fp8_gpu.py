@@ -248,3 +248,30 @@ def test_full_size_workload_sampled(fa, oracle_mod):
     sel = lambda x: x[:, rows][:, :, heads]
     sl = lambda x: x[:, heads][:, :, rows]
     check(name, sel(got_o), sl(got_lse), sel(o), sl(lse), sel(bound), sl(lb))
+
+
+def draw_fp8(seed):
+    r = np.random.default_rng(7000 + seed)
+    kv = int(r.integers(1, 3))
+    cfg = dict(head_dim=int(16 * r.integers(1, 9)), heads=kv * int(r.choice([1, 2, 4])), kv_heads=kv,
+               causal=bool(r.integers(0, 2)))
+    if r.random() < 0.3:
+        cfg["window"] = (int(r.integers(0, 150)), int(r.integers(0, 40)) if r.random() < 0.5 else -1)
+    if r.random() < 0.3:
+        cfg.update(batch=0, seqlen=0, seqlens=[int(x) for x in r.integers(1, 260, int(r.integers(1, 4)))])
+    else:
+        cfg.update(batch=int(r.integers(1, 3)), seqlen=int(r.integers(1, 300)))
+        if r.random() < 0.4:
+            cfg["seqlen_k"] = int(r.integers(1, 300))
+    return cfg, (torch.bfloat16 if r.random() < 0.5 else torch.float16)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_fp8(fa, oracle_mod, seed):
+    """Seeded random shapes, masks and layouts, against the derived bound."""
+    cfg, out_dtype = draw_fp8(seed)
+    say(f"[fp8 random {seed}] {cfg}")
+    p = synth.make_problem(dtype="fp8", seed=80 + seed, **cfg)
+    got_o, got_lse = run_gpu(fa, p, out_dtype)
+    o, lse, bound, lb = reference_and_bound(oracle_mod, p, out_dtype)
+    check(f"random {seed}", got_o, got_lse, o, lse, bound, lb)
