@@ -21,6 +21,9 @@ Subcommands (run from anywhere; the repository root is found from this file):
           hash still matches).
   trace   --db FILE --title T --command C
           Print a markdown table of a rocprofv3 kernel-trace database.
+  util    --prefix P [--kernels fwd,dkdv,dq,fwd_fp8]
+          Print a utilisation table from two counter passes per kernel
+          (directories P_<kernel>_1 and P_<kernel>_2, see profiles/).
 """
 from __future__ import annotations
 
@@ -207,6 +210,44 @@ def _traffic(args):
     print(json.dumps(data["kernels"][args.kernel], indent=1))
 
 
+def _counters_mean(run_dir: str, name_sub: str) -> dict:
+    """Mean per dispatch of every counter rocprofv3 recorded for kernels whose
+    name contains name_sub (fwd_kernel excludes the FP8 forward)."""
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    tot, disp = defaultdict(float), defaultdict(set)
+    for path in files:
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                kn = r["Kernel_Name"]
+                if name_sub not in kn or (name_sub == "fwd_kernel" and "fp8" in kn):
+                    continue
+                tot[r["Counter_Name"]] += float(r["Counter_Value"])
+                disp[r["Counter_Name"]].add(r["Dispatch_Id"])
+    return {c: tot[c] / len(disp[c]) for c in tot}
+
+
+# gfx950: 8 XCDs of 32 CUs with 4 SIMDs each
+_XCDS, _SIMDS = 8, 1024
+
+
+def _util(args):
+    """Utilisation table from two counter passes per kernel (run directories
+    <prefix>_<kernel>_1 and _2)."""
+    rows = ["| kernel | clock cycles per XCD | matrix cores busy | VALU and MFMA co-issue | "
+            "waves waiting | LDS instructions | LDS bank-conflict cycles |",
+            "|---|---|---|---|---|---|---|"]
+    for k in args.kernels.split(","):
+        c = _counters_mean(f"{args.prefix}_{k}_1", KERNEL_NAMES[k])
+        c.update(_counters_mean(f"{args.prefix}_{k}_2", KERNEL_NAMES[k]))
+        simd_cycles = c["GRBM_GUI_ACTIVE"] / _XCDS * _SIMDS
+        busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / simd_cycles
+        coex = c["SQ_VALU_MFMA_COEXEC_CYCLES"] / simd_cycles
+        wait = c["SQ_WAIT_ANY"] / c["SQ_WAVE_CYCLES"]
+        rows.append(f"| {k} | {c['GRBM_GUI_ACTIVE'] / _XCDS:.3g} | {100 * busy:.1f}% | {100 * coex:.1f}% | "
+                    f"{100 * wait:.1f}% | {c['SQ_INSTS_LDS']:.3g} | {c['SQ_LDS_BANK_CONFLICT']:.0f} |")
+    print("\n".join(rows))
+
+
 def _trace(args):
     c = sqlite3.connect(args.db)
     rows = list(c.execute("select name, total_calls, total_duration, average, percentage from top_kernels"))
@@ -260,6 +301,9 @@ def main(argv=None):
     for a in ("--fetch", "--write", "--copy-fetch", "--copy-write"):
         t.add_argument(a, required=True)
     t.add_argument("--mib", type=int, default=1024)
+    u = sub.add_parser("util")
+    u.add_argument("--prefix", required=True, help="counter run directories <prefix>_<kernel>_1 and _2")
+    u.add_argument("--kernels", default="fwd,dkdv,dq,fwd_fp8")
     tr = sub.add_parser("trace")
     tr.add_argument("--db", required=True)
     tr.add_argument("--title", required=True)
@@ -267,7 +311,7 @@ def main(argv=None):
     tr.add_argument("--last", type=int, default=5)
     tr.add_argument("--bench-log", default=None)
     args = ap.parse_args(argv)
-    {"run": _run, "copy": _copy, "traffic": _traffic, "trace": _trace}[args.cmd](args)
+    {"run": _run, "copy": _copy, "traffic": _traffic, "trace": _trace, "util": _util}[args.cmd](args)
 
 
 if __name__ == "__main__":
