@@ -38,6 +38,8 @@ int check_common(int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
     if (cu_q && (!aligned(cu_q, 4) || !aligned(cu_k, 4))) return FA_ERR_INVALID_ARG;
     // indices are 32-bit inside a sequence, 64-bit across the batch
     if ((long long)batch * heads > (1LL << 31) - 1) return FA_ERR_INVALID_ARG;
+    // byte offsets inside a tile (up to 256 rows of heads * head_dim 16-bit values) are 32-bit
+    if ((long long)heads * head_dim >= (1LL << 23)) return FA_ERR_INVALID_ARG;
     if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
     if (!head_dim_ok(head_dim)) return FA_ERR_UNSUPPORTED;
     return FA_OK;

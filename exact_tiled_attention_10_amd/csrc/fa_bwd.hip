@@ -108,12 +108,13 @@ struct TileDma {
     // relative to g (rows beyond are clamped); tail: whether clamping applies.
     __device__ __forceinline__ void issue(const uint16_t* g, uint16_t* tile, int wave, int stride,
                                           bool tail, int last) const {
+        const rsrc_t src = buffer_of(g);
 #pragma unroll
         for (int i = 0; i < kPerWave; ++i) {
             const int r = row0 + i * kRowsPerBlock;
             const int rg = tail && r > last ? last : r;
             const int off = rg * stride + min(slot ^ swz<CPR>(r), last_chunk) * 8;
-            dma16(g + off, tile + (wave * kPerWave + i) * 512);
+            dma16(src, (uint32_t)off * 2u, tile + (wave * kPerWave + i) * 512);
         }
     }
 };
@@ -443,8 +444,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
             const int arr = wave / kRowLoads, part = wave % kRowLoads;
             const int64_t idx0 = a.cu_q ? (int64_t)h * total_q + s.q_start + row0
                                         : ((int64_t)b * a.heads + h) * a.seqlen_q + row0;
-            const float* src = (arr == 0 ? a.lse2 : a.dsum) + idx0 + min(64 * part + lane, last);
-            dma4(src, lse_lds(buf) + arr * BMR + 64 * part);
+            const float* src = (arr == 0 ? a.lse2 : a.dsum) + idx0;
+            dma4(buffer_of(src), (uint32_t)min(64 * part + lane, last) * 4u, lse_lds(buf) + arr * BMR + 64 * part);
         }
     };
 

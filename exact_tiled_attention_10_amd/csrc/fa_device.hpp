@@ -123,14 +123,28 @@ __device__ __forceinline__ int swz(int row) {
     else return ((row & 3) << 1) | ((row >> 2) & 1);
 }
 
-// One direct load: each lane moves 16 bytes from `gsrc` to lds_dst + 16 * lane
-// (lds_dst must be the same for the whole wave).
-__device__ __forceinline__ void dma16(const void* gsrc, void* lds_dst) {
-    __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+// Direct loads go through a buffer resource (wave-uniform base address in
+// scalar registers, a 32-bit byte offset per lane), not global_load_lds: the
+// compiler takes an outstanding global_load_lds as a flat access that may
+// also touch LDS, and while one is in flight it turns every LDS wait into a
+// wait for all outstanding LDS reads, so operand reads issued ahead of their
+// MFMAs would be waited for at once.  The buffer form leaves those waits
+// exact.  Raw addressing (stride 0), no range limit (num_records at its
+// maximum), 32-bit data format (a zero format would read zeros).
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+__device__ __forceinline__ rsrc_t buffer_of(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
+}
+// One direct load: each lane moves 16 bytes from src + byte_off to
+// lds_dst + 16 * lane (lds_dst must be the same for the whole wave).
+__device__ __forceinline__ void dma16(rsrc_t src, uint32_t byte_off, void* lds_dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, byte_off,
+                                             0, 0, 0);
 }
 // Same with 4 bytes per lane (256 B per instruction).
-__device__ __forceinline__ void dma4(const void* gsrc, void* lds_dst) {
-    __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_dst, 4, 0, 0);
+__device__ __forceinline__ void dma4(rsrc_t src, uint32_t byte_off, void* lds_dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 4, byte_off,
+                                             0, 0, 0);
 }
 
 // s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt left at their

@@ -174,15 +174,14 @@ void fwd_kernel(FwdArgs a) {
         const int last = s.len_k - 1 - key0;
         const int64_t tile_off = (int64_t)key0 * kv_row_stride;
         uint16_t* kl = stage(buf);
+        const rsrc_t ksrc = buffer_of(kbase + tile_off), vsrc = buffer_of(vbase + tile_off);
 #pragma unroll
         for (int i = 0; i < C::kDmaPerWave; ++i) {
             int off = dma_goff[i];
             if (tail && dma_row[i] > last) off += (last - dma_row[i]) * kv_row_stride;  // clamp to the last key
             uint16_t* dst = kl + (wave * C::kDmaPerWave + i) * 512;
-            __builtin_amdgcn_global_load_lds((const void*)(kbase + tile_off + off),
-                                             (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void*)(vbase + tile_off + off),
-                                             (__attribute__((address_space(3))) void*)(dst + C::tileElems), 16, 0, 0);
+            dma16(ksrc, (uint32_t)off * 2u, dst);
+            dma16(vsrc, (uint32_t)off * 2u, dst + C::tileElems);
         }
     };
 

@@ -213,6 +213,7 @@ void fwd_fp8_kernel(Fp8Args a8) {
         const int last = s.len_k - 1 - key0;
         const int64_t tile_off = (int64_t)key0 * kv_row_stride;
         uint8_t* kl = stage(buf);
+        const rsrc_t ksrc = buffer_of(kbase + tile_off), vsrc = buffer_of(vbase + tile_off);
 #pragma unroll
         for (int i = 0; i < C::kDmaPerWave; ++i) {
             int ok = dk_off[i], ov = dv_off[i];
@@ -222,8 +223,8 @@ void fwd_fp8_kernel(Fp8Args a8) {
                 ov += adj;
             }
             uint8_t* dst = kl + (wave * C::kDmaPerWave + i) * 1024;
-            dma16(kbase + tile_off + ok, dst);
-            dma16(vbase + tile_off + ov, dst + C::tileBytes);
+            dma16(ksrc, (uint32_t)ok, dst);
+            dma16(vsrc, (uint32_t)ov, dst + C::tileBytes);
         }
     };
 

@@ -46,6 +46,9 @@
  *   (window_right < 0 or j <= p + window_right).
  * A row with no visible key gets O = 0 and LSE = -inf (and zero gradient).
  * GQA / MQA: query head h reads kv head h / (heads / kv_heads).
+ * Sizes: heads * head_dim must stay below 2^23 (offsets inside a tile of up
+ * to 256 rows are 32-bit) and batch * heads below 2^31; FA_ERR_INVALID_ARG
+ * otherwise.
  *
  * LSE[i] = ln(sum over visible j of exp(softmax_scale * q_i . k_j)).
  *
