@@ -91,6 +91,7 @@ BAD_FWD = [
     (dict(drop=-0.1), INVALID), (dict(drop=1.0), INVALID), (dict(drop=float("nan")), INVALID),
     (dict(used_q=FAKE[11], cu_q=FAKE[10], cu_k=FAKE[9]), INVALID),   # padded lengths with a packed batch
     (dict(used_k=ctypes.c_void_p(0x10002)), INVALID),                # misaligned
+    (dict(heads=1 << 16, kv_heads=2), INVALID),  # heads x head_dim = 2^23: tile offsets past 32 bits
     (dict(head_dim=100), UNSUPPORTED), (dict(head_dim=264), UNSUPPORTED), (dict(head_dim=0), UNSUPPORTED),
     (dict(head_dim=252), UNSUPPORTED), (dict(head_dim=4), UNSUPPORTED), (dict(head_dim=-8), UNSUPPORTED),
     (dict(head_dim=512), UNSUPPORTED),
@@ -121,6 +122,7 @@ BAD_FWD8 = [
     (dict(scale=-1.0), INVALID), (dict(scale=1e30, dq=1e30, dk=1e30), INVALID),   # product overflows
     (dict(heads=6, kv_heads=4), INVALID), (dict(causal=3), INVALID), (dict(cu_k=FAKE[10]), INVALID),
     (dict(used_q=FAKE[11], cu_q=FAKE[10], cu_k=FAKE[9]), INVALID),
+    (dict(heads=1 << 16, kv_heads=2), INVALID),
     (dict(head_dim=40), UNSUPPORTED), (dict(head_dim=8), UNSUPPORTED), (dict(head_dim=256), UNSUPPORTED),
     (dict(head_dim=144), UNSUPPORTED),
     (dict(dtype=2), UNSUPPORTED),
@@ -137,6 +139,7 @@ BAD_BWD = [
     (dict(dv=None), INVALID), (dict(ws=None), INVALID),
     (dict(dv=ctypes.c_void_p(0x10004)), INVALID),
     (dict(heads=3, kv_heads=2), INVALID), (dict(head_dim=36), UNSUPPORTED),
+    (dict(heads=1 << 16, kv_heads=2), INVALID),
     (dict(wsb=2 * 4 * 4 * 128 - 4), WORKSPACE), (dict(wsb=0), WORKSPACE),
     (dict(drop=1.5), INVALID), (dict(drop=float("inf")), INVALID),
 ]
@@ -182,6 +185,9 @@ def test_valid_call_without_gfx950_reports_arch(L):
     assert fwd(L, k=None, v=None, seqlen_k=0) == ARCH
     assert fwd(L, q=None, o=None, lse=None, seqlen_q=0) == ARCH
     assert bwd(L, k=None, v=None, dk=None, dv=None, seqlen_k=0) == ARCH
+    # just below the tile-offset bound on heads x head_dim (2^23)
+    assert fwd(L, heads=(1 << 16) - 2, kv_heads=2) == ARCH
+    assert bwd(L, heads=(1 << 16) - 2, kv_heads=2, wsb=1 << 40) == ARCH
 
 
 def test_null_pointers_only_for_empty_tensors(L):
