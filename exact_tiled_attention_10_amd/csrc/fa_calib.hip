@@ -1,9 +1,13 @@
-// Calibration kernel for the HBM byte counters: a plain streaming copy of a
-// known number of bytes, with the same 16-byte-per-lane loads and stores of
-// whole 128-byte lines that the attention kernels issue.  Built into its own
-// small library (libfacalib.so), outside the attention interface; the
-// profiling entry point runs it under `rocprofv3 --pmc` to learn how many
-// bytes the read and write counters report per byte moved.
+// Calibration kernels for the hardware counters, built into their own small
+// library (libfacalib.so), outside the attention interface; the profiling
+// entry point runs them under `rocprofv3 --pmc`.
+//  * HBM: a plain streaming copy of a known number of bytes, with the same
+//    16-byte-per-lane loads and stores of whole 128-byte lines that the
+//    attention kernels issue, to learn how many bytes the read and write
+//    counters report per byte moved.
+//  * LDS: conflict-free LDS reads of a known number of bytes, as many as the
+//    CUs can serve, to learn the unit of the LDS activity counter and the read
+//    bandwidth the LDS sustains.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -26,6 +30,37 @@ __global__ __launch_bounds__(64) void calib_copy_kernel(const u32x4* __restrict_
     }
 }
 
+// Each wave reads 1 KiB of LDS per step (64 lanes x 16 bytes, or two
+// transposing reads of 64 x 8 bytes), 8 steps per iteration, over 64 blocks of
+// 1 KiB; 512 threads and 64 KiB of LDS per workgroup.
+template <bool TR>
+__global__ __launch_bounds__(512) void calib_lds_kernel(uint32_t* __restrict__ out, int iters) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[65536];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    for (int i = t; i < 65536 / 16; i += 512) ((u32x4*)lds)[i] = u32x4{(uint32_t)i, i * 3u, i * 5u, i * 7u};
+    __syncthreads();
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int blk = (it * 8 + u + w * 3) & 63;
+            if constexpr (!TR) {
+                acc ^= *(const u32x4*)(lds + blk * 1024 + lane * 16);
+            } else {
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + blk * 1024 + lane * 8));
+                const s16x4 hi =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + blk * 1024 + 512 + lane * 8));
+                const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+                acc ^= u32x4{l2.x, l2.y, h2.x, h2.y};
+            }
+        }
+    }
+    out[(int64_t)blockIdx.x * 512 + t] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -38,6 +73,19 @@ int fa_calib_copy(const void* src, void* dst, size_t bytes, int waves, void* str
     const int64_t per_wave = (int64_t)(bytes / 16 / (size_t)waves);
     hipLaunchKernelGGL(calib_copy_kernel, dim3(waves), dim3(64), 0, (hipStream_t)stream,
                        (const u32x4*)src, (u32x4*)dst, per_wave);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// Reads workgroups * 8 waves * iters * 8 KiB from LDS (b128 reads, or
+// transposing b64 reads when `transposing` is 1); out (device) receives
+// workgroups * 512 uint32.  Returns 0 when the launch was accepted, 1 for bad
+// arguments, 2 for a failed launch.
+int fa_calib_lds(uint32_t* out, int workgroups, int iters, int transposing, void* stream) {
+    if (!out || workgroups < 1 || iters < 1 || (transposing != 0 && transposing != 1)) return 1;
+    if (transposing)
+        hipLaunchKernelGGL(calib_lds_kernel<true>, dim3(workgroups), dim3(512), 0, (hipStream_t)stream, out, iters);
+    else
+        hipLaunchKernelGGL(calib_lds_kernel<false>, dim3(workgroups), dim3(512), 0, (hipStream_t)stream, out, iters);
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 

@@ -11,6 +11,13 @@ Subcommands (run from anywhere; the repository root is found from this file):
           Run the calibration copy (libfacalib.so: read M MiB, write M MiB with
           16-byte-per-lane loads and stores of whole lines, as the attention
           kernels do) N times: the reference for the HBM byte counters.
+  lds     [--workgroups G] [--iters N]
+          Run the LDS calibration (libfacalib.so: conflict-free LDS reads of a
+          known number of bytes, b128 reads, then transposing b64 reads) and
+          print their times: the reference for the LDS activity counter.
+  ldscal  --dir DIR [--workgroups G] [--iters N]
+          From a `rocprofv3 --pmc SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS GRBM_GUI_ACTIVE`
+          run of `lds`, print bytes per counter unit and bytes per clock per CU.
   traffic --workload W --kernel K --fetch DIR --write DIR --copy-fetch DIR
           --copy-write DIR [--mib M]
           Read the counter CSVs of four `rocprofv3 --pmc` runs (FETCH_SIZE and
@@ -156,6 +163,53 @@ def _copy(args):
     print(f"copied {args.mib} MiB x{args.iters}", flush=True)
 
 
+LDS_NAME = "calib_lds_kernel"
+_LDS_WAVE_STEP_BYTES = 1024  # bytes one wave reads per step of the LDS calibration
+
+
+def _lds_bytes(workgroups: int, iters: int) -> int:
+    return workgroups * 8 * iters * 8 * _LDS_WAVE_STEP_BYTES
+
+
+def _lds(args):
+    import ctypes
+    import torch
+    if not os.path.exists(CALIB_LIB):
+        raise RuntimeError(f"{CALIB_LIB} is not built; run `python -m exact_tiled_attention_10_amd.build`")
+    L = ctypes.CDLL(CALIB_LIB)
+    L.fa_calib_lds.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    L.fa_calib_lds.restype = ctypes.c_int
+    out = torch.empty(args.workgroups * 512, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    for tr in (0, 1):
+        for rep in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            rc = L.fa_calib_lds(ctypes.c_void_p(out.data_ptr()), args.workgroups, args.iters, tr,
+                                ctypes.c_void_p(stream.cuda_stream))
+            e1.record(stream)
+            if rc != 0:
+                raise RuntimeError(f"fa_calib_lds returned {rc}")
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            nb = _lds_bytes(args.workgroups, args.iters)
+            print(f"lds {'transposing b64' if tr else 'b128'} run {rep}: {ms:.3f} ms, "
+                  f"{nb / ms / 1e9:.1f} TB/s", flush=True)
+
+
+def _ldscal(args):
+    """Bytes per SQ_LDS_IDX_ACTIVE unit and LDS read bandwidth per CU and clock,
+    per dispatch of the LDS calibration."""
+    nb = _lds_bytes(args.workgroups, args.iters)
+    idx = _counter_per_dispatch(args.dir, LDS_NAME, "SQ_LDS_IDX_ACTIVE")
+    gui = _counter_per_dispatch(args.dir, LDS_NAME, "GRBM_GUI_ACTIVE")
+    ins = _counter_per_dispatch(args.dir, LDS_NAME, "SQ_INSTS_LDS")
+    for i, (a, g, n) in enumerate(zip(idx, gui, ins)):
+        cyc = g / _XCDS
+        print(f"dispatch {i}: {nb / a:.1f} bytes per SQ_LDS_IDX_ACTIVE unit, {nb / n:.0f} bytes per LDS "
+              f"instruction, {nb / cyc / _CUS:.1f} bytes per clock per CU ({cyc:.3g} cycles per XCD)")
+
+
 def _counter_per_dispatch(run_dir: str, name_sub: str, counter: str) -> list:
     """Per-dispatch values (summed over the rows rocprofv3 reports for one
     dispatch) of `counter` for kernels whose name contains name_sub."""
@@ -227,15 +281,18 @@ def _counters_mean(run_dir: str, name_sub: str) -> dict:
 
 
 # gfx950: 8 XCDs of 32 CUs with 4 SIMDs each
-_XCDS, _SIMDS = 8, 1024
+_XCDS, _SIMDS, _CUS = 8, 1024, 256
+# SQ_LDS_IDX_ACTIVE advances once per 256 bytes of LDS reads (the LDS
+# calibration above), i.e. it counts cycles of the LDS at its full width.
+_LDS_BYTES_PER_UNIT = 256
 
 
 def _util(args):
     """Utilisation table from two counter passes per kernel (run directories
     <prefix>_<kernel>_1 and _2)."""
     rows = ["| kernel | clock cycles per XCD | matrix cores busy | VALU and MFMA co-issue | "
-            "waves waiting | LDS instructions | LDS bank-conflict cycles |",
-            "|---|---|---|---|---|---|---|"]
+            "waves waiting | LDS instructions | LDS bank-conflict cycles | LDS busy |",
+            "|---|---|---|---|---|---|---|---|"]
     for k in args.kernels.split(","):
         c = _counters_mean(f"{args.prefix}_{k}_1", KERNEL_NAMES[k])
         c.update(_counters_mean(f"{args.prefix}_{k}_2", KERNEL_NAMES[k]))
@@ -243,8 +300,10 @@ def _util(args):
         busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / simd_cycles
         coex = c["SQ_VALU_MFMA_COEXEC_CYCLES"] / simd_cycles
         wait = c["SQ_WAIT_ANY"] / c["SQ_WAVE_CYCLES"]
+        lds = c["SQ_LDS_IDX_ACTIVE"] / (c["GRBM_GUI_ACTIVE"] / _XCDS * _CUS)
         rows.append(f"| {k} | {c['GRBM_GUI_ACTIVE'] / _XCDS:.3g} | {100 * busy:.1f}% | {100 * coex:.1f}% | "
-                    f"{100 * wait:.1f}% | {c['SQ_INSTS_LDS']:.3g} | {c['SQ_LDS_BANK_CONFLICT']:.0f} |")
+                    f"{100 * wait:.1f}% | {c['SQ_INSTS_LDS']:.3g} | {c['SQ_LDS_BANK_CONFLICT']:.0f} | "
+                    f"{100 * lds:.1f}% |")
     print("\n".join(rows))
 
 
@@ -295,6 +354,13 @@ def main(argv=None):
     cp = sub.add_parser("copy")
     cp.add_argument("--mib", type=int, default=1024)
     cp.add_argument("--iters", type=int, default=3)
+    ld = sub.add_parser("lds")
+    ld.add_argument("--workgroups", type=int, default=512)
+    ld.add_argument("--iters", type=int, default=4096)
+    lc = sub.add_parser("ldscal")
+    lc.add_argument("--dir", required=True)
+    lc.add_argument("--workgroups", type=int, default=512)
+    lc.add_argument("--iters", type=int, default=4096)
     t = sub.add_parser("traffic")
     t.add_argument("--workload", required=True)
     t.add_argument("--kernel", required=True, choices=list(KERNEL_NAMES))
@@ -311,7 +377,8 @@ def main(argv=None):
     tr.add_argument("--last", type=int, default=5)
     tr.add_argument("--bench-log", default=None)
     args = ap.parse_args(argv)
-    {"run": _run, "copy": _copy, "traffic": _traffic, "trace": _trace, "util": _util}[args.cmd](args)
+    {"run": _run, "copy": _copy, "lds": _lds, "ldscal": _ldscal, "traffic": _traffic, "trace": _trace,
+     "util": _util}[args.cmd](args)
 
 
 if __name__ == "__main__":
