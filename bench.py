@@ -186,7 +186,7 @@ def main():
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (default min(16, cores))")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+        print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr, flush=True)
         sys.exit(2)
 
