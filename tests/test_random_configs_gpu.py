@@ -234,3 +234,30 @@ def test_single_visible_key(fa, oracle_mod, dtype, head_dim, layout):
     gq, gk = rn(g(dq)), rn(g(dk))
     say(f"  max |dQ_i| / bound {np.max(gq / bq):.2e}, max |dK_i| / bound {np.max(gk / bk):.2e}")
     assert np.all(gq <= bq) and np.all(gk <= bk)
+
+
+def test_many_heads_wide_rows(fa, oracle_mod):
+    """2048 query heads over 512 kv heads at head_dim 256: a token row is 1 MiB
+    of queries, so the direct loads of a tile reach tens of MiB past its base
+    (32-bit offsets).  130 tokens span several tiles with a ragged tail; the
+    oracle checks the first and the last kv-head group (4 query heads each,
+    complete GQA groups, so their dK and dV are fully determined)."""
+    p = synth.make_problem(dtype="bf16", batch=1, heads=2048, kv_heads=512, seqlen=130, head_dim=256,
+                           causal=True, seed=17)
+    say("[many heads] bf16 b1 h2048 kv512 n130 d256 causal")
+    dev = torch.device("cuda:0")
+    q, k, v, do = (t.to(dev) for t in (p.q, p.k, p.v, p.do))
+    o, lse = fa.forward(q, k, v, causal=True, softmax_scale=p.scale)
+    dq, dk, dv = fa.backward(do, q, k, v, o, lse, causal=True, softmax_scale=p.scale)
+    torch.cuda.synchronize()
+    g = lambda t: t.float().cpu().double().numpy()
+    for hs, ks in ((slice(0, 4), slice(0, 1)), (slice(2044, 2048), slice(511, 512))):
+        rdq, rdk, rdv, ro, rlse = oracle_mod.attention_bwd(p.q[:, :, hs], p.k[:, :, ks], p.v[:, :, ks],
+                                                           p.do[:, :, hs], scale=p.scale, causal=True, threads=16)
+        eo = float(np.abs(g(o[:, :, hs]) - ro).max())
+        el = float(np.abs(lse[:, hs].cpu().double().numpy() - rlse).max())
+        errs = {n: rel_l2(g(x), r) for n, x, r in (("dq", dq[:, :, hs], rdq), ("dk", dk[:, :, ks], rdk),
+                                                   ("dv", dv[:, :, ks], rdv))}
+        say(f"  heads {hs.start}..{hs.stop - 1}: O {eo:.2e} LSE {el:.2e} " +
+            " ".join(f"{n} {e:.2e}" for n, e in errs.items()))
+        assert eo <= O_TOL["bf16"] and el <= LSE_TOL and all(e <= GRAD_TOL for e in errs.values())
