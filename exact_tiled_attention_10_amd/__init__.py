@@ -54,11 +54,11 @@ def lib() -> ctypes.CDLL:
     U64 = ctypes.c_uint64
     L.fa_fwd.argtypes = [P] * 9 + [I] * 9 + [F, F, U64, I, P]
     L.fa_fwd.restype = I
-    L.fa_bwd_workspace_size.argtypes = [I] * 5
+    L.fa_bwd_workspace_size.argtypes = [I] * 6
     L.fa_bwd_workspace_size.restype = S
-    L.fa_bwd.argtypes = [P] * 10 + [S] + [P] * 4 + [I] * 9 + [F, F, U64, I, P]
+    L.fa_bwd.argtypes = [P] * 10 + [S] + [P] * 4 + [I] * 9 + [F, F, U64, I, I, P]
     L.fa_bwd.restype = I
-    L.fa_bwd_stage.argtypes = [I] + [P] * 10 + [S] + [P] * 4 + [I] * 9 + [F, F, U64, I, P]
+    L.fa_bwd_stage.argtypes = [I] + [P] * 10 + [S] + [P] * 4 + [I] * 9 + [F, F, U64, I, I, P]
     L.fa_bwd_stage.restype = I
     L.fa_fwd_fp8.argtypes = [P] * 9 + [I] * 9 + [F, F, F, F, I, P]
     L.fa_fwd_fp8.restype = I
@@ -122,6 +122,13 @@ class _Geom:
             self.batch = cu_q.numel() - 1
             _, self.heads, self.d = q.shape
             _, self.kv_heads, dk = k.shape
+            # the kernels index rows (and LSE) by the prefix sums: the query-side
+            # tensors must hold exactly cu_seqlens_q[-1] rows, k / v at least cu_seqlens_k[-1]
+            ends = torch.stack([cu_q[-1], cu_k[-1]]).cpu().tolist()
+            if ends[0] != q.shape[0]:
+                raise ValueError(f"q holds {q.shape[0]} rows but cu_seqlens_q[-1] = {ends[0]}")
+            if ends[1] > k.shape[0]:
+                raise ValueError(f"k holds {k.shape[0]} rows but cu_seqlens_k[-1] = {ends[1]}")
             if max_q is None:
                 max_q = int((cu_q[1:] - cu_q[:-1]).max().item()) if self.batch else 0
             if max_k is None:
@@ -182,10 +189,14 @@ def forward(q, k, v, *, causal=False, window_size=(-1, -1), softmax_scale=None,
         out = torch.empty_like(q)
     else:
         _check(out, "out", dt, q.device)
+        if out.shape != q.shape:
+            raise ValueError("out must have the shape of q")
     if lse is None:
         lse = torch.empty(g.lse_shape, dtype=torch.float32, device=q.device)
     else:
         _check(lse, "lse", torch.float32, q.device)
+        if tuple(lse.shape) != g.lse_shape:
+            raise ValueError(f"lse must have shape {g.lse_shape}")
     rc = L.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                   _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(seqused_q), _ptr(seqused_k),
                   g.batch, g.heads, g.kv_heads, g.seqlen_q, g.seqlen_k, g.d,
@@ -227,6 +238,8 @@ def _fp8_args(q, k, v, descale_q, descale_k, descale_v, causal, window_size, sof
         lse = torch.empty(g.lse_shape, dtype=torch.float32, device=q.device)
     else:
         _check(lse, "lse", torch.float32, q.device)
+        if tuple(lse.shape) != g.lse_shape:
+            raise ValueError(f"lse must have shape {g.lse_shape}")
     args = [_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
             _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(seqused_q), _ptr(seqused_k),
             g.batch, g.heads, g.kv_heads, g.seqlen_q, g.seqlen_k, g.d,
@@ -276,17 +289,23 @@ class Fp8Plan:
             raise FaError(rc, "fa_fwd_fp8")
 
 
-def workspace_size(batch, heads, seqlen_q, head_dim, dtype) -> int:
+def workspace_size(batch, heads, seqlen_q, head_dim, dtype, deterministic=True) -> int:
     code = dtype if isinstance(dtype, int) else (FA_DTYPE_BF16 if dtype == torch.bfloat16 else FA_DTYPE_F16)
-    return int(lib().fa_bwd_workspace_size(batch, heads, seqlen_q, head_dim, code))
+    return int(lib().fa_bwd_workspace_size(batch, heads, seqlen_q, head_dim, code, int(bool(deterministic))))
 
 
 def backward(dout, q, k, v, out, lse, *, causal=False, window_size=(-1, -1),
              softmax_scale=None, cu_seqlens_q=None, cu_seqlens_k=None,
              max_seqlen_q=None, max_seqlen_k=None, dq=None, dk=None, dv=None,
-             workspace=None, dropout_p=0.0, dropout_seed=0, seqused_q=None, seqused_k=None):
+             workspace=None, dropout_p=0.0, dropout_seed=0, seqused_q=None, seqused_k=None,
+             deterministic=True):
     """dQ, dK, dV of exact attention for upstream gradient ``dout``, from the
-    forward's ``out`` and ``lse`` (recomputing the scores)."""
+    forward's ``out`` and ``lse`` (recomputing the scores).  By default
+    (``deterministic=True``) dQ comes from the separate dQ pass and every call
+    gives the same bytes; ``deterministic=False`` lets head dims up to 128
+    accumulate dQ with float32 atomics inside the key-tile pass instead (its
+    last bits then vary from call to call; slower on MI355X, whose L2 float
+    atomics are the bottleneck there).  See include/fa.h."""
     L = lib()
     dt = q.dtype
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
@@ -296,6 +315,14 @@ def backward(dout, q, k, v, out, lse, *, causal=False, window_size=(-1, -1),
         _check(cu_seqlens_q, "cu_seqlens_q", torch.int32, q.device)
         _check(cu_seqlens_k, "cu_seqlens_k", torch.int32, q.device)
     g = _Geom(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    if k.shape != v.shape:
+        raise ValueError("k and v shapes differ")
+    for name, t in (("out", out), ("dout", dout)):
+        if t.shape != q.shape:
+            raise ValueError(f"{name} must have the shape of q")
+    if tuple(lse.shape) != g.lse_shape:
+        raise ValueError(f"lse must have shape {g.lse_shape}")
+    det = int(bool(deterministic))
     _check_used(seqused_q, "seqused_q", g.batch, q.device)
     _check_used(seqused_k, "seqused_k", g.batch, q.device)
     dq = torch.empty_like(q) if dq is None else dq
@@ -305,16 +332,16 @@ def backward(dout, q, k, v, out, lse, *, causal=False, window_size=(-1, -1),
         _check(t, name, dt, q.device)
         if t.shape != like.shape:
             raise ValueError(f"{name} must have the shape of its input")
-    need = int(L.fa_bwd_workspace_size(g.batch, g.heads, g.seqlen_q, g.d, _dtype_code(q)))
+    need = int(L.fa_bwd_workspace_size(g.batch, g.heads, g.seqlen_q, g.d, _dtype_code(q), det))
     if workspace is None:
-        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     rc = L.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
                   _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
                   _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(seqused_q), _ptr(seqused_k),
                   g.batch, g.heads, g.kv_heads, g.seqlen_q, g.seqlen_k, g.d,
                   int(bool(causal)), int(window_size[0]), int(window_size[1]),
                   _default_scale(g.d, softmax_scale), float(dropout_p), _seed(dropout_seed),
-                  _dtype_code(q), _stream(q.device))
+                  _dtype_code(q), det, _stream(q.device))
     if rc != 0:
         raise FaError(rc, "fa_bwd")
     return dq, dk, dv
@@ -324,11 +351,12 @@ class Plan:
     """Pre-resolved C-ABI arguments for repeated calls on fixed buffers (the
     benchmark loop): ``fwd()`` runs fa_fwd, ``bwd_stage(s)`` one backward
     kernel, ``bwd()`` all three, each enqueued on ``stream`` (default: the
-    current torch stream of q's device).  Buffers are allocated once here."""
+    current torch stream of q's device).  Buffers are allocated once here.
+    ``deterministic`` selects the backward's dQ path as in ``backward``."""
 
     def __init__(self, q, k, v, dout=None, *, causal=False, window_size=(-1, -1), softmax_scale=None,
                  cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, stream=None,
-                 dropout_p=0.0, dropout_seed=0, seqused_q=None, seqused_k=None):
+                 dropout_p=0.0, dropout_seed=0, seqused_q=None, seqused_k=None, deterministic=True):
         L = lib()
         dt = q.dtype
         _check(q, "q"); _check(k, "k", dt, q.device); _check(v, "v", dt, q.device)
@@ -346,19 +374,21 @@ class Plan:
         common = [g.batch, g.heads, g.kv_heads, g.seqlen_q, g.seqlen_k, g.d,
                   int(bool(causal)), int(window_size[0]), int(window_size[1]),
                   _default_scale(g.d, softmax_scale), float(dropout_p), _seed(dropout_seed),
-                  _dtype_code(q), sp]
+                  _dtype_code(q)]
+        self.deterministic = bool(deterministic)
         self._used = (seqused_q, seqused_k)
         self._fwd = [_ptr(q), _ptr(k), _ptr(v), _ptr(self.out), _ptr(self.lse),
-                     _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(seqused_q), _ptr(seqused_k)] + common
+                     _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(seqused_q), _ptr(seqused_k)] + common + [sp]
         if dout is not None:
             _check(dout, "dout", dt, q.device)
             self.dq, self.dk, self.dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-            need = int(L.fa_bwd_workspace_size(g.batch, g.heads, g.seqlen_q, g.d, _dtype_code(q)))
-            self.workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+            det = int(self.deterministic)
+            need = int(L.fa_bwd_workspace_size(g.batch, g.heads, g.seqlen_q, g.d, _dtype_code(q), det))
+            self.workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
             self._bwd = [_ptr(q), _ptr(k), _ptr(v), _ptr(self.out), _ptr(self.lse), _ptr(dout),
                          _ptr(self.dq), _ptr(self.dk), _ptr(self.dv), _ptr(self.workspace),
                          self.workspace.numel(), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
-                         _ptr(seqused_q), _ptr(seqused_k)] + common
+                         _ptr(seqused_q), _ptr(seqused_k)] + common + [det, sp]
         self._L = L
 
     def fwd(self):
@@ -380,30 +410,32 @@ class Plan:
 class _FlashAttn(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, softmax_scale, causal, window_size, cu_q, cu_k, max_q, max_k,
-                dropout_p, dropout_seed, used_q, used_k):
+                dropout_p, dropout_seed, used_q, used_k, deterministic):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
         out, lse = forward(q, k, v, causal=causal, window_size=window_size,
                            softmax_scale=softmax_scale, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k,
                            max_seqlen_q=max_q, max_seqlen_k=max_k,
                            dropout_p=dropout_p, dropout_seed=dropout_seed, seqused_q=used_q, seqused_k=used_k)
         ctx.save_for_backward(q, k, v, out, lse, cu_q, cu_k, used_q, used_k)
-        ctx.args = (softmax_scale, causal, window_size, max_q, max_k, dropout_p, dropout_seed)
+        ctx.args = (softmax_scale, causal, window_size, max_q, max_k, dropout_p, dropout_seed, deterministic)
         return out
 
     @staticmethod
     def backward(ctx, dout):
         q, k, v, out, lse, cu_q, cu_k, used_q, used_k = ctx.saved_tensors
-        softmax_scale, causal, window_size, max_q, max_k, dropout_p, dropout_seed = ctx.args
+        softmax_scale, causal, window_size, max_q, max_k, dropout_p, dropout_seed, deterministic = ctx.args
         dq, dk, dv = backward(dout.contiguous(), q, k, v, out, lse, causal=causal,
                               window_size=window_size, softmax_scale=softmax_scale,
                               cu_seqlens_q=cu_q, cu_seqlens_k=cu_k,
                               max_seqlen_q=max_q, max_seqlen_k=max_k,
-                              dropout_p=dropout_p, dropout_seed=dropout_seed, seqused_q=used_q, seqused_k=used_k)
-        return dq, dk, dv, None, None, None, None, None, None, None, None, None, None, None
+                              dropout_p=dropout_p, dropout_seed=dropout_seed, seqused_q=used_q, seqused_k=used_k,
+                              deterministic=deterministic)
+        return dq, dk, dv, None, None, None, None, None, None, None, None, None, None, None, None
 
 
 def flash_attn_func(q, k, v, dropout_p=0.0, softmax_scale=None, causal=False,
-                    window_size=(-1, -1), dropout_seed=None, seqused_q=None, seqused_k=None):
+                    window_size=(-1, -1), dropout_seed=None, seqused_q=None, seqused_k=None,
+                    deterministic=True):
     """Autograd entry with the call shape the pages use.  With dropout_p > 0
     and no dropout_seed, a seed is drawn from torch's default generator; the
     backward reuses the forward's seed.  seqused_q / seqused_k (int32 per
@@ -412,19 +444,21 @@ def flash_attn_func(q, k, v, dropout_p=0.0, softmax_scale=None, causal=False,
     if dropout_p > 0.0 and dropout_seed is None:
         dropout_seed = new_dropout_seed()
     return _FlashAttn.apply(q, k, v, softmax_scale, causal, tuple(window_size), None, None, None, None,
-                            float(dropout_p), 0 if dropout_seed is None else dropout_seed, seqused_q, seqused_k)
+                            float(dropout_p), 0 if dropout_seed is None else dropout_seed, seqused_q, seqused_k,
+                            bool(deterministic))
 
 
 def flash_attn_varlen_func(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
                            dropout_p=0.0, softmax_scale=None, causal=False, window_size=(-1, -1),
-                           dropout_seed=None):
+                           dropout_seed=None, deterministic=True):
     """Packed variable-length batches: q (total_q, heads, d), k/v (total_k,
     kv_heads, d), int32 prefix sums cu_seqlens_*; dropout as flash_attn_func."""
     if dropout_p > 0.0 and dropout_seed is None:
         dropout_seed = new_dropout_seed()
     return _FlashAttn.apply(q, k, v, softmax_scale, causal, tuple(window_size),
                             cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
-                            float(dropout_p), 0 if dropout_seed is None else dropout_seed, None, None)
+                            float(dropout_p), 0 if dropout_seed is None else dropout_seed, None, None,
+                            bool(deterministic))
 
 
 # ---------------------------------------------------------------------------

@@ -4,10 +4,11 @@
 // Every argument check runs before the first HIP call, so misuse is reported
 // the same way on a host without a GPU.  The device check is cached per
 // device ordinal.
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <atomic>
 #include <cmath>
+#include <cstdint>
 #include <cstring>
 
 #include "../../include/fa.h"
@@ -25,6 +26,16 @@ bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) %
 // kernels run them in tiles 64, 128 or 256 wide.
 bool head_dim_ok(int d) { return d >= 8 && d <= 256 && d % 8 == 0; }
 int tile_width(int d) { return d > 128 ? 256 : (d > 64 ? 128 : 64); }
+
+// The backward accumulates dQ with float32 atomics inside the dK/dV pass when
+// the caller does not ask for bitwise repeatable results and the head fits a
+// tile of 64 or 128 columns; otherwise it runs the separate dQ pass.
+bool atomic_dq(int deterministic, int head_dim) { return deterministic == 0 && head_dim <= 128; }
+// Bytes of the dQ accumulator ([rows, heads, tile width] float32), rounded up
+// to 256 so the arrays after it stay aligned.
+size_t dq_acc_bytes(size_t rows_heads, int head_dim) {
+    return (rows_heads * (size_t)tile_width(head_dim) * sizeof(float) + 255) & ~(size_t)255;
+}
 
 int check_common(int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k, int head_dim,
                  int causal, int window_left, int window_right, float softmax_scale, int dtype,
@@ -175,12 +186,20 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
     return FA_OK;
 }
 
-size_t fa_bwd_workspace_size(int batch, int heads, int seqlen_q, int head_dim, int dtype) {
+size_t fa_bwd_workspace_size(int batch, int heads, int seqlen_q, int head_dim, int dtype, int deterministic) {
     if (batch < 0 || heads < 1 || seqlen_q < 0) return 0;
     if (!head_dim_ok(head_dim)) return 0;
     if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return 0;
-    // two float arrays (D and LSE * log2 e), each one entry per query row and head
-    const size_t n = 2 * (size_t)batch * (size_t)heads * (size_t)seqlen_q * sizeof(float);
+    if (deterministic != 0 && deterministic != 1) return 0;
+    const size_t rows = (size_t)batch * (size_t)seqlen_q * (size_t)heads;
+    // sizes whose byte count would not fit a size_t are invalid
+    if (batch > 0 && heads > 0 && seqlen_q > 0 &&
+        ((size_t)batch * (size_t)heads > SIZE_MAX / (size_t)seqlen_q || rows > SIZE_MAX / (2 * 4 + 128 * 4 + 256)))
+        return 0;
+    // two float arrays (D and LSE * log2 e), one entry per query row and head;
+    // on the atomic dQ path first a float32 dQ accumulator, tile width wide
+    size_t n = 2 * rows * sizeof(float);
+    if (atomic_dq(deterministic, head_dim)) n += dq_acc_bytes(rows, head_dim);
     return n > 0 ? n : 4;  // never zero for valid sizes, so a null workspace is an error
 }
 
@@ -196,10 +215,12 @@ int bwd_common(int stage_lo, int stage_hi,
                const int32_t* seqused_q, const int32_t* seqused_k,
                int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
                int head_dim, int causal, int window_left, int window_right,
-               float softmax_scale, float dropout_p, uint64_t dropout_seed, int dtype, void* stream) {
+               float softmax_scale, float dropout_p, uint64_t dropout_seed, int dtype, int deterministic,
+               void* stream) {
     int rc = check_common(batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim, causal, window_left,
                           window_right, softmax_scale, dtype, cu_seqlens_q, cu_seqlens_k);
     if (rc != FA_OK) return rc;
+    if (deterministic != 0 && deterministic != 1) return FA_ERR_INVALID_ARG;
     uint32_t drop_t;
     float drop_scale;
     if (!dropout_params(dropout_p, drop_t, drop_scale)) return FA_ERR_INVALID_ARG;
@@ -207,18 +228,23 @@ int bwd_common(int stage_lo, int stage_hi,
     const bool has_q = (long long)batch * seqlen_q > 0, has_k = (long long)batch * seqlen_k > 0;
     if ((has_q && (!q || !o || !lse || !dout || !dq)) || (has_k && (!k || !v || !dk || !dv)) || !workspace)
         return FA_ERR_INVALID_ARG;
-    const void* p16[] = {q, k, v, o, dout, dq, dk, dv};
+    const void* p16[] = {q, k, v, o, dout, dq, dk, dv, workspace};
     for (const void* p : p16)
         if (!aligned(p, 16)) return FA_ERR_INVALID_ARG;
-    if (!aligned(lse, 4) || !aligned(workspace, 4)) return FA_ERR_INVALID_ARG;
-    if (workspace_bytes < fa_bwd_workspace_size(batch, heads, seqlen_q, head_dim, dtype))
-        return FA_ERR_WORKSPACE;
+    if (!aligned(lse, 4)) return FA_ERR_INVALID_ARG;
+    const size_t need = fa_bwd_workspace_size(batch, heads, seqlen_q, head_dim, dtype, deterministic);
+    if (need == 0) return FA_ERR_INVALID_ARG;  // sizes past what a size_t counts
+    if (workspace_bytes < need) return FA_ERR_WORKSPACE;
     rc = check_arch();
     if (rc != FA_OK) return rc;
+    const size_t rows = (size_t)batch * (size_t)heads * (size_t)seqlen_q;
     fa::BwdArgs a;
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
-    a.dq = dq; a.dk = dk; a.dv = dv; a.dsum = (float*)workspace;
-    a.lse2 = a.dsum + (size_t)batch * (size_t)heads * (size_t)seqlen_q;
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    const bool adq = atomic_dq(deterministic, head_dim);
+    a.dq_acc = adq ? (float*)workspace : nullptr;
+    a.dsum = (float*)((char*)workspace + (adq ? dq_acc_bytes(rows, head_dim) : 0));
+    a.lse2 = a.dsum + rows;
     a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
     a.used_q = seqused_q; a.used_k = seqused_k;
     a.batch = batch; a.heads = heads; a.kv_heads = kv_heads;
@@ -254,11 +280,12 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const int32_t* seqused_q, const int32_t* seqused_k,
            int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
            int head_dim, int causal, int window_left, int window_right,
-           float softmax_scale, float dropout_p, uint64_t dropout_seed, int dtype, void* stream) {
+           float softmax_scale, float dropout_p, uint64_t dropout_seed, int dtype, int deterministic,
+           void* stream) {
     return bwd_common(0, 2, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes,
                       cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k, batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim,
                       causal, window_left, window_right, softmax_scale, dropout_p, dropout_seed, dtype,
-                      stream);
+                      deterministic, stream);
 }
 
 int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o,
@@ -268,12 +295,13 @@ int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const v
                  const int32_t* seqused_q, const int32_t* seqused_k,
                  int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
                  int head_dim, int causal, int window_left, int window_right,
-                 float softmax_scale, float dropout_p, uint64_t dropout_seed, int dtype, void* stream) {
+                 float softmax_scale, float dropout_p, uint64_t dropout_seed, int dtype, int deterministic,
+                 void* stream) {
     if (stage < 0 || stage > 2) return FA_ERR_INVALID_ARG;
     return bwd_common(stage, stage, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes,
                       cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k, batch, heads, kv_heads, seqlen_q, seqlen_k, head_dim,
                       causal, window_left, window_right, softmax_scale, dropout_p, dropout_seed, dtype,
-                      stream);
+                      deterministic, stream);
 }
 
 }  // extern "C"
@@ -389,7 +417,7 @@ const char* fa_strerror(int status) {
     switch (status) {
         case FA_OK: return "ok";
         case FA_ERR_INVALID_ARG: return "invalid argument";
-        case FA_ERR_UNSUPPORTED: return "unsupported head_dim (a multiple of 8 up to 128) or dtype";
+        case FA_ERR_UNSUPPORTED: return "unsupported head_dim (a multiple of 8 from 8 to 256; FP8: of 16 up to 128) or dtype";
         case FA_ERR_ARCH: return "no gfx950 (MI355X) device is current";
         case FA_ERR_WORKSPACE: return "workspace too small";
         case FA_ERR_LAUNCH: return "kernel launch failed";

@@ -26,6 +26,14 @@
 //                registers, no atomics
 //   bwd_dq       per query tile (outer) over the visible key tiles (inner):
 //                the separate dQ accumulation pass, no atomics
+// or, on the atomic dQ path (head_dim up to 128, when the caller allows a
+// summation order that varies from call to call):
+//   bwd_rowdot   as above, and zeroes a float32 dQ accumulator
+//   bwd_dkdv     also forms dQ += dS K for each 32-row block over the
+//                workgroup's 128 keys and adds it into the accumulator with
+//                float32 atomics, so the scores and dP are computed once
+//                (five products per visible pair instead of seven)
+//   bwd_dq_cvt   dQ = scale * accumulator, rounded to the 16-bit type
 // Both main kernels stream their tiles row-major into LDS with direct
 // global -> LDS loads (double-buffered) and build every transposed MFMA
 // operand (dO^T, Q^T, K^T) with the transposing LDS reads of gfx950, so no
@@ -79,8 +87,40 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(BwdArgs a) {
             idx = (b * a.heads + h) * a.seqlen_q + i;
         }
         a.dsum[idx] = acc;
-        a.lse2[idx] = a.lse[idx] * kLog2e;  // -inf (a row without keys) stays -inf
+        // a row without visible keys (LSE = -inf) gets +inf, so that every
+        // recomputed probability of it is exp2(-inf) = 0 rather than inf
+        const float l = a.lse[idx];
+        a.lse2[idx] = l == kNegInf ? __builtin_inff() : l * kLog2e;
     }
+    if (a.dq_acc && live) {  // atomic dQ path: clear the accumulator row (all D columns)
+        f32x4* z = (f32x4*)(a.dq_acc + (t * a.heads + h) * D + part * 8);
+        z[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        z[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+}
+
+// Atomic dQ path: dq = scale * dq_acc, rounded to the 16-bit type (columns
+// below head_dim only).
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void bwd_dq_cvt_kernel(BwdArgs a) {
+    constexpr int LPR = D / 8;
+    constexpr int RPB = 256 / LPR;
+    const int tid = threadIdx.x;
+    const int64_t item = (int64_t)blockIdx.x * RPB + tid / LPR;
+    const int part = tid % LPR;
+    const int64_t rows = a.cu_q ? (int64_t)a.cu_q[a.batch] : (int64_t)a.batch * a.seqlen_q;
+    const int64_t t = item / a.heads;
+    const int h = (int)(item % a.heads);
+    if (t >= rows || part * 8 >= a.head_dim) return;
+    const f32x4* src = (const f32x4*)(a.dq_acc + (t * a.heads + h) * D + part * 8);
+    const f32x4 x0 = src[0], x1 = src[1];
+    const float sc = a.scale;
+    u32x4 w;
+    w[0] = pack2<BF16>(x0[0] * sc, x0[1] * sc);
+    w[1] = pack2<BF16>(x0[2] * sc, x0[3] * sc);
+    w[2] = pack2<BF16>(x1[0] * sc, x1[1] * sc);
+    w[3] = pack2<BF16>(x1[2] * sc, x1[3] * sc);
+    *(u32x4*)((uint16_t*)a.dq + (t * a.heads + h) * a.head_dim + part * 8) = w;
 }
 
 // Direct loads of ROWS rows of a [rows, heads, D] tensor (row stride `stride`
@@ -647,6 +687,443 @@ void bwd_dkdv_kernel(BwdArgs a) {
         }
 }
 
+// ---------------------------------------------------------------------------
+// dK, dV (and on the atomic path dQ) with producer and consumer waves.
+//
+// One workgroup per (batch, kv head, 128-key tile), 8 waves, two per SIMD.
+// Waves p = 0..3 (producers) and c = p + 4 (consumers) share the 32 keys
+// j0 + 32 p ..; the workgroup streams 64-row query tiles (Q, dO and the row
+// terms) through three LDS stages and handles them as 32-row blocks, one
+// block per iteration, the consumers one block behind the producers:
+//   producer, block n:   S = Q K^T, dP = dO V^T        (K^T, V^T resident)
+//                        P = exp2(c S - lse2), dS = P o (dP - D), masked,
+//                        stored transposed (key rows) into LDS
+//   consumer, block n-1: dV^T += dO^T P, dK^T += Q^T dS (accumulators
+//                        resident; P, dS read back as B operands)
+//                        atomic path: dQ[32 rows][its d-block] = dS K over
+//                        the keys of its key group (dS by transposing reads,
+//                        K resident), added into dq_acc with float32 atomics
+// and one barrier per iteration.  A wave keeps only its role's state, so two
+// fit a SIMD (256 registers each) and the SIMD overlaps one wave's softmax
+// arithmetic with the other's matrix products.  Only producers load tiles
+// (their vmcnt waits count direct loads only); only consumers issue atomics.
+// ---------------------------------------------------------------------------
+constexpr int kPcBM = 64;  // query rows per streamed tile (two blocks)
+#ifndef FA_PC_PF
+#define FA_PC_PF 1
+#endif
+
+template <int D>
+struct PcCfg {
+    static constexpr int tileElems = kPcBM * D;                        // Q or dO tile (16-bit)
+    static constexpr int stageBytes = 2 * tileElems * 2 + 2 * kPcBM * 4;  // Q, dO, lse2, D
+    static constexpr int xElems = kKvBN * 32;  // P^T or dS^T of one block: [128 keys][32 rows]
+    static_assert(2 * tileElems * 2 >= kKvBN * D * 2, "the key tile passes through one stage");
+};
+
+// Offset (16-bit elements) of rows 8 g + 4 h .. + 3 of key row kt in a
+// [128 keys][32 rows] exchange tile: 16-byte chunk g at slot g ^ ((kt >> 2) & 3),
+// and its 8-byte halves swapped on odd 16-key groups.  The 8-byte accesses of
+// one half-wave (32 lanes: 32 keys, one h) then cover all 64 banks once.
+__device__ __forceinline__ int xch_off(int kt, int g, int h) {
+    return kt * 32 + ((g ^ ((kt >> 2) & 3)) * 8) + 4 * (h ^ ((kt >> 4) & 1));
+}
+
+template <bool BF16, int D, bool DROP, bool ADQ>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void bwd_pc_kernel(BwdArgs a) {
+    using C = PcCfg<D>;
+    using Dma = TileDma<D, kPcBM, 4>;  // issued by the four producers
+    using KDma = TileDma<D, kKvBN, 4>;
+    constexpr int KS = D / 16, DB = D / 32, CPR = D / 8;
+    // three stages, separate objects (reads of one never wait on loads into another)
+    __shared__ __attribute__((aligned(16))) uint8_t st0[C::stageBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t st1[C::stageBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t st2[C::stageBytes];
+    // P^T and dS^T of a block, by block parity
+    __shared__ __attribute__((aligned(16))) uint16_t pt0[C::xElems];
+    __shared__ __attribute__((aligned(16))) uint16_t pt1[C::xElems];
+    __shared__ __attribute__((aligned(16))) uint16_t dt0[C::xElems];
+    __shared__ __attribute__((aligned(16))) uint16_t dt1[C::xElems];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kw = wave & 3;  // key block of this wave
+    const int r32 = lane & 31, half = lane >> 5;
+    const int g = a.heads / a.kv_heads;
+    const int b = blockIdx.x / a.kv_heads, hk = blockIdx.x % a.kv_heads;
+    const Seq s = seq_of(b, a.cu_q, a.cu_k, a.used_q, a.used_k, a.seqlen_q, a.seqlen_k);
+    const int j0 = blockIdx.y * kKvBN;
+    if (j0 >= s.len_k) return;
+    const Mask mk{a.causal, a.left, a.right};
+    const int j1 = min(j0 + kKvBN, s.len_k) - 1;
+
+    const int dh = a.head_dim;
+    const int q_stride = a.heads * dh, kv_stride = a.kv_heads * dh;
+    const uint16_t* kbase = (const uint16_t*)a.k + (s.k_start * a.kv_heads + hk) * dh;
+    const uint16_t* vbase = (const uint16_t*)a.v + (s.k_start * a.kv_heads + hk) * dh;
+    const int64_t total_q = a.cu_q ? (int64_t)a.cu_q[a.batch] : 0;
+
+    // Query rows that see any key of this tile, as whole 64-row tiles.
+    int i_lo = 0, i_hi = s.len_q - 1;
+    if (a.causal) i_lo = max(i_lo, j0 - s.off);
+    if (a.right >= 0) i_lo = max(i_lo, j0 - s.off - a.right);
+    if (a.left >= 0) i_hi = min(i_hi, j1 - s.off + a.left);
+    const int it_lo = i_lo / kPcBM;
+    const int nt = i_hi >= i_lo ? i_hi / kPcBM + 1 - it_lo : 0;  // tiles per query head
+    const int ntiles = g * nt;                                      // over the GQA group
+    const int nblocks = 2 * ntiles;
+
+    const int kw0 = j0 + 32 * kw;
+    const int key = kw0 + r32;
+    int q_lo = 0, q_hi = s.len_q - 1;  // this lane's key is visible to rows q_lo .. q_hi
+    if (a.causal) q_lo = max(q_lo, key - s.off);
+    if (a.right >= 0) q_lo = max(q_lo, key - s.off - a.right);
+    if (a.left >= 0) q_hi = min(q_hi, key - s.off + a.left);
+    if (key >= s.len_k) q_hi = -1;
+
+    auto stage = [&](int i) -> uint8_t* { return i == 0 ? st0 : (i == 1 ? st1 : st2); };
+    auto q_tile = [&](int i) { return (const uint16_t*)stage(i); };
+    auto do_tile = [&](int i) { return (const uint16_t*)stage(i) + C::tileElems; };
+    auto rows_lds = [&](int i) { return (const float*)(stage(i) + 2 * C::tileElems * 2); };
+    auto ptile = [&](int par) { return par ? pt1 : pt0; };
+    auto dtile = [&](int par) { return par ? dt1 : dt0; };
+    // (query head, first row) of tile t of the sequence; t past the last is
+    // clamped to it (its loads then only refill a free stage)
+    auto tile_head = [&](int t) { return hk * g + min(t, ntiles - 1) / nt; };
+    auto tile_row0 = [&](int t) { return (it_lo + min(t, ntiles - 1) % nt) * kPcBM; };
+
+    if (wave < 4) {
+        // =========================== producer ===========================
+        Dma dma;
+        dma.init(wave, lane, dh);
+        const int p = wave;
+        u32x4 kf[KS], vf[KS];  // K^T, V^T B operands: lane column = key
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bool ok = key < s.len_k && ks * 16 + 8 * half < dh;
+            kf[ks] = ok ? *(const u32x4*)(kbase + (int64_t)key * kv_stride + ks * 16 + 8 * half) : u32x4{0, 0, 0, 0};
+            vf[ks] = ok ? *(const u32x4*)(vbase + (int64_t)key * kv_stride + ks * 16 + 8 * half) : u32x4{0, 0, 0, 0};
+        }
+        int q_rd[KS];  // A operand reads of the Q / dO tiles: row r32 (+32 blk), chunk 2 ks + half
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) q_rd[ks] = r32 * D + (((2 * ks + half) ^ swz<CPR>(r32)) * 8);
+        int x_wr[4];
+        const int kt = 32 * p + r32;
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) x_wr[gq] = xch_off(kt, gq, half);
+        const float c = a.scale_log2;
+
+        // Tile t into stage st: Q, dO, and the row terms (lse2 by producers 0 and
+        // 2, D by 1 and 3: the duplicates write the same bytes, so that every
+        // producer issues the same number of loads per tile).
+        auto issue_tile = [&](int t, int st) {
+            const int h = tile_head(t), row0 = tile_row0(t);
+            const bool tail = row0 + kPcBM > s.len_q;
+            const int last = s.len_q - 1 - row0;
+            const int64_t hoff = (s.q_start * a.heads + h) * dh + (int64_t)row0 * q_stride;
+            uint16_t* qt = (uint16_t*)stage(st);
+            dma.issue((const uint16_t*)a.q + hoff, qt, p, q_stride, tail, last);
+            dma.issue((const uint16_t*)a.dout + hoff, qt + C::tileElems, p, q_stride, tail, last);
+            const int64_t idx0 = a.cu_q ? (int64_t)h * total_q + s.q_start + row0
+                                        : ((int64_t)b * a.heads + h) * a.seqlen_q + row0;
+            const float* src = ((p & 1) ? a.dsum : a.lse2) + idx0;
+            dma4(buffer_of(src), (uint32_t)min(lane, last) * 4u, (float*)(stage(st) + 2 * C::tileElems * 2) + (p & 1) * kPcBM);
+        };
+        constexpr int kOps = 2 * Dma::kPerWave + 1;  // direct loads per tile and producer
+
+        // S = Q K^T and dP = dO V^T of block n (tile n / 2 in stage st, rows
+        // 32 (n % 2) .. of it), one k-step per call: operands read two k-steps ahead.
+        struct Sdp {
+            f32x16 s, dp;
+        };
+        constexpr int kPfP = FA_PC_PF;  // k-steps of operand reads ahead of their products
+        u32x4 qa[KS], da[KS];
+        auto sdp_load = [&](int n, int st, int ks) {
+            const int blk = n & 1;
+            qa[ks] = *(const u32x4*)(q_tile(st) + blk * 32 * D + q_rd[ks]);
+            da[ks] = *(const u32x4*)(do_tile(st) + blk * 32 * D + q_rd[ks]);
+        };
+        auto sdp_step = [&](Sdp& x, int ks) {
+            x.s = mfma32<BF16>(qa[ks], kf[ks], ks ? x.s : f32x16{0});
+            x.dp = mfma32<BF16>(da[ks], vf[ks], ks ? x.dp : f32x16{0});
+        };
+        // Iteration n of the producer: S, dP of block n + 1 (when there is one)
+        // on the matrix cores, interleaved k-step by k-step with P, dS of block
+        // n (from the S, dP the previous iteration left in `cur`) on the vector
+        // ALU, so one wave keeps both busy; then block n's P, dS, masked, go to
+        // the exchange tiles of parity par.
+        auto produce = [&](int n, int st, int st_next, int par, Sdp& cur, Sdp& nxt, bool has_next) {
+            // Opaque per iteration: LDS objects past 64 KiB cannot take the
+            // instruction's 16-bit offset, so each (lane offset, object) sum
+            // costs a register if the compiler hoists it out of the loop;
+            // this keeps the additions next to their reads.
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(q_rd[ks]));
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) asm volatile("" : "+v"(x_wr[gq]));
+            const int t = n >> 1, blk = n & 1;
+            const int hq = tile_head(t), row0 = tile_row0(t) + 32 * blk;
+            const float* lses = rows_lds(st) + 32 * blk;
+            const float* dss = lses + kPcBM;
+            // row terms of this lane's 16 rows 8 gq + 4 half + 0..3, group gq read
+            // one group ahead of its first pair (pairs 2 gq, 2 gq + 1)
+            f32x4 l4[4], d4[4];
+            auto load_rows = [&](int gq) {
+                l4[gq] = *(const f32x4*)(lses + 8 * gq + 4 * half);
+                d4[gq] = *(const f32x4*)(dss + 8 * gq + 4 * half);
+            };
+            load_rows(0);
+            u32x4 kwd;
+            if constexpr (DROP) {
+                const uint32_t iq = (uint32_t)row0 / 4 + 2 * (r32 & 3) + half;
+                kwd = quad_transpose(byte_transpose(philox4x32_10((uint32_t)key / 4, iq, hq, b, a.seed_lo, a.seed_hi)));
+            }
+            uint32_t pp[8], dsp[8];
+            // P, dS of register pair m (register i: row 8 (i / 4) + 4 half + i % 4)
+            auto pair = [&](int m) {
+                if (m % 2 == 0 && m / 2 + 1 < 4) load_rows(m / 2 + 1);
+                float pv[2], dv2[2];
+#pragma unroll
+                for (int t2 = 0; t2 < 2; ++t2) {
+                    const int i = 2 * m + t2;
+                    const float pr = fast_exp2(__builtin_fmaf(cur.s[i], c, -l4[i / 4][i % 4]));
+                    if constexpr (DROP) {
+                        const bool kp = keep_byte(kwd[i / 4], i % 4, a.drop_t);
+                        pv[t2] = kp ? pr : 0.f;
+                        dv2[t2] = pr * ((kp ? cur.dp[i] * a.drop_scale : 0.f) - d4[i / 4][i % 4]);
+                    } else {
+                        pv[t2] = pr;
+                        dv2[t2] = pr * (cur.dp[i] - d4[i / 4][i % 4]);
+                    }
+                }
+                pp[m] = pack2<BF16>(pv[0], pv[1]);
+                dsp[m] = pack2<BF16>(dv2[0], dv2[1]);
+            };
+            constexpr int MPS = 8 / KS > 0 ? 8 / KS : 1;  // softmax pairs per k-step
+            // Without a next block the products still run, on this block's own
+            // (valid) stage, and their result is never used: no branch splits
+            // the k-steps, so the products and the vector work interleave.
+            const int nn = has_next ? n + 1 : n;
+            const int sn = has_next ? st_next : st;
+#pragma unroll
+            for (int ks = 0; ks < kPfP && ks < KS; ++ks) sdp_load(nn, sn, ks);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                if (ks + kPfP < KS) sdp_load(nn, sn, ks + kPfP);
+                sdp_step(nxt, ks);
+#pragma unroll
+                for (int m = ks * MPS; m < (ks + 1) * MPS && m < 8; ++m) pair(m);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int m = KS * MPS; m < 8; ++m) pair(m);
+            // visibility: all pairs visible, or AND the words with the mask
+            const int lo = q_lo - row0, hi = q_hi - row0;
+            const bool full = lo <= 0 && hi >= 31;  // this lane's key sees all 32 rows
+            if (__builtin_amdgcn_ballot_w64(!full) != 0) {  // uniform
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    const int r0 = 8 * (m / 2) + 4 * half + 2 * (m % 2);
+                    const uint32_t keep = ((r0 >= lo && r0 <= hi) ? 0x0000FFFFu : 0u) |
+                                          ((r0 + 1 >= lo && r0 + 1 <= hi) ? 0xFFFF0000u : 0u);
+                    pp[m] &= keep;
+                    dsp[m] &= keep;
+                }
+            }
+            uint16_t* ptw = ptile(par);
+            uint16_t* dtw = dtile(par);
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                *(u32x2*)(ptw + x_wr[gq]) = u32x2{pp[2 * gq], pp[2 * gq + 1]};
+                *(u32x2*)(dtw + x_wr[gq]) = u32x2{dsp[2 * gq], dsp[2 * gq + 1]};
+            }
+        };
+
+        // prologue: the key tile through stage 2 for the consumers' K operands
+        KDma kd;
+        kd.init(p, lane, dh);
+        kd.issue(kbase + (int64_t)j0 * kv_stride, (uint16_t*)st2, p, kv_stride, j0 + kKvBN > s.len_k, s.len_k - 1 - j0);
+        wait_vmcnt<0>();
+        lds_barrier();  // (1) key tile in LDS
+        lds_barrier();  // (2) consumers have read it
+        Sdp sa, sb;     // S, dP of the next block to soften: by iteration parity
+        if (ntiles > 0) {
+            issue_tile(0, 0);
+            issue_tile(1, 1);
+            wait_vmcnt<kOps>();  // tile 0 landed
+            lds_barrier();       // (3) ... for every producer
+            // S, dP of block 0
+#pragma unroll
+            for (int ks = 0; ks < 2 && ks < KS; ++ks) sdp_load(0, 0, ks);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                if (ks + 2 < KS) sdp_load(0, 0, ks + 2);
+                sdp_step(sa, ks);
+            }
+        } else {
+            lds_barrier();  // (3)
+        }
+        // Iteration n: P, dS of block n (n < nblocks) and S, dP of block n + 1.
+        // Tile X (blocks 2X, 2X + 1, stage X % 3) is loaded from odd iteration
+        // 2X - 3 (its stage's previous tile was last read in iteration 2X - 4)
+        // and waited for at the end of iteration 2X - 2, before its first S, dP
+        // in iteration 2X - 1.  Unrolled by 6 so stages and parities are static.
+        for (int n0 = 0; n0 <= nblocks; n0 += 6) {
+#pragma unroll
+            for (int u = 0; u < 6; ++u) {
+                const int n = n0 + u;
+                if (n > nblocks) break;
+                if (u & 1) issue_tile((n + 3) >> 1, ((u + 3) >> 1) % 3);
+                if (n < nblocks) {
+                    Sdp& cur = (u & 1) ? sb : sa;
+                    Sdp& nxt = (u & 1) ? sa : sb;
+                    produce(n, (u >> 1) % 3, ((u + 1) >> 1) % 3, u & 1, cur, nxt, n + 1 < nblocks);
+                }
+                if (!(u & 1)) wait_vmcnt<0>();  // tile n / 2 + 1 (the last one issued) landed
+                lds_barrier();
+            }
+        }
+    } else {
+        // =========================== consumer ===========================
+        const int cw = wave - 4;
+        int t_rd[2][DB];  // transposing reads (X^T operands) of a row-major tile
+        tr_offsets<D, DB>(lane, t_rd);
+        f32x16 dk[DB], dv[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db) { dk[db] = f32x16{0}; dv[db] = f32x16{0}; }
+        int x_rd[2][2];  // B operand reads of P^T / dS^T: k-step kk, chunk 2 kk + e
+        {
+            const int kt = 32 * cw + r32;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) x_rd[kk][e] = xch_off(kt, 2 * kk + e, half);
+        }
+        // atomic dQ: d-block and key group of this wave, K operands, dS reads
+        const int dqb = cw % DB, dkg = cw / DB;
+        u32x4 kq[ADQ ? KS : 1];
+        int dq_rd[2][2];  // [parity of the 16-key k-step][instruction]
+        lds_barrier();  // (1)
+        if constexpr (ADQ) {
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) kq[kk] = read_tr<D, DB>((const uint16_t*)st2, KS * dkg + kk, dqb, t_rd);
+            const int g4 = lane >> 4, jl = lane & 15;
+#pragma unroll
+            for (int par = 0; par < 2; ++par)
+#pragma unroll
+                for (int inst = 0; inst < 2; ++inst) {
+                    // key row 16 k + rr, query rows col .. col + 3 (xch_off's layout)
+                    const int rr = 8 * inst + 4 * (g4 >> 1) + (jl >> 2);
+                    const int col = 16 * (g4 & 1) + 4 * (jl & 3);
+                    dq_rd[par][inst] = rr * 32 + (((col >> 3) ^ ((rr >> 2) & 3)) * 8) + 4 * (((col >> 2) & 1) ^ par);
+                }
+        }
+        lds_barrier();  // (2) (waits for the reads above)
+        lds_barrier();  // (3)
+        const int64_t dq_row_stride = (int64_t)a.heads * D;
+        const uint32_t dq_lane = (uint32_t)(4 * half * dq_row_stride) + 32 * dqb + r32;
+
+        auto consume = [&](int m, int st, int par) {
+            // lane offsets opaque per iteration (as in the producer)
+#pragma unroll
+            for (int inst = 0; inst < 2; ++inst)
+#pragma unroll
+                for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(t_rd[inst][db]));
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) asm volatile("" : "+v"(x_rd[kk][e]));
+            const int t = m >> 1, blk = m & 1;
+            const int hq = tile_head(t), row0 = tile_row0(t) + 32 * blk;
+            const uint16_t* qt = q_tile(st);
+            const uint16_t* dot = do_tile(st);
+            const uint16_t* ptr = ptile(par);
+            const uint16_t* dtr = dtile(par);
+            auto xread = [&](const uint16_t* x, int kk) {
+                const u32x2 lo = *(const u32x2*)(x + x_rd[kk][0]);
+                const u32x2 hi = *(const u32x2*)(x + x_rd[kk][1]);
+                return u32x4{lo.x, lo.y, hi.x, hi.y};
+            };
+            auto dsa_read = [&](int kk) {
+                typedef short s16x4 __attribute__((ext_vector_type(4)));
+                typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+                const int kst = KS * dkg + kk;  // 16-key k-step of the tile
+                const uint16_t* x = dtr + kst * 16 * 32;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(x + dq_rd[kst & 1][0]));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(x + dq_rd[kst & 1][1]));
+                const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+                return u32x4{l2.x, l2.y, h2.x, h2.y};
+            };
+            f32x16 dqa = f32x16{0};
+            // two k-steps of 16 rows; per k-step DB dV and DB dK products, and
+            // (atomic path) KS / 2 dQ products interleaved with them
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const u32x4 pb = xread(ptr, kk), sb = xread(dtr, kk);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const u32x4 ta = read_tr<D, DB>(dot, 2 * blk + kk, db, t_rd);
+                    const u32x4 tb = read_tr<D, DB>(qt, 2 * blk + kk, db, t_rd);
+                    dv[db] = mfma32<BF16>(ta, pb, dv[db]);
+                    dk[db] = mfma32<BF16>(tb, sb, dk[db]);
+                    if constexpr (ADQ) {
+                        const int j = kk * DB + db;  // dQ k-step, 0 .. 2 DB - 1 = KS - 1
+                        dqa = mfma32<BF16>(dsa_read(j), kq[j], dqa);
+                    }
+                }
+            }
+            if constexpr (ADQ) {
+                float* dqh = a.dq_acc + ((s.q_start + row0) * a.heads + hq) * (int64_t)D;
+                const int last_row = s.len_q - 1 - row0;
+                if (31 <= last_row) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        unsafeAtomicAdd(dqh + (int64_t)(8 * (i / 4) + (i % 4)) * dq_row_stride + dq_lane, dqa[i]);
+                } else {  // tail block: rows past the sequence (dS zero there) clamped to its last row
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int r = min(8 * (i / 4) + 4 * half + (i % 4), last_row);
+                        unsafeAtomicAdd(dqh + (int64_t)r * dq_row_stride + 32 * dqb + r32, dqa[i]);
+                    }
+                }
+            }
+        };
+
+        for (int n0 = 0; n0 <= nblocks; n0 += 6) {
+#pragma unroll
+            for (int u = 0; u < 6; ++u) {
+                const int n = n0 + u;
+                if (n > nblocks) break;
+                // block n - 1: tile (n - 1) / 2, stage ((u + 5) % 6 / 2) % 3, parity (n - 1) & 1
+                if (n >= 1) consume(n - 1, ((u + 5) % 6) >> 1, (u + 1) & 1);
+                lds_barrier();
+            }
+        }
+
+        // store dK = scale * dK^T, dV = dV^T (lane column = key, registers = d)
+        if (kw0 >= s.len_k || key >= s.len_k) return;
+        uint16_t* dkrow = (uint16_t*)a.dk + ((s.k_start + key) * a.kv_heads + hk) * dh;
+        uint16_t* dvrow = (uint16_t*)a.dv + ((s.k_start + key) * a.kv_heads + hk) * dh;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int col = db * 32 + 8 * gq + 4 * half;  // four columns, all below dh or none
+                if (col >= dh) continue;
+                u32x2 wk, wv;
+                wk.x = pack2<BF16>(dk[db][4 * gq] * a.scale, dk[db][4 * gq + 1] * a.scale);
+                wk.y = pack2<BF16>(dk[db][4 * gq + 2] * a.scale, dk[db][4 * gq + 3] * a.scale);
+                const float sv = DROP ? a.drop_scale : 1.f;
+                wv.x = pack2<BF16>(dv[db][4 * gq] * sv, dv[db][4 * gq + 1] * sv);
+                wv.y = pack2<BF16>(dv[db][4 * gq + 2] * sv, dv[db][4 * gq + 3] * sv);
+                *(u32x2*)(dkrow + col) = wk;
+                *(u32x2*)(dvrow + col) = wv;
+            }
+    }
+}
+
 #ifndef FA_DQ_NW
 #define FA_DQ_NW 8
 #endif
@@ -663,13 +1140,33 @@ int launch_bwd_t(const BwdArgs& a, int stage, hipStream_t stream) {
         }
         return 0;
     }
-    if (stage == 1) {  // dK, dV
-        constexpr int DO = D > 128 ? 128 : D, BMR = D > 128 ? 64 : kKvBM;
+    if (stage == 1) {  // dK, dV (and dQ into dq_acc on the atomic path)
         const int ntiles = (a.seqlen_k + kKvBN - 1) / kKvBN;
         if (ntiles > 0 && a.batch > 0) {
+            // The separate-dQ path runs the one-wave-per-SIMD kernel (measured
+            // faster than the producer / consumer kernel without dQ); the atomic
+            // path runs the producer / consumer kernel, which forms dQ as well.
+            if constexpr (D <= 128) {
+                if (a.dq_acc) {
+                    auto kern = a.drop_t < 256 ? bwd_pc_kernel<BF16, D, true, true> : bwd_pc_kernel<BF16, D, false, true>;
+                    hipLaunchKernelGGL(kern, dim3(a.batch * a.kv_heads, ntiles), dim3(512), 0, stream, a);
+                    return hipGetLastError() == hipSuccess ? 0 : 1;
+                }
+            }
+            constexpr int DO = D > 128 ? 128 : D, BMR = D > 128 ? 64 : kKvBM;
             auto kern = a.drop_t < 256 ? bwd_dkdv_kernel<BF16, D, true, DO, BMR>
                                        : bwd_dkdv_kernel<BF16, D, false, DO, BMR>;
             hipLaunchKernelGGL(kern, dim3(a.batch * a.kv_heads, ntiles, D / DO), dim3(256), 0, stream, a);
+            if (hipGetLastError() != hipSuccess) return 1;
+        }
+        return 0;
+    }
+    if (a.dq_acc) {  // stage 2 of the atomic path: dq = scale * dq_acc
+        constexpr int RPB = 256 / (D / 8);
+        const int64_t items = (int64_t)a.batch * a.seqlen_q * a.heads;
+        const int64_t blocks = (items + RPB - 1) / RPB;
+        if (blocks > 0) {
+            hipLaunchKernelGGL((bwd_dq_cvt_kernel<BF16, D>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
             if (hipGetLastError() != hipSuccess) return 1;
         }
         return 0;

@@ -8,6 +8,11 @@
 //  * LDS: conflict-free LDS reads of a known number of bytes, as many as the
 //    CUs can serve, to learn the unit of the LDS activity counter and the read
 //    bandwidth the LDS sustains.
+//  * Matrix cores: independent chains of the 32x32 MFMAs the kernels use
+//    (bf16 32x32x16, fp8 32x32x64 with unit scales) on every SIMD, with the
+//    shader clock read beside the fixed 100 MHz real-time counter: the
+//    matrix-core rate the chip sustains under load, and its clock, as a
+//    measured denominator next to the published peak.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -61,9 +66,82 @@ __global__ __launch_bounds__(512) void calib_lds_kernel(uint32_t* __restrict__ o
     out[(int64_t)blockIdx.x * 512 + t] = acc.x ^ acc.y ^ acc.z ^ acc.w;
 }
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// Each wave runs `iters` rounds of NACC independent accumulator chains (one
+// MFMA per chain per round), so the matrix core of its SIMD never waits on a
+// result; two waves per SIMD.  Wave 0 of each workgroup records the shader
+// clock counter (s_memtime) and the 100 MHz real-time counter at its start
+// and end.  The accumulators go to `sink` so the chains are not removed.
+template <bool FP8>
+__global__ __launch_bounds__(512) void calib_mfma_kernel(float* __restrict__ sink, uint64_t* __restrict__ clocks,
+                                                         int iters) {
+    constexpr int NACC = 4;
+    const int t = threadIdx.x;
+    uint64_t c0 = 0, r0 = 0;
+    if (t == 0) {
+        c0 = __builtin_amdgcn_s_memtime();
+        r0 = __builtin_amdgcn_s_memrealtime();
+    }
+    f32x16 acc[NACC];
+#pragma unroll
+    for (int i = 0; i < NACC; ++i) acc[i] = f32x16{0};
+    // operands differ per lane and stay finite: small integers in bf16 / E4M3
+    const uint32_t x = 0x3F803F80u ^ ((uint32_t)(t & 7) << 16);  // 1.0, 1.x in bf16
+    if constexpr (!FP8) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{x, x, x, x});
+        const bf16x8 b = __builtin_bit_cast(bf16x8, u32x4{x ^ 1u, x, x, x});
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int i = 0; i < NACC; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i], 0, 0, 0);
+        }
+    } else {
+        const int w = 0x38383838 ^ (t & 3);  // E4M3 1.0 and neighbours
+        const i32x8 a = {w, w, w, w, w, w, w, w};
+        const i32x8 b = {w ^ 1, w, w, w, w, w, w, w};
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int i = 0; i < NACC; ++i)
+                acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i], 0, 0, 0, 127, 0, 127);
+        }
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NACC; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) s += acc[i][j];
+    sink[(int64_t)blockIdx.x * 512 + t] = s;
+    if (t == 0) {
+        const uint64_t c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+        clocks[4 * blockIdx.x + 0] = c0;
+        clocks[4 * blockIdx.x + 1] = c1;
+        clocks[4 * blockIdx.x + 2] = r0;
+        clocks[4 * blockIdx.x + 3] = r1;
+    }
+}
+
 }  // namespace
 
 extern "C" {
+
+// Runs the matrix-core calibration: `workgroups` workgroups of 8 waves, each
+// wave `iters` x 4 MFMAs (bf16 32x32x16: 32768 FLOP each; fp8 32x32x64:
+// 131072 FLOP each).  sink (device) receives workgroups * 512 floats, clocks
+// (device) workgroups * 4 uint64: shader clock at start and end, real-time
+// counter (100 MHz) at start and end, of wave 0.  Returns 0 when the launch
+// was accepted, 1 for bad arguments, 2 for a failed launch.
+int fa_calib_mfma(float* sink, uint64_t* clocks, int workgroups, int iters, int fp8, void* stream) {
+    if (!sink || !clocks || workgroups < 1 || iters < 1 || (fp8 != 0 && fp8 != 1)) return 1;
+    if (fp8)
+        hipLaunchKernelGGL(calib_mfma_kernel<true>, dim3(workgroups), dim3(512), 0, (hipStream_t)stream, sink, clocks,
+                           iters);
+    else
+        hipLaunchKernelGGL(calib_mfma_kernel<false>, dim3(workgroups), dim3(512), 0, (hipStream_t)stream, sink,
+                           clocks, iters);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
 
 // Copies `bytes` bytes from src to dst (device buffers that do not overlap)
 // with `waves` waves.  bytes must be a multiple of waves * 16 KiB.  Returns 0

@@ -156,6 +156,20 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
+// Workgroup barrier that waits only for this wave's LDS reads and writes
+// (lgkmcnt(0)), not for its direct global -> LDS loads still in flight: the
+// fence __syncthreads() carries counts those loads as LDS writes and would
+// wait for all of them (vmcnt(0)), so a kernel that keeps tile loads in
+// flight across barriers waits for them explicitly (wait_vmcnt) before the
+// barrier that publishes the tile.  The empty asm statements keep the
+// compiler from moving memory operations across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt at their maxima
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Per-lane offsets (in 16-bit elements inside the tile) of the transposing
 // reads that build the A operand "X^T" of a 32x32x16 MFMA from a row-major
 // tile X (rows = contraction index, columns = M index).  In every 16-lane

@@ -2,7 +2,7 @@
 // the kernel files.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
 namespace fa {
@@ -46,6 +46,10 @@ struct BwdArgs {
     void* dv;
     float* dsum;  // workspace: D_i = dO_i . O_i, laid out like lse
     float* lse2;  // workspace: LSE_i * log2(e), laid out like lse
+    // workspace of the atomic dQ path, or null (separate dQ pass): unscaled
+    // dQ in float32, [rows, heads, W] with W the tile width (64 or 128) and
+    // rows as in dq
+    float* dq_acc;
     const int32_t* cu_q;
     const int32_t* cu_k;
     const int32_t* used_q;  // as in FwdArgs
@@ -83,7 +87,9 @@ struct DecArgs {
 };
 
 // Each returns 0 when every launch was accepted, 1 otherwise.  Backward
-// stages: 0 = D_i = dO_i . O_i, 1 = dK/dV pass, 2 = dQ pass.
+// stages: 0 = D_i = dO_i . O_i (and, on the atomic dQ path, dq_acc = 0),
+// 1 = dK/dV pass (on the atomic dQ path it also adds dQ into dq_acc),
+// 2 = dQ pass (atomic dQ path: dq = scale * dq_acc in the 16-bit type).
 int launch_fwd(const FwdArgs& a, hipStream_t stream);
 // FP8 forward: f.q/k/v hold E4M3 bytes, f.scale = softmax_scale * dq * dk
 // (f.scale_log2 likewise), f.o is bf16 or fp16 (f.bf16); no dropout.

@@ -26,6 +26,10 @@ Subcommands (run from anywhere; the repository root is found from this file):
           bytes per launch in profiles/traffic.json together with the hash of
           the kernel's sources (bench.py reports the figure only while the
           hash still matches).
+  mfma    [--workgroups G] [--iters N]
+          Run the matrix-core calibration (libfacalib.so: independent bf16
+          32x32x16 and fp8 32x32x64 MFMA chains on every SIMD) and print the
+          rate it sustains and the shader clock under that load.
   trace   --db FILE --title T --command C
           Print a markdown table of a rocprofv3 kernel-trace database.
   util    --prefix P [--kernels fwd,dkdv,dq,fwd_fp8]
@@ -161,6 +165,58 @@ def _copy(args):
             raise RuntimeError(f"fa_calib_copy returned {rc}")
     torch.cuda.synchronize()
     print(f"copied {args.mib} MiB x{args.iters}", flush=True)
+
+
+def mfma_peak(fp8: bool, workgroups: int = 1024, iters: int = 20000, reps: int = 3):
+    """Sustained dense MFMA rate (TFLOP/s) and shader clock (GHz) measured on
+    the current device by the calibration kernel: `workgroups` workgroups of
+    8 waves, each wave `iters` rounds of 4 independent MFMA chains.  Returns
+    (tflops, clock_ghz), the median over `reps` timed launches after one
+    untimed launch."""
+    import ctypes
+    import numpy as np
+    import torch
+    if not os.path.exists(CALIB_LIB):
+        raise RuntimeError(f"{CALIB_LIB} is not built; run `python -m exact_tiled_attention_10_amd.build`")
+    L = ctypes.CDLL(CALIB_LIB)
+    L.fa_calib_mfma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                ctypes.c_void_p]
+    L.fa_calib_mfma.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    sink = torch.empty(workgroups * 512, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(workgroups * 4, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def launch():
+        rc = L.fa_calib_mfma(ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(clocks.data_ptr()), workgroups, iters,
+                             int(bool(fp8)), sp)
+        if rc != 0:
+            raise RuntimeError(f"fa_calib_mfma returned {rc}")
+
+    launch()
+    torch.cuda.synchronize()
+    times, ghz = [], []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / 1e3)
+        c = clocks.cpu().numpy().view(np.uint64).reshape(-1, 4).astype(np.float64)
+        ok = c[:, 3] > c[:, 2]
+        ghz.append(float(np.median((c[ok, 1] - c[ok, 0]) / (c[ok, 3] - c[ok, 2]) * 0.1)))
+    flops = workgroups * 8.0 * iters * 4 * (131072 if fp8 else 32768)
+    t = float(np.median(times))
+    return flops / t / 1e12, float(np.median(ghz))
+
+
+def _mfma(args):
+    sys.path.insert(0, ROOT)
+    for fp8 in (False, True):
+        tf, ghz = mfma_peak(fp8, args.workgroups, args.iters)
+        print(f"{'fp8' if fp8 else 'bf16'}: {tf:.1f} TFLOP/s sustained, shader clock {ghz:.3f} GHz", flush=True)
 
 
 LDS_NAME = "calib_lds_kernel"
@@ -361,6 +417,9 @@ def main(argv=None):
     lc.add_argument("--dir", required=True)
     lc.add_argument("--workgroups", type=int, default=512)
     lc.add_argument("--iters", type=int, default=4096)
+    mf = sub.add_parser("mfma")
+    mf.add_argument("--workgroups", type=int, default=1024)
+    mf.add_argument("--iters", type=int, default=20000)
     t = sub.add_parser("traffic")
     t.add_argument("--workload", required=True)
     t.add_argument("--kernel", required=True, choices=list(KERNEL_NAMES))
@@ -378,7 +437,7 @@ def main(argv=None):
     tr.add_argument("--bench-log", default=None)
     args = ap.parse_args(argv)
     {"run": _run, "copy": _copy, "lds": _lds, "ldscal": _ldscal, "traffic": _traffic, "trace": _trace,
-     "util": _util}[args.cmd](args)
+     "util": _util, "mfma": _mfma}[args.cmd](args)
 
 
 if __name__ == "__main__":

@@ -44,6 +44,9 @@
  *   key j is visible iff 0 <= j < Lk, (causal == 0 or j <= p),
  *   (window_left < 0 or j >= p - window_left) and
  *   (window_right < 0 or j <= p + window_right).
+ * The conditions combine as an intersection, so with causal = 1 a
+ * window_right > 0 is accepted and has no effect (causal already bounds the
+ * keys at p).
  * A row with no visible key gets O = 0 and LSE = -inf (and zero gradient).
  * GQA / MQA: query head h reads kv head h / (heads / kv_heads).
  * Sizes: heads * head_dim must stay below 2^23 (offsets inside a tile of up
@@ -68,17 +71,17 @@
  * Arithmetic: 16-bit inputs (fp16 or bf16, same type for every tensor),
  * products on the matrix cores with fp32 accumulation, softmax statistics
  * in fp32, P rounded to the input type before P.V, outputs rounded to
- * nearest even.  Results are deterministic (no atomics): the same call on
- * the same inputs gives the same bytes.
+ * nearest even.  Every entry point except fa_bwd / fa_bwd_stage with
+ * deterministic = 0 gives the same bytes for the same call on the same
+ * inputs (no atomics); see fa_bwd.
  *
- * Pointers: device pointers, 16-byte aligned (lse and the workspace 4-byte
- * aligned).  A tensor with no elements may be passed as NULL: the query-side
- * tensors (q, o, lse, dout, dq) when batch * seqlen_q == 0, the key-side ones
+ * Pointers: device pointers, 16-byte aligned (lse 4-byte aligned).  A
+ * tensor with no elements may be passed as NULL: the query-side tensors
+ * (q, o, lse, dout, dq) when batch * seqlen_q == 0, the key-side ones
  * (k, v, dk, dv) when batch * seqlen_k == 0.  The caller owns every
- * buffer; the library allocates nothing, frees nothing and keeps no pointer
- * after returning.  Inputs are never
- * written, outputs are fully overwritten (no zeroing needed) and must not
- * alias inputs or each other.
+ * buffer; the library allocates nothing, frees nothing and keeps no
+ * pointer after returning.  Inputs are never written, outputs are fully
+ * overwritten (no zeroing needed) and must not alias inputs or each other.
  *
  * Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL is the null
  * stream) and the call returns without waiting.  Execution errors surface at
@@ -168,12 +171,17 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                float descale_q, float descale_k, float descale_v, int out_dtype, void* stream);
 
 /*
- * Bytes of device workspace fa_bwd needs for these sizes: two float32
- * arrays of batch * heads * seqlen_q entries, the per-row term
- * D_i = dO_i . O_i and LSE_i * log2(e).  For packed batches pass the same
- * batch and seqlen_q as to fa_bwd.  Returns 0 for invalid sizes.
+ * Bytes of device workspace fa_bwd needs for these sizes (the workspace is
+ * part of the backward's contract as laid down for this library, not a
+ * quantity the pages define): two float32 arrays of batch * heads *
+ * seqlen_q entries, the per-row term D_i = dO_i . O_i and LSE_i * log2(e),
+ * and, when deterministic = 0 and head_dim <= 128, before them a float32 dQ
+ * accumulator of batch * seqlen_q * heads rows of 64 (head_dim <= 64) or
+ * 128 values, padded to a multiple of 256 bytes.  For packed batches pass
+ * the same batch and seqlen_q as to fa_bwd (batch * seqlen_q must be at
+ * least total_q).  deterministic is 0 or 1.  Returns 0 for invalid sizes.
  */
-size_t fa_bwd_workspace_size(int batch, int heads, int seqlen_q, int head_dim, int dtype);
+size_t fa_bwd_workspace_size(int batch, int heads, int seqlen_q, int head_dim, int dtype, int deterministic);
 
 /*
  * Backward: given the forward's inputs, its O and LSE, and dout = dL/dO,
@@ -182,12 +190,23 @@ size_t fa_bwd_workspace_size(int batch, int heads, int seqlen_q, int head_dim, i
  * the N x N matrices are never stored.  Three kernels run in order on
  * `stream`: the row term D_i = dO_i . O_i, a pass over key tiles that
  * accumulates dK and dV (summing the query heads of a GQA group inside the
- * workgroup), and a separate pass over query tiles that accumulates dQ.
+ * workgroup), and a dQ stage:
+ *   deterministic = 1 (or head_dim > 128): a separate pass over query tiles
+ *     accumulates dQ in registers; the same call gives the same bytes.
+ *   deterministic = 0, head_dim <= 128: the key-tile pass also forms dQ from
+ *     the same scores and adds each tile's part into a float32 accumulator
+ *     in the workspace with atomic adds, and the last kernel rounds it to
+ *     dq.  Five matrix products per visible pair instead of seven; the
+ *     order of the float32 additions varies from call to call, so dq may
+ *     differ in its last bits between calls (dk, dv do not).
  *   workspace / workspace_bytes: device memory of at least
- *   fa_bwd_workspace_size(batch, heads, seqlen_q, head_dim, dtype) bytes,
- *   owned by the caller; its contents on entry do not matter.
+ *   fa_bwd_workspace_size(batch, heads, seqlen_q, head_dim, dtype,
+ *   deterministic) bytes, 16-byte aligned, owned by the caller; its contents
+ *   on entry do not matter.
  * All other arguments as for fa_fwd, which must have produced o and lse
  * with the same arguments (dropout_p and dropout_seed included).
+ * Packed batches: the query-side tensors must hold exactly
+ * cu_seqlens_q[batch] rows (not checked on the device).
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const float* lse, const void* dout, void* dq, void* dk, void* dv,
@@ -196,15 +215,19 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const int32_t* seqused_q, const int32_t* seqused_k,
            int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
            int head_dim, int causal, int window_left, int window_right,
-           float softmax_scale, float dropout_p, uint64_t dropout_seed, int dtype, void* stream);
+           float softmax_scale, float dropout_p, uint64_t dropout_seed, int dtype, int deterministic,
+           void* stream);
 
 /*
  * One stage of fa_bwd, for callers that schedule or time the three kernels
- * themselves: stage 0 writes D_i = dO_i . O_i into the workspace, stage 1
- * writes dk and dv, stage 2 writes dq.  fa_bwd is exactly stages 0, 1, 2 in
- * this order on one stream; stages 1 and 2 read the workspace stage 0 wrote
- * and are independent of each other.  Arguments as for fa_bwd; a stage
- * outside 0..2 returns FA_ERR_INVALID_ARG.
+ * themselves: stage 0 writes D_i = dO_i . O_i into the workspace (and
+ * clears the dQ accumulator on the atomic path), stage 1 writes dk and dv
+ * (atomic path: and adds dQ into the accumulator), stage 2 writes dq.
+ * fa_bwd is exactly stages 0, 1, 2 in this order on one stream.  With
+ * deterministic = 1 stages 1 and 2 only read what stage 0 wrote and are
+ * independent of each other; on the atomic path stage 2 reads what stage 1
+ * added.  Arguments as for fa_bwd; a stage outside 0..2 returns
+ * FA_ERR_INVALID_ARG.
  */
 int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o,
                  const float* lse, const void* dout, void* dq, void* dk, void* dv,
@@ -213,7 +236,8 @@ int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const v
                  const int32_t* seqused_q, const int32_t* seqused_k,
                  int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
                  int head_dim, int causal, int window_left, int window_right,
-                 float softmax_scale, float dropout_p, uint64_t dropout_seed, int dtype, void* stream);
+                 float softmax_scale, float dropout_p, uint64_t dropout_seed, int dtype, int deterministic,
+                 void* stream);
 
 /*
  * Decode over a key/value cache (the KV-cache call named on the overview
@@ -273,7 +297,9 @@ int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, void
 int fa_fwd_kvcache_splits(int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k, int head_dim,
                           int num_splits);
 
-/* Static text for a status code ("unknown status" for others). */
+/* Static text for a status code ("unknown status" for others).  Part of
+ * this library's contract, like the status codes themselves; the pages
+ * define no error reporting. */
 const char* fa_strerror(int status);
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */

@@ -39,14 +39,20 @@ int main(void) {
            FA_ERR_UNSUPPORTED);
     expect("bwd: workspace too small",
            fa_bwd(p, p, p, p, lse, p, p, p, p, p, 16, NULL, NULL, NULL, NULL, 1, 4, 2, 128, 128, 128, 1, -1, -1,
-                  0.125f, 0.0f, 0, FA_DTYPE_BF16, NULL),
+                  0.125f, 0.0f, 0, FA_DTYPE_BF16, 1, NULL),
            FA_ERR_WORKSPACE);
     expect("bwd_stage: stage 3",
            fa_bwd_stage(3, p, p, p, p, lse, p, p, p, p, p, 1 << 20, NULL, NULL, NULL, NULL, 1, 4, 2, 128, 128, 128,
-                        1, -1, -1, 0.125f, 0.0f, 0, FA_DTYPE_BF16, NULL),
+                        1, -1, -1, 0.125f, 0.0f, 0, FA_DTYPE_BF16, 0, NULL),
+           FA_ERR_INVALID_ARG);
+    expect("bwd: deterministic = 2",
+           fa_bwd(p, p, p, p, lse, p, p, p, p, p, 1 << 20, NULL, NULL, NULL, NULL, 1, 4, 2, 128, 128, 128, 1, -1,
+                  -1, 0.125f, 0.0f, 0, FA_DTYPE_BF16, 2, NULL),
            FA_ERR_INVALID_ARG);
     expect("bwd workspace size: 2 float arrays of B*H*N",
-           (int)fa_bwd_workspace_size(2, 4, 100, 128, FA_DTYPE_BF16), 2 * 2 * 4 * 100 * 4);
+           (int)fa_bwd_workspace_size(2, 4, 100, 128, FA_DTYPE_BF16, 1), 2 * 2 * 4 * 100 * 4);
+    expect("bwd workspace size, atomic dQ: + B*N*H*128 floats",
+           (int)fa_bwd_workspace_size(2, 4, 100, 128, FA_DTYPE_BF16, 0), 2 * 2 * 4 * 100 * 4 + 2 * 100 * 4 * 128 * 4);
     expect("kvcache workspace size > 0", fa_fwd_kvcache_workspace_size(2, 8, 2, 1, 4096, 128, 0) > 0, 1);
     expect("kvcache: head_dim 7 (size 0)", (int)fa_fwd_kvcache_workspace_size(2, 8, 2, 1, 4096, 7, 0), 0);
     printf("%s\n", fails ? "FAILED" : "all checks passed");

@@ -70,13 +70,13 @@ def bwd(L, **over):
     args = dict(q=FAKE[0], k=FAKE[1], v=FAKE[2], o=FAKE[3], lse=FAKE[4], do=FAKE[5], dq=FAKE[6],
                 dk=FAKE[7], dv=FAKE[8], ws=FAKE[9], wsb=1 << 20, cu_q=None, cu_k=None,
                 used_q=None, used_k=None, batch=1, heads=4, kv_heads=2, seqlen_q=128, seqlen_k=128, head_dim=128,
-                causal=1, left=-1, right=-1, scale=0.125, drop=0.0, seed=0, dtype=1, stream=None)
+                causal=1, left=-1, right=-1, scale=0.125, drop=0.0, seed=0, dtype=1, det=1, stream=None)
     args.update(over)
     return L.fa_bwd(args["q"], args["k"], args["v"], args["o"], args["lse"], args["do"], args["dq"],
                     args["dk"], args["dv"], args["ws"], args["wsb"], args["cu_q"], args["cu_k"],
                     args["used_q"], args["used_k"], args["batch"], args["heads"], args["kv_heads"], args["seqlen_q"], args["seqlen_k"],
                     args["head_dim"], args["causal"], args["left"], args["right"], args["scale"],
-                    args["drop"], args["seed"], args["dtype"], args["stream"])
+                    args["drop"], args["seed"], args["dtype"], args["det"], args["stream"])
 
 
 BAD_FWD = [
@@ -142,6 +142,10 @@ BAD_BWD = [
     (dict(heads=1 << 16, kv_heads=2), INVALID),
     (dict(wsb=2 * 4 * 4 * 128 - 4), WORKSPACE), (dict(wsb=0), WORKSPACE),
     (dict(drop=1.5), INVALID), (dict(drop=float("inf")), INVALID),
+    (dict(det=2), INVALID), (dict(det=-1), INVALID),
+    (dict(ws=ctypes.c_void_p(0x10008)), INVALID),       # workspace must be 16-byte aligned
+    # the atomic path needs the dQ accumulator too: the deterministic size is short
+    (dict(det=0, wsb=2 * 4 * 4 * 128), WORKSPACE),
 ]
 
 
@@ -153,24 +157,34 @@ def test_bwd_rejects_bad_arguments(L, over, code):
 @pytest.mark.parametrize("stage", [-1, 3, 100])
 def test_bwd_stage_rejects_unknown_stage(L, stage):
     args = [FAKE[i] for i in range(10)] + [1 << 20, None, None, None, None, 1, 4, 2, 128, 128, 128, 1, -1, -1,
-                                           0.125, 0.0, 0, 1, None]
+                                           0.125, 0.0, 0, 1, 1, None]
     assert L.fa_bwd_stage(stage, *args) == INVALID
 
 
 def test_bwd_stage_validates_like_fa_bwd(L):
-    args = [FAKE[i] for i in range(10)] + [16, None, None, None, None, 1, 4, 2, 128, 128, 128, 1, -1, -1,
-                                           0.125, 0.1, 7, 1, None]
-    for stage in range(3):
-        assert L.fa_bwd_stage(stage, *args) == WORKSPACE
+    for det in (0, 1):
+        args = [FAKE[i] for i in range(10)] + [16, None, None, None, None, 1, 4, 2, 128, 128, 128, 1, -1, -1,
+                                               0.125, 0.1, 7, 1, det, None]
+        for stage in range(3):
+            assert L.fa_bwd_stage(stage, *args) == WORKSPACE
 
 
 def test_workspace_size(L):
     f = L.fa_bwd_workspace_size
-    assert f(2, 8, 1000, 128, 1) == 2 * (2 * 8 * 1000 * 4)
-    assert f(1, 4, 128, 64, 0) == 2 * (4 * 128 * 4)
-    assert f(0, 4, 128, 64, 0) == 4  # never zero for valid sizes
-    assert f(1, 4, 128, 96, 0) == 2 * (4 * 128 * 4) and f(1, 4, 128, 8, 1) == 2 * (4 * 128 * 4)
-    assert f(1, 4, 128, 100, 0) == 0 and f(1, 0, 128, 64, 0) == 0 and f(1, 4, 128, 64, 7) == 0
+    # deterministic: D and lse2, one float per (row, head) each
+    assert f(2, 8, 1000, 128, 1, 1) == 2 * (2 * 8 * 1000 * 4)
+    assert f(1, 4, 128, 64, 0, 1) == 2 * (4 * 128 * 4)
+    assert f(0, 4, 128, 64, 0, 1) == 4 and f(0, 4, 128, 64, 0, 0) == 4  # never zero for valid sizes
+    assert f(1, 4, 128, 96, 0, 1) == 2 * (4 * 128 * 4) and f(1, 4, 128, 8, 1, 1) == 2 * (4 * 128 * 4)
+    assert f(1, 4, 128, 100, 0, 1) == 0 and f(1, 0, 128, 64, 0, 1) == 0 and f(1, 4, 128, 64, 7, 1) == 0
+    assert f(1, 4, 128, 64, 0, 2) == 0 and f(1, 4, 128, 64, 0, -1) == 0
+    # atomic dQ: first a float32 accumulator of the tile width (64 or 128), padded to 256 bytes
+    acc = lambda rows, w: -(-rows * w * 4 // 256) * 256
+    assert f(2, 8, 1000, 128, 1, 0) == acc(2 * 8 * 1000, 128) + 2 * (2 * 8 * 1000 * 4)
+    assert f(1, 4, 128, 96, 0, 0) == acc(4 * 128, 128) + 2 * (4 * 128 * 4)
+    assert f(1, 3, 5, 8, 0, 0) == acc(15, 64) + 2 * (15 * 4)
+    # head_dim above 128 always runs the separate dQ pass: no accumulator
+    assert f(1, 4, 128, 256, 1, 0) == f(1, 4, 128, 256, 1, 1) == 2 * (4 * 128 * 4)
 
 
 @no_gpu
