@@ -24,7 +24,7 @@ __all__ = [
     "FaError", "lib", "forward", "backward", "Plan", "flash_attn_func",
     "flash_attn_varlen_func", "workspace_size", "FA_DTYPE_F16", "FA_DTYPE_BF16",
     "forward_kvcache", "kvcache_workspace_size", "kvcache_splits", "DecodePlan",
-    "flash_attn_with_kvcache", "new_dropout_seed", "forward_fp8", "Fp8Plan",
+    "flash_attn_with_kvcache", "new_dropout_seed", "forward_fp8", "Fp8Plan", "backward_noalloc",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd.restype = I
     L.fa_bwd_stage.argtypes = [I] + [P] * 10 + [S] + [P] * 4 + [I] * 9 + [F, F, U64, I, I, P]
     L.fa_bwd_stage.restype = I
+    L.fa_bwd_noalloc.argtypes = [P] * 13 + [I] * 9 + [F, F, U64, I, P]
+    L.fa_bwd_noalloc.restype = I
     L.fa_fwd_fp8.argtypes = [P] * 9 + [I] * 9 + [F, F, F, F, I, P]
     L.fa_fwd_fp8.restype = I
     L.fa_fwd_kvcache_workspace_size.argtypes = [I] * 7
@@ -344,6 +346,35 @@ def backward(dout, q, k, v, out, lse, *, causal=False, window_size=(-1, -1),
                   _dtype_code(q), det, _stream(q.device))
     if rc != 0:
         raise FaError(rc, "fa_bwd")
+    return dq, dk, dv
+
+
+def backward_noalloc(dout, q, k, v, out, lse, dq, dk, dv, *, causal=False, window_size=(-1, -1),
+                     softmax_scale=None, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
+                     max_seqlen_k=None, dropout_p=0.0, dropout_seed=0, seqused_q=None, seqused_k=None):
+    """fa_bwd_noalloc: the deterministic backward into caller-given dq, dk, dv
+    with the library's own per-device workspace (no allocation by the library
+    or here; batch * heads * seqlen_q at most 2^21; overlapping calls on one
+    GPU race, see include/fa.h)."""
+    L = lib()
+    dt = q.dtype
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(t, name, dt, q.device)
+    _check(lse, "lse", torch.float32, q.device)
+    g = _Geom(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    for name, t, like in (("out", out, q), ("dout", dout, q), ("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.shape != like.shape:
+            raise ValueError(f"{name} must have the shape of {'q' if like is q else 'k'}")
+    if tuple(lse.shape) != g.lse_shape:
+        raise ValueError(f"lse must have shape {g.lse_shape}")
+    rc = L.fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                          _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(seqused_q), _ptr(seqused_k),
+                          g.batch, g.heads, g.kv_heads, g.seqlen_q, g.seqlen_k, g.d,
+                          int(bool(causal)), int(window_size[0]), int(window_size[1]),
+                          _default_scale(g.d, softmax_scale), float(dropout_p), _seed(dropout_seed),
+                          _dtype_code(q), _stream(q.device))
+    if rc != 0:
+        raise FaError(rc, "fa_bwd_noalloc")
     return dq, dk, dv
 
 

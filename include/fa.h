@@ -240,6 +240,25 @@ int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const v
                  void* stream);
 
 /*
+ * fa_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (work being captured into a HIP graph, serving loops,
+ * harnesses that forbid allocation).  The workspace is a 16 MiB array inside
+ * the library, one per device, held until the process ends; the call
+ * allocates nothing.  Runs the deterministic path (deterministic = 1).
+ * Limit: batch * heads * seqlen_q <= 2^21 (two float32 per query row and
+ * head), FA_ERR_WORKSPACE beyond it.  All calls on one device share the
+ * array, so calls that overlap on one GPU (other streams or threads) race:
+ * the caller orders them.  Arguments and errors otherwise as for fa_bwd.
+ */
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                   const int32_t* seqused_q, const int32_t* seqused_k,
+                   int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
+                   int head_dim, int causal, int window_left, int window_right,
+                   float softmax_scale, float dropout_p, uint64_t dropout_seed, int dtype, void* stream);
+
+/*
  * Decode over a key/value cache (the KV-cache call named on the overview
  * page, section 3.3, for incremental inference): the same exact attention
  * as fa_fwd for a few new query tokens per sequence against a long cache.

@@ -37,7 +37,7 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_fwd",
+    assert declared_functions() == ["fa_bwd", "fa_bwd_noalloc", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_fwd",
                                     "fa_fwd_fp8", "fa_fwd_kvcache", "fa_fwd_kvcache_splits",
                                     "fa_fwd_kvcache_workspace_size", "fa_strerror", "fa_version"]
 
