@@ -13,6 +13,14 @@
 //    shader clock read beside the fixed 100 MHz real-time counter: the
 //    matrix-core rate the chip sustains under load, and its clock, as a
 //    measured denominator next to the published peak.
+//  * Matrix cores fed from LDS: every MFMA takes its A operand from a 1 KiB
+//    LDS read of its own, the ratio of the attention kernels' products for 32
+//    query rows per wave, with one or two waves per SIMD and the reads issued
+//    1, 2 or 4 MFMAs ahead.
+//  * Pipe mix: the two waves of each SIMD given different work (idle, MFMA
+//    chains from registers or from LDS, independent FMA chains, independent
+//    exp2 chains), to see which pairs overlap and at what vector rate one and
+//    two waves issue.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -122,6 +130,133 @@ __global__ __launch_bounds__(512) void calib_mfma_kernel(float* __restrict__ sin
     }
 }
 
+// Records the shader clock and the 100 MHz real-time counter at the start and
+// end of wave 0 of the workgroup (the kernel's clock under its own load).
+struct ClockPair {
+    uint64_t c0 = 0, r0 = 0;
+    __device__ void start() {
+        if (threadIdx.x == 0) {
+            c0 = __builtin_amdgcn_s_memtime();
+            r0 = __builtin_amdgcn_s_memrealtime();
+        }
+    }
+    __device__ void stop(uint64_t* clocks) {
+        if (threadIdx.x == 0) {
+            const uint64_t c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+            clocks[4 * blockIdx.x + 0] = c0;
+            clocks[4 * blockIdx.x + 1] = c1;
+            clocks[4 * blockIdx.x + 2] = r0;
+            clocks[4 * blockIdx.x + 3] = r1;
+        }
+    }
+};
+
+// 64 KiB of LDS as 64 blocks of 1 KiB, filled with bf16 values near 1.
+__device__ __forceinline__ void fill_lds(uint32_t* lds) {
+    for (int i = threadIdx.x; i < 16384; i += blockDim.x) lds[i] = 0x3F803F80u ^ (uint32_t)(i & 7);
+    __syncthreads();
+}
+// Wave w's 16-byte operand of step s: block (s + 5 w) mod 64, lane order
+// (conflict-free).
+__device__ __forceinline__ u32x4 lds_operand(const uint32_t* lds, int s, int w, int lane) {
+    return *(const u32x4*)&lds[(((s + w * 5) & 63) * 256) + lane * 4];
+}
+
+// 4 WPE waves (WPE per SIMD), each `iters` x 16 MFMAs over 4 accumulator
+// chains; MFMA k takes A from LDS read k, issued PF MFMAs earlier.
+template <int WPE, int PF>
+__global__ __attribute__((amdgpu_flat_work_group_size(256 * WPE, 256 * WPE), amdgpu_waves_per_eu(WPE, WPE)))
+void calib_lds_mfma_kernel(float* __restrict__ sink, uint64_t* __restrict__ clocks, int iters) {
+    __shared__ __attribute__((aligned(16))) uint32_t lds[16384];
+    ClockPair ck;
+    ck.start();
+    fill_lds(lds);
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    f32x16 acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = f32x16{0};
+    const bf16x8 b = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F81u, 0x3F803F80u, 0x3F803F80u});
+    u32x4 ring[PF + 1];
+#pragma unroll
+    for (int p = 0; p < PF; ++p) ring[p] = lds_operand(lds, p, w, lane);
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            ring[(s + PF) % (PF + 1)] = lds_operand(lds, it * 16 + s + PF, w, lane);
+            acc[s % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ring[s % (PF + 1)]), b,
+                                                                 acc[s % 4], 0, 0, 0);
+        }
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sum += acc[i][j];
+    sink[(int64_t)blockIdx.x * 512 + t] = sum;
+    ck.stop(clocks);
+}
+
+// Waves 0-3 run role RA, waves 4-7 (the same four SIMDs) role RB:
+//   0 idle; 1 MFMA, register operands, 4 chains, iters_m x 16 MFMAs;
+//   2 the same with a 1 KiB LDS read per MFMA, 4 ahead;
+//   3 16 independent FMA chains, iters_v x 16 FMAs;
+//   4 16 independent exp2 chains, iters_v x 16 exponentials.
+template <int RA, int RB>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void calib_mix_kernel(float* __restrict__ sink, uint64_t* __restrict__ clocks, int iters_m, int iters_v, float c) {
+    __shared__ __attribute__((aligned(16))) uint32_t lds[16384];
+    ClockPair ck;
+    ck.start();
+    fill_lds(lds);
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int role = w < 4 ? RA : RB;
+    float out = 0.f;
+    if (role == 1 || role == 2) {
+        f32x16 acc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = f32x16{0};
+        const bf16x8 b = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F81u, 0x3F803F80u, 0x3F803F80u});
+        const u32x4 areg = {0x3F803F80u, 1u, 2u, 3u};
+        u32x4 ring[5];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) ring[p] = role == 2 ? lds_operand(lds, p, w, lane) : areg;
+        for (int it = 0; it < iters_m; ++it) {
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                if (role == 2) ring[(s + 4) % 5] = lds_operand(lds, it * 16 + s + 4, w, lane);
+                const u32x4 a = role == 2 ? ring[s % 5] : areg;
+                acc[s % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), b, acc[s % 4], 0,
+                                                                     0, 0);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) out += acc[i][j];
+    } else if (role == 3 || role == 4) {
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = lane * 0.001f + i;
+        for (int it = 0; it < iters_v; ++it) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) x[i] = role == 3 ? __builtin_fmaf(x[i], c, 0.5f) : __builtin_amdgcn_exp2f(x[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) out += x[i];
+    }
+    sink[(int64_t)blockIdx.x * 512 + t] = out;
+    ck.stop(clocks);
+}
+
+template <int RA>
+int launch_mix(int rb, float* sink, uint64_t* clocks, int workgroups, int iters_m, int iters_v, hipStream_t st) {
+    void (*k)(float*, uint64_t*, int, int, float) = rb == 0   ? calib_mix_kernel<RA, 0>
+                                                    : rb == 3 ? calib_mix_kernel<RA, 3>
+                                                              : calib_mix_kernel<RA, 4>;
+    hipLaunchKernelGGL(k, dim3(workgroups), dim3(512), 0, st, sink, clocks, iters_m, iters_v, 0.999f);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
 }  // namespace
 
 extern "C" {
@@ -165,6 +300,48 @@ int fa_calib_lds(uint32_t* out, int workgroups, int iters, int transposing, void
     else
         hipLaunchKernelGGL(calib_lds_kernel<false>, dim3(workgroups), dim3(512), 0, (hipStream_t)stream, out, iters);
     return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// Matrix cores fed from LDS: `workgroups` workgroups of 4 * waves_per_simd
+// waves (1 or 2 per SIMD), each wave `iters` x 16 bf16 32x32x16 MFMAs, every
+// MFMA's A operand a 1 KiB LDS read of its own issued `prefetch` (1, 2 or 4)
+// MFMAs ahead.  sink (device): workgroups * 512 floats; clocks (device):
+// workgroups * 4 uint64 as for fa_calib_mfma.  Returns 0 when the launch was
+// accepted, 1 for bad arguments, 2 for a failed launch.
+int fa_calib_lds_mfma(float* sink, uint64_t* clocks, int workgroups, int iters, int waves_per_simd, int prefetch,
+                      void* stream) {
+    if (!sink || !clocks || workgroups < 1 || iters < 1) return 1;
+    if (waves_per_simd != 1 && waves_per_simd != 2) return 1;
+    if (prefetch != 1 && prefetch != 2 && prefetch != 4) return 1;
+    void (*k)(float*, uint64_t*, int) =
+        waves_per_simd == 1 ? (prefetch == 1 ? calib_lds_mfma_kernel<1, 1>
+                               : prefetch == 2 ? calib_lds_mfma_kernel<1, 2>
+                                               : calib_lds_mfma_kernel<1, 4>)
+                            : (prefetch == 1 ? calib_lds_mfma_kernel<2, 1>
+                               : prefetch == 2 ? calib_lds_mfma_kernel<2, 2>
+                                               : calib_lds_mfma_kernel<2, 4>);
+    hipLaunchKernelGGL(k, dim3(workgroups), dim3(256 * waves_per_simd), 0, (hipStream_t)stream, sink, clocks, iters);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// Pipe mix: `workgroups` workgroups of 8 waves; waves 0-3 take role_a, waves
+// 4-7 (same SIMDs) role_b.  Roles: 0 idle, 1 MFMA from registers and 2 MFMA
+// with an LDS read each (iters_m x 16 bf16 32x32x16 MFMAs per wave), 3 FMA
+// and 4 exp2 chains (iters_v x 16 per wave).  role_a in 0..4, role_b in
+// {0, 3, 4}.  sink and clocks as for fa_calib_lds_mfma.  Returns 0 when the
+// launch was accepted, 1 for bad arguments, 2 for a failed launch.
+int fa_calib_mix(float* sink, uint64_t* clocks, int workgroups, int iters_m, int iters_v, int role_a, int role_b,
+                 void* stream) {
+    if (!sink || !clocks || workgroups < 1 || iters_m < 0 || iters_v < 0) return 1;
+    if (role_a < 0 || role_a > 4 || (role_b != 0 && role_b != 3 && role_b != 4)) return 1;
+    hipStream_t st = (hipStream_t)stream;
+    switch (role_a) {
+        case 0: return launch_mix<0>(role_b, sink, clocks, workgroups, iters_m, iters_v, st);
+        case 1: return launch_mix<1>(role_b, sink, clocks, workgroups, iters_m, iters_v, st);
+        case 2: return launch_mix<2>(role_b, sink, clocks, workgroups, iters_m, iters_v, st);
+        case 3: return launch_mix<3>(role_b, sink, clocks, workgroups, iters_m, iters_v, st);
+        default: return launch_mix<4>(role_b, sink, clocks, workgroups, iters_m, iters_v, st);
+    }
 }
 
 }  // extern "C"

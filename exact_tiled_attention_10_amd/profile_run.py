@@ -30,6 +30,15 @@ Subcommands (run from anywhere; the repository root is found from this file):
           Run the matrix-core calibration (libfacalib.so: independent bf16
           32x32x16 and fp8 32x32x64 MFMA chains on every SIMD) and print the
           rate it sustains and the shader clock under that load.
+  ldsmfma [--workgroups G] [--iters N]
+          Run the LDS-fed matrix-core calibration (every MFMA with a 1 KiB LDS
+          read of its own; 1 and 2 waves per SIMD; reads 1, 2, 4 MFMAs ahead)
+          and print the rate each sustains, as a fraction of the matrix-core
+          peak at the clock measured during the run.
+  mix     [--workgroups G]
+          Run the pipe-mix calibration (the two waves of each SIMD given
+          idle / MFMA / FMA / exp2 work) and print each pair's time, its rates
+          per SIMD-cycle at the measured clock, and the times of its halves.
   trace   --db FILE --title T --command C
           Print a markdown table of a rocprofv3 kernel-trace database.
   util    --prefix P [--kernels fwd,dkdv,dq,fwd_fp8]
@@ -63,8 +72,10 @@ KERNEL_SOURCES = {
     "decode": ["fa_decode.hip", "fa_device.hpp"],
     "fwd_fp8": ["fa_fwd_fp8.hip", "fa_device.hpp"],
 }
-# Kernel-name substrings in rocprofv3 output.
-KERNEL_NAMES = {"fwd": "fwd_kernel", "rowdot": "bwd_rowdot_kernel", "dkdv": "bwd_dkdv_kernel",
+# Patterns (re.search) for the kernel names in rocprofv3 output.  The forward
+# is either of two kernels (two wave groups alternating matrix and vector
+# phases for head_dim <= 128, the single-group kernel above that).
+KERNEL_NAMES = {"fwd": r"fwd_(pp_)?kernel<", "rowdot": "bwd_rowdot_kernel", "dkdv": "bwd_dkdv_kernel",
                 "dq": "bwd_dq_kernel", "decode": "decode_split_kernel", "fwd_fp8": "fwd_fp8_kernel"}
 COPY_NAME = "calib_copy_kernel"
 CALIB_LIB = os.path.join(HERE, "libfacalib.so")
@@ -219,6 +230,107 @@ def _mfma(args):
         print(f"{'fp8' if fp8 else 'bf16'}: {tf:.1f} TFLOP/s sustained, shader clock {ghz:.3f} GHz", flush=True)
 
 
+def _calib_timed(fn, sink, clocks, reps=3):
+    """Median time (s) and shader clock (GHz) of `reps` launches of fn() after
+    one untimed launch; fn launches a calibration kernel writing `clocks`."""
+    import numpy as np
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    times, ghz = [], []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / 1e3)
+        c = clocks.cpu().numpy().view(np.uint64).reshape(-1, 4).astype(np.float64)
+        ok = c[:, 3] > c[:, 2]
+        ghz.append(float(np.median((c[ok, 1] - c[ok, 0]) / (c[ok, 3] - c[ok, 2]) * 0.1)))
+    return float(np.median(times)), float(np.median(ghz))
+
+
+def _calib_lib():
+    import ctypes
+    if not os.path.exists(CALIB_LIB):
+        raise RuntimeError(f"{CALIB_LIB} is not built; run `python -m exact_tiled_attention_10_amd.build`")
+    L = ctypes.CDLL(CALIB_LIB)
+    P, I = ctypes.c_void_p, ctypes.c_int
+    L.fa_calib_lds_mfma.argtypes = [P, P, I, I, I, I, P]
+    L.fa_calib_lds_mfma.restype = I
+    L.fa_calib_mix.argtypes = [P, P, I, I, I, I, I, P]
+    L.fa_calib_mix.restype = I
+    return L
+
+
+# gfx950 bf16 32x32x16 MFMA: 32768 FLOP in 32 cycles on one SIMD
+_MFMA_FLOP_PER_SIMD_CYCLE = 1024.0
+
+
+def _ldsmfma(args):
+    import ctypes
+    import torch
+    L = _calib_lib()
+    dev = torch.device("cuda:0")
+    sink = torch.empty(args.workgroups * 512, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(args.workgroups * 4, dtype=torch.int64, device=dev)
+    sp = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    print("| waves per SIMD | reads ahead | TFLOP/s | clock (GHz) | fraction of the matrix-core peak at that clock |")
+    print("|---|---|---|---|---|")
+    for wps in (1, 2):
+        for pf in (1, 2, 4):
+            def fn():
+                rc = L.fa_calib_lds_mfma(ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(clocks.data_ptr()),
+                                         args.workgroups, args.iters, wps, pf, sp)
+                if rc != 0:
+                    raise RuntimeError(f"fa_calib_lds_mfma returned {rc}")
+            t, ghz = _calib_timed(fn, sink, clocks)
+            flops = args.workgroups * 4.0 * wps * args.iters * 16 * 32768
+            frac = flops / t / (_SIMDS * _MFMA_FLOP_PER_SIMD_CYCLE * ghz * 1e9)
+            print(f"| {wps} | {pf} | {flops / t / 1e12:.0f} | {ghz:.3f} | {frac:.3f} |", flush=True)
+
+
+_ROLE = {0: "idle", 1: "MFMA (registers)", 2: "MFMA (1 KiB LDS read each)", 3: "FMA chains", 4: "exp2 chains"}
+
+
+def _mix(args):
+    import ctypes
+    import torch
+    L = _calib_lib()
+    dev = torch.device("cuda:0")
+    sink = torch.empty(args.workgroups * 512, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(args.workgroups * 4, dtype=torch.int64, device=dev)
+    sp = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    it_m, it_v = args.iters_mfma, args.iters_valu
+
+    def run(ra, rb):
+        def fn():
+            rc = L.fa_calib_mix(ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(clocks.data_ptr()),
+                                args.workgroups, it_m, it_v, ra, rb, sp)
+            if rc != 0:
+                raise RuntimeError(f"fa_calib_mix returned {rc}")
+        return _calib_timed(fn, sink, clocks)
+
+    alone = {}
+    for r in (1, 2, 3, 4):
+        alone[r] = run(r, 0)
+    print("| waves 0-3 (one per SIMD) | waves 4-7 (one per SIMD) | time (ms) | clock (GHz) | MFMA fraction of peak "
+          "| vector instructions per SIMD-cycle | sum of the halves alone (ms) |")
+    print("|---|---|---|---|---|---|---|")
+    for ra, rb in ((1, 0), (2, 0), (3, 0), (4, 0), (3, 3), (4, 4), (1, 3), (1, 4), (2, 3), (2, 4)):
+        t, ghz = run(ra, rb) if (ra, rb) not in ((r, 0) for r in alone) else alone[ra]
+        cyc = t * ghz * 1e9
+        mf = sum(4 for r in (ra, rb) if r in (1, 2)) * args.workgroups * it_m * 16 * 32768.0
+        vw = sum(4 for r in (ra, rb) if r in (3, 4)) * args.workgroups * it_v * 16.0
+        mfrac = mf / (_SIMDS * _MFMA_FLOP_PER_SIMD_CYCLE * cyc) if mf else 0.0
+        vrate = vw / (_SIMDS * cyc) if vw else 0.0
+        parts = [alone[r][0] for r in (ra, rb) if r]
+        print(f"| {_ROLE[ra]} | {_ROLE[rb]} | {1e3 * t:.3f} | {ghz:.3f} | {mfrac:.3f} | {vrate:.3f} | "
+              f"{1e3 * sum(parts):.3f} |", flush=True)
+
+
 LDS_NAME = "calib_lds_kernel"
 _LDS_WAVE_STEP_BYTES = 1024  # bytes one wave reads per step of the LDS calibration
 
@@ -268,7 +380,7 @@ def _ldscal(args):
 
 def _counter_per_dispatch(run_dir: str, name_sub: str, counter: str) -> list:
     """Per-dispatch values (summed over the rows rocprofv3 reports for one
-    dispatch) of `counter` for kernels whose name contains name_sub."""
+    dispatch) of `counter` for kernels whose name matches the pattern name_sub."""
     files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
     if not files:
         raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
@@ -276,7 +388,7 @@ def _counter_per_dispatch(run_dir: str, name_sub: str, counter: str) -> list:
     for path in files:
         with open(path) as fh:
             for r in csv.DictReader(fh):
-                if name_sub in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                if re.search(name_sub, r["Kernel_Name"]) and r["Counter_Name"] == counter:
                     per[r["Dispatch_Id"]] += float(r["Counter_Value"])
     if not per:
         raise ValueError(f"no {counter} rows for kernels matching {name_sub!r} in {run_dir}")
@@ -322,14 +434,14 @@ def _traffic(args):
 
 def _counters_mean(run_dir: str, name_sub: str) -> dict:
     """Mean per dispatch of every counter rocprofv3 recorded for kernels whose
-    name contains name_sub (fwd_kernel excludes the FP8 forward)."""
+    name matches the pattern name_sub."""
     files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
     tot, disp = defaultdict(float), defaultdict(set)
     for path in files:
         with open(path) as fh:
             for r in csv.DictReader(fh):
                 kn = r["Kernel_Name"]
-                if name_sub not in kn or (name_sub == "fwd_kernel" and "fp8" in kn):
+                if not re.search(name_sub, kn):
                     continue
                 tot[r["Counter_Name"]] += float(r["Counter_Value"])
                 disp[r["Counter_Name"]].add(r["Dispatch_Id"])
@@ -429,6 +541,13 @@ def main(argv=None):
     u = sub.add_parser("util")
     u.add_argument("--prefix", required=True, help="counter run directories <prefix>_<kernel>_1 and _2")
     u.add_argument("--kernels", default="fwd,dkdv,dq,fwd_fp8")
+    lm = sub.add_parser("ldsmfma")
+    lm.add_argument("--workgroups", type=int, default=256)
+    lm.add_argument("--iters", type=int, default=2000)
+    mx = sub.add_parser("mix")
+    mx.add_argument("--workgroups", type=int, default=256)
+    mx.add_argument("--iters-mfma", type=int, default=500)
+    mx.add_argument("--iters-valu", type=int, default=2000)
     tr = sub.add_parser("trace")
     tr.add_argument("--db", required=True)
     tr.add_argument("--title", required=True)
@@ -437,7 +556,7 @@ def main(argv=None):
     tr.add_argument("--bench-log", default=None)
     args = ap.parse_args(argv)
     {"run": _run, "copy": _copy, "lds": _lds, "ldscal": _ldscal, "traffic": _traffic, "trace": _trace,
-     "util": _util, "mfma": _mfma}[args.cmd](args)
+     "util": _util, "mfma": _mfma, "ldsmfma": _ldsmfma, "mix": _mix}[args.cmd](args)
 
 
 if __name__ == "__main__":
