@@ -1,8 +1,9 @@
 """Pins of the fp64 oracle against facts fixed by the mathematics, not by the
-oracle itself: closed forms, a 50-digit brute force, a library routine
-(torch's fp64 CPU attention with an explicit boolean mask), central finite
-differences for the backward, invariants, and reductions of GQA / packed
-batches / wide windows to simpler calls.
+oracle itself: closed forms, a 50-digit brute force, a torch fp64 CPU
+composition of the definition differentiated by autograd (for the backward an
+independent derivation of the gradient), central finite differences for the
+backward, invariants, and reductions of GQA / packed batches / wide windows to
+simpler calls.
 
 Exact attention is defined on the FlashAttention-2 overview page
 (lshu.cn/news/55956), section 2.1 (score matrix, row softmax, weighted sum of
@@ -74,7 +75,7 @@ CASES = [
 
 
 @pytest.mark.parametrize("case", CASES)
-def test_matches_torch_fp64_library_attention(oracle_mod, case):
+def test_matches_torch_autograd_composition(oracle_mod, case):
     b, nq, nk, h, hk, d, causal, left, right = case
     q = rnd((b, nq, h, d), 1)
     k = rnd((b, nk, hk, d), 2)
