@@ -181,6 +181,11 @@ def time_plan(plan, steps: int, warmup: int, torch):
             "stages": [[x[i] for x in per] for i in range(1, 4)]}
 
 
+def note(msg):
+    """One progress line on stderr (the JSON line alone goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def workload_entry(p, t, peak_meas):
     """fwd / bwd times and rates of one workload from time_plan's result."""
     pairs = visible_pairs(p)
@@ -290,6 +295,7 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    note(f"main step: {WORKLOAD}, {args.steps} timed steps after {args.warmup}")
     p = synth.workload(WORKLOAD)
     q, k, v, do = (t.to(dev) for t in (p.q, p.k, p.v, p.do))
     plan = fa.Plan(q, k, v, do, causal=p.causal, window_size=(p.window_left, p.window_right),
@@ -333,6 +339,7 @@ def main():
     }
     peak = None
     if not args.no_peak:
+        note("matrix-core calibration")
         from exact_tiled_attention_10_amd.profile_run import mfma_peak
         tf16, ghz16 = mfma_peak(False)
         tf8, ghz8 = mfma_peak(True)
@@ -410,6 +417,7 @@ def main():
     if not args.no_workloads:
         wl = {}
         for name, steps in OTHER_WORKLOADS:
+            note(f"workload {name}")
             pw = synth.workload(name)
             plan_w = make_plan(fa, pw, dev)
             wl[name] = workload_entry(pw, time_plan(plan_w, steps, 2, torch), pk16)
@@ -419,6 +427,7 @@ def main():
         # the opt-in atomic-dQ backward on the 8K and 32K shapes, same process
         at = {}
         for name, steps in ((WORKLOAD, K), ("bf16_causal_gqa_b1_h32kv8_n32768_d128", 5)):
+            note(f"atomic-dQ backward on {name}")
             pw = p if name == WORKLOAD else synth.workload(name)
             plan_a = make_plan(fa, pw, dev, deterministic=False)
             ta = time_plan(plan_a, steps, 2, torch)
@@ -437,13 +446,17 @@ def main():
             torch.cuda.empty_cache()
         out["atomic_dq"] = at
     if not args.no_dropout:
+        note("dropout step")
         out["dropout"] = bench_dropout(fa, p, q, k, v, do, K, args.warmup, fwd_flops + bwd_flops, torch)
     if not args.no_fp8:
+        note("fp8 forward")
         out["fp8"] = bench_fp8(fa, synth, torch, max(K, 20), max(args.warmup, 3), measured_traffic)
     if not args.no_decode:
+        note("decode")
         out["decode"] = bench_decode(fa, synth, torch, max(K, 20), max(args.warmup, 3), measured_traffic)
     if not args.no_cpu_baseline:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+        note(f"cpu baseline (oracle, {threads} threads)")
         out["cpu_baseline"] = cpu_baseline(p, threads)
     print(json.dumps(out), flush=True)
 

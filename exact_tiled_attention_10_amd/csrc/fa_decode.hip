@@ -261,10 +261,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecArgs a) {
                     sacc[i] = (key < lo_q || key > hi_q) ? kNegInf : sacc[i];
                 }
             }
-            float mx = kNegInf;
-#pragma unroll
-            for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[i], sacc[i + 1]));
-            mx = max_halves(mx);
+            float mx = max_halves(max16(sacc, kNegInf));
             const bool up = (mx > m_run) & ((m_run == kNegInf) | ((mx - m_run) * c > kDecLazyLog2));
             if (__builtin_amdgcn_ballot_w64(up)) {
                 const float alpha = !up ? 1.f : (m_run == kNegInf ? 0.f : fast_exp2((m_run - mx) * c));

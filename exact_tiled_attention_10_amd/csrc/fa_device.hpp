@@ -82,6 +82,16 @@ __device__ __forceinline__ float sum_halves(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// m folded with the 16 values of a C-tile register block as a chain of
+// three-way maxima: one v_max3_f32 per pair, where a running max of pairwise
+// maxima compiles to twice as many instructions.  The maximum of a set does
+// not depend on the order it is taken in (no NaNs reach it).
+__device__ __forceinline__ float max16(const f32x16& s, float m) {
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) m = fmaxf(fmaxf(m, s[i]), s[i + 1]);
+    return m;
+}
+
 // Position, inside a row of the permuted LDS layout, of the 4-element chunk
 // holding rows 4*c .. 4*c+3 of a tile: chunks 1 and 2 of every 4 swap places.
 __device__ __forceinline__ int perm_chunk_pos(int c) {

@@ -253,9 +253,7 @@ void fwd_kernel(FwdArgs a) {
         for (int qb = 0; qb < QB; ++qb) {
             float mx = kNegInf;
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[kb][qb][i], sacc[kb][qb][i + 1]));
+            for (int kb = 0; kb < KB; ++kb) mx = max16(sacc[kb][qb], mx);
             mx = max_halves(mx);
             const float m_old = m_run[qb];
             const bool up = mx > m_old && (m_old == kNegInf || (mx - m_old) * c > kLazyLog2);

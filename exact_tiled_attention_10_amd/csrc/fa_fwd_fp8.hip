@@ -271,9 +271,7 @@ void fwd_fp8_kernel(Fp8Args a8) {
         // ---- online softmax, P rounded to E4M3 ----------------------------------------
         float mx = kNegInf;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[kb][i], sacc[kb][i + 1]));
+        for (int kb = 0; kb < KB; ++kb) mx = max16(sacc[kb], mx);
         mx = max_halves(mx);
         const float m_old = m_run;
         const bool up = mx > m_old && (m_old == kNegInf || (mx - m_old) * c > kLazyLog2F8);
