@@ -476,26 +476,32 @@ def _util(args):
 
 
 def _trace(args):
+    """Per (kernel, grid) launch statistics of a rocprofv3 kernel-trace
+    database: one kernel template serves several workloads, told apart by
+    their grids."""
     c = sqlite3.connect(args.db)
-    rows = list(c.execute("select name, total_calls, total_duration, average, percentage from top_kernels"))
     durs = defaultdict(list)
     info = {}
-    for r in c.execute("select name, duration, grid_x, grid_y, grid_z, workgroup_x, lds_size, scratch_size, "
-                       "vgpr_count, accum_vgpr_count from kernels order by start"):
-        durs[r[0]].append(r[1])
-        info[r[0]] = r[2:]
+    for r in c.execute("select name, duration, grid_x, grid_y, grid_z, workgroup_x, lds_size, scratch_size "
+                       "from kernels order by start"):
+        key = (r[0], r[2], r[3], r[4])
+        durs[key].append(r[1])
+        info[key] = r[5:]
+    total = sum(sum(v) for v in durs.values())
     out = [f"# {args.title}", "", "Commands (from the repository root):", "", "```", args.command, "```", "",
-           f"Per kernel: all calls, and the mean of the last {args.last} (the timed steps).", "",
-           f"| kernel | calls | avg (us) | avg last {args.last} (us) | % | grid | WG | LDS (B) | scratch (B) |",
+           "Per kernel and grid (a grid identifies the workload): all calls, and the mean of the last "
+           f"{args.last} (the timed calls).", "",
+           f"| kernel | grid | calls | avg (us) | avg last {args.last} (us) | % of traced time | WG | LDS (B) | "
+           "scratch (B) |",
            "|---|---|---|---|---|---|---|---|---|"]
-    for n, calls, tot, avg, pct in rows:
-        g = info.get(n)
+    for key in sorted(durs, key=lambda k: -sum(durs[k])):
+        n, gx, gy, gz = key
+        d = durs[key]
         short = n.replace("fa::(anonymous namespace)::", "").replace("void ", "")
-        last = durs[n][-args.last:]
-        lavg = sum(last) / len(last) / 1e3  # ns -> us
-        gs = f"{g[0]}x{g[1]}x{g[2]}" if g else ""
-        rest = " | ".join(str(x) for x in g[3:6]) if g else " | " * 2
-        out.append(f"| `{short}` | {calls} | {avg:.1f} | {lavg:.1f} | {pct:.1f} | {gs} | {rest} |")
+        last = d[-args.last:]
+        wg, lds, scr = info[key]
+        out.append(f"| `{short}` | {gx}x{gy}x{gz} | {len(d)} | {sum(d) / len(d) / 1e3:.1f} | "
+                   f"{sum(last) / len(last) / 1e3:.1f} | {100 * sum(d) / total:.1f} | {wg} | {lds} | {scr} |")
     if args.bench_log:
         with open(args.bench_log) as fh:
             line = next((l for l in fh if l.startswith('{"metric"')), None)
@@ -507,6 +513,11 @@ def _trace(args):
                 summary["decode"] = {k: d["decode"][k] for k in ("workload", "ms_per_call", "achieved", "unit")}
             if d.get("fp8"):
                 summary["fp8"] = {k: d["fp8"][k] for k in ("workload", "ms", "achieved", "unit")}
+            if d.get("workloads"):
+                summary["workloads_median_ms"] = {n: {ph: w[ph]["ms"]["median"] for ph in ("fwd", "bwd")}
+                                                  for n, w in d["workloads"].items()}
+            if d.get("atomic_dq"):
+                summary["atomic_dq_bwd_median_ms"] = {n: e["bwd_ms"]["median"] for n, e in d["atomic_dq"].items()}
             out += ["", "bench.py line of the same run (HIP-event kernel times, ms):", "", "```",
                     json.dumps(summary), "```"]
     print("\n".join(out))
