@@ -26,7 +26,10 @@ FLAGS = [
 
 
 # Kernel sources only: they never form a NaN (masked scores are -inf and every
-# -inf - -inf is guarded), so the max reductions need no NaN canonicalisation.
+# -inf - -inf is guarded; probabilities recomputed from the saved LSE are
+# clamped to [0, 1] by the exponential's output clamp, so a masked key's score
+# cannot overflow into inf * 0), so the max reductions need no NaN
+# canonicalisation.
 # The C-ABI front end keeps full IEEE semantics (it rejects NaN scales).
 KERNEL_FLAGS = ["-fno-honor-nans"]
 # Per-source extras.  The decode kernel keeps its accumulators in VGPRs:

@@ -286,8 +286,8 @@ void bwd_dq_kernel(BwdArgs a) {
         };
         auto pair = [&](int kb, int m) {  // P, dS of registers 2m, 2m + 1 of block kb
             const int i = 2 * m;
-            float p0 = fast_exp2(__builtin_fmaf(sacc[kb][i], c, -lse2));
-            float p1 = fast_exp2(__builtin_fmaf(sacc[kb][i + 1], c, -lse2));
+            float p0 = exp2_prob(__builtin_fmaf(sacc[kb][i], c, -lse2));
+            float p1 = exp2_prob(__builtin_fmaf(sacc[kb][i + 1], c, -lse2));
             if (masked) {
                 const int k0 = kb * 32 + 8 * (i / 4) + 4 * half + (i % 4);
                 p0 = (k0 < lo || k0 > hi) ? 0.f : p0;
@@ -564,7 +564,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const int i = 2 * m + t;
-                const float pr = fast_exp2(__builtin_fmaf(sacc[qb][i], c, -l4[qb][i / 4][i % 4]));
+                const float pr = exp2_prob(__builtin_fmaf(sacc[qb][i], c, -l4[qb][i / 4][i % 4]));
                 if constexpr (DROP) {
                     const bool kp = keep_byte(kwd[i / 4], i % 4, a.drop_t);
                     pv[t] = kp ? pr : 0.f;
@@ -887,7 +887,7 @@ void bwd_pc_kernel(BwdArgs a) {
 #pragma unroll
                 for (int t2 = 0; t2 < 2; ++t2) {
                     const int i = 2 * m + t2;
-                    const float pr = fast_exp2(__builtin_fmaf(cur.s[i], c, -l4[i / 4][i % 4]));
+                    const float pr = exp2_prob(__builtin_fmaf(cur.s[i], c, -l4[i / 4][i % 4]));
                     if constexpr (DROP) {
                         const bool kp = keep_byte(kwd[i / 4], i % 4, a.drop_t);
                         pv[t2] = kp ? pr : 0.f;

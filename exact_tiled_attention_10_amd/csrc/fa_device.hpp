@@ -81,6 +81,16 @@ __device__ __forceinline__ float sum_halves(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// A probability recomputed from the saved log-sum-exp, exp2(x) clamped to
+// [0, 1] by the instruction's own output clamp (v_exp_f32 ... clamp, no extra
+// instruction).  For every visible key x <= 0 up to rounding, so the clamp
+// changes nothing but an overshoot of the last bit; for a key masked out of an
+// edge tile the row's LSE does not cover its score, and without the clamp the
+// exponential could overflow to +inf and meet a zero factor before the mask
+// removes it.
+__device__ __forceinline__ float exp2_prob(float x) {
+    return __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(x), 0.f, 1.f);
+}
 
 // m folded with the 16 values of a C-tile register block as a chain of
 // three-way maxima: one v_max3_f32 per pair, where a running max of pairwise

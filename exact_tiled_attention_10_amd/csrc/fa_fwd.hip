@@ -384,8 +384,8 @@ int launch_fwd(const FwdArgs& a, hipStream_t stream) {
     constexpr int B1 = FA_FWD_BN128, B2 = FA_FWD_BN64;
     // tile width: the smallest of 64, 128, 256 holding head_dim.  At 256 the
     // O accumulators (128 per lane) and the resident Q^T (64) need more than
-    // half the register file: 4 waves at one per SIMD, 64-key tiles (two
-    // 64 KiB LDS stages).
+    // half the register file: 4 waves at one per SIMD, 32-key tiles (K and V
+    // of a tile 32 KiB, two stages in 64 KiB of LDS).
     if (a.head_dim > 128)
         return a.bf16 ? launch_fwd_t<true, 256, 4, 1, 32, 1>(a, stream)
                       : launch_fwd_t<false, 256, 4, 1, 32, 1>(a, stream);

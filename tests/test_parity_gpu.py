@@ -164,6 +164,26 @@ def test_small_parity(fa, name, det):
     compare_full(fa, p, deterministic=det)
 
 
+@pytest.mark.parametrize("det", [False, True], ids=["atomic_dq", "dq_pass"])
+def test_masked_key_far_above_visible(fa, det):
+    """A key hidden by the causal mask from most rows, whose score lies far
+    above everything those rows can see: every query is 2.0 in every
+    component and key 150 is 40.0 in every component (exact in bf16), so at
+    d = 64 and scale 1/8 its score is 640 against visible scores of a few
+    units.  Rows before 150 share edge tiles with it in the backward, where
+    its probability is recomputed from their LSE: exp2 of about 900 overflows
+    fp32 unless the recomputed probability is clamped, and inf * 0 would
+    follow before the mask removes it.  Rows from 150 on see the key and put
+    almost all their weight on it."""
+    say(f"[parity] masked key far above visible deterministic={det}")
+    p = synth.make_problem(seed=11, dtype="bf16", batch=1, heads=2, kv_heads=1, seqlen=200, head_dim=64, causal=True)
+    p.q.fill_(2.0)
+    p.k[:, 150] = 40.0
+    g = compare_full(fa, p, deterministic=det)
+    for n, t in g.items():
+        assert np.isfinite(t[~np.isneginf(t)]).all(), n
+
+
 @pytest.mark.parametrize("name", ["causal_bf16_d64_gqa", "causal_bf16_d128", "varlen_causal_window_fp16_d128"])
 def test_repeatable_bytes(fa, name):
     """The deterministic path (separate dQ pass, no atomics): two runs on the
