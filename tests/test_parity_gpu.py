@@ -350,3 +350,41 @@ def test_full_size_workload(fa, name):
         # sum_j dS_ij = 0 for every row, so sum_j dK_j = 0 per (batch, kv head, column)
         sdk = dkg.sum(1)
         assert float(sdk.abs().max()) <= 1e-2 * float(dkg.abs().max()) * math.sqrt(p.seqlen_k)
+
+
+def test_long_sequence_131072(fa):
+    """One 131072-token sequence (bf16, causal, 4 query heads over 2 kv heads,
+    d = 64): tile counts, row offsets and LSE indices four times past the
+    largest named workload.  The oracle checks the forward and dQ on sampled
+    rows and dK/dV on the last 64 keys (the only rows that see them are the
+    last ones, so the oracle's work stays small); every key's dK and dV enter
+    the invariants sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i per kv head."""
+    say("[parity-long] 131072 tokens: generating inputs")
+    p = synth.make_problem(seed=21, dtype="bf16", batch=1, heads=4, kv_heads=2, seqlen=131072, head_dim=64,
+                           causal=True)
+    say("[parity-long] GPU forward+backward")
+    g = gpu_run(fa, p)
+    import oracle
+    n = p.seqlen_q
+    rows = sample_rows(n, 24, 3)
+    say("[parity-long] oracle forward on sampled rows")
+    o, lse = oracle.attention_fwd(p.q, p.k, p.v, rows=rows, heads=[0, 3], **okw(p))
+    eo = max_abs(g["o"], o)
+    el = check_lse(g["lse"], lse)
+    assert eo <= O_TOL[p.dtype], f"O max-abs {eo}"
+    qrows = sample_rows(n, 16, 4)
+    krows = np.arange(n - 64, n).astype(np.int32)
+    say("[parity-long] oracle backward on sampled rows and the last 64 keys")
+    dq, dk, dv, _, _ = oracle.attention_bwd(p.q, p.k, p.v, p.do, q_rows=qrows, k_rows=krows, kv_heads=[1], **okw(p))
+    errs = {nm: rel_l2(g[nm], r) for nm, r in (("dq", dq), ("dk", dk), ("dv", dv))}
+    assert all(e is not None for e in errs.values()), errs
+    say(f"[parity-long] O {eo:.2e} LSE {el:.2e} " + " ".join(f"{a} {b:.2e}" for a, b in errs.items()))
+    for nm, e in errs.items():
+        assert e <= GRAD_TOL, (nm, e)
+    dkg = torch.from_numpy(g["dk"])
+    dvg = torch.from_numpy(g["dv"])
+    sdv = dvg.sum(1)
+    want = p.do.double().reshape(1, n, 2, 2, 64).sum((1, 3))
+    assert float((sdv - want).norm() / want.norm()) <= GRAD_TOL
+    assert float(dkg.sum(1).abs().max()) <= 1e-2 * float(dkg.abs().max()) * math.sqrt(n)
+
