@@ -200,7 +200,11 @@ void calib_lds_mfma_kernel(float* __restrict__ sink, uint64_t* __restrict__ cloc
 //   0 idle; 1 MFMA, register operands, 4 chains, iters_m x 16 MFMAs;
 //   2 the same with a 1 KiB LDS read per MFMA, 4 ahead;
 //   3 16 independent FMA chains, iters_v x 16 FMAs;
-//   4 16 independent exp2 chains, iters_v x 16 exponentials.
+//   4 16 independent exp2 chains, iters_v x 16 exponentials;
+//   5 roles 1 and 3 in one wave: each MFMA followed by iters_v / iters_m FMAs
+//     (the same totals, interleaved in one instruction stream);
+//   6 the same with exp2 in place of the FMAs;
+//   7, 8 roles 5, 6 with each MFMA's A operand a 1 KiB LDS read, 4 ahead.
 template <int RA, int RB>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void calib_mix_kernel(float* __restrict__ sink, uint64_t* __restrict__ clocks, int iters_m, int iters_v, float c) {
@@ -233,6 +237,44 @@ void calib_mix_kernel(float* __restrict__ sink, uint64_t* __restrict__ clocks, i
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 16; ++j) out += acc[i][j];
+    } else if (role >= 5 && role <= 8) {
+        f32x16 acc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = f32x16{0};
+        const bf16x8 b = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F81u, 0x3F803F80u, 0x3F803F80u});
+        const u32x4 areg = {0x3F803F80u, 1u, 2u, 3u};
+        const bool from_lds = role >= 7, fma_work = role == 5 || role == 7;
+        u32x4 ring[5];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) ring[p] = from_lds ? lds_operand(lds, p, w, lane) : areg;
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = lane * 0.001f + i;
+        constexpr int PER = 4;  // vector instructions per MFMA (iters_v = 4 iters_m)
+        for (int it = 0; it < iters_m; ++it) {
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                // step s issues the operand read of step s + 4; fences keep each
+                // step's MFMA and vector work together and the reads ahead
+                if (from_lds) ring[(s + 4) % 5] = lds_operand(lds, it * 16 + s + 4, w, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                const u32x4 a = from_lds ? ring[s % 5] : areg;
+                acc[s % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), b, acc[s % 4], 0,
+                                                                     0, 0);
+#pragma unroll
+                for (int v = 0; v < PER; ++v) {
+                    float& y = x[(s * PER + v) % 16];
+                    y = fma_work ? __builtin_fmaf(y, c, 0.5f) : __builtin_amdgcn_exp2f(y);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) out += acc[i][j];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) out += x[i];
     } else if (role == 3 || role == 4) {
         float x[16];
 #pragma unroll
@@ -252,7 +294,11 @@ template <int RA>
 int launch_mix(int rb, float* sink, uint64_t* clocks, int workgroups, int iters_m, int iters_v, hipStream_t st) {
     void (*k)(float*, uint64_t*, int, int, float) = rb == 0   ? calib_mix_kernel<RA, 0>
                                                     : rb == 3 ? calib_mix_kernel<RA, 3>
-                                                              : calib_mix_kernel<RA, 4>;
+                                                    : rb == 4 ? calib_mix_kernel<RA, 4>
+                                                    : rb == 5 ? calib_mix_kernel<RA, 5>
+                                                    : rb == 6 ? calib_mix_kernel<RA, 6>
+                                                    : rb == 7 ? calib_mix_kernel<RA, 7>
+                                                              : calib_mix_kernel<RA, 8>;
     hipLaunchKernelGGL(k, dim3(workgroups), dim3(512), 0, st, sink, clocks, iters_m, iters_v, 0.999f);
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
@@ -327,20 +373,28 @@ int fa_calib_lds_mfma(float* sink, uint64_t* clocks, int workgroups, int iters, 
 // Pipe mix: `workgroups` workgroups of 8 waves; waves 0-3 take role_a, waves
 // 4-7 (same SIMDs) role_b.  Roles: 0 idle, 1 MFMA from registers and 2 MFMA
 // with an LDS read each (iters_m x 16 bf16 32x32x16 MFMAs per wave), 3 FMA
-// and 4 exp2 chains (iters_v x 16 per wave).  role_a in 0..4, role_b in
-// {0, 3, 4}.  sink and clocks as for fa_calib_lds_mfma.  Returns 0 when the
-// launch was accepted, 1 for bad arguments, 2 for a failed launch.
+// and 4 exp2 chains (iters_v x 16 per wave), 5 and 6 role 1 with the FMAs
+// (exp2s) of role 3 (4) interleaved in the same wave (iters_v must be
+// 4 iters_m), 7 and 8 the same with role 2's LDS reads.  role_a in 0..8,
+// role_b in 0 or 3..8.  sink and clocks
+// as for fa_calib_lds_mfma.  Returns 0 when the launch was accepted, 1 for
+// bad arguments, 2 for a failed launch.
 int fa_calib_mix(float* sink, uint64_t* clocks, int workgroups, int iters_m, int iters_v, int role_a, int role_b,
                  void* stream) {
     if (!sink || !clocks || workgroups < 1 || iters_m < 0 || iters_v < 0) return 1;
-    if (role_a < 0 || role_a > 4 || (role_b != 0 && role_b != 3 && role_b != 4)) return 1;
+    if (role_a < 0 || role_a > 8 || role_b < 0 || role_b > 8 || role_b == 1 || role_b == 2) return 1;
+    if ((role_a >= 5 || role_b >= 5) && iters_v != 4 * iters_m) return 1;
     hipStream_t st = (hipStream_t)stream;
     switch (role_a) {
         case 0: return launch_mix<0>(role_b, sink, clocks, workgroups, iters_m, iters_v, st);
         case 1: return launch_mix<1>(role_b, sink, clocks, workgroups, iters_m, iters_v, st);
         case 2: return launch_mix<2>(role_b, sink, clocks, workgroups, iters_m, iters_v, st);
         case 3: return launch_mix<3>(role_b, sink, clocks, workgroups, iters_m, iters_v, st);
-        default: return launch_mix<4>(role_b, sink, clocks, workgroups, iters_m, iters_v, st);
+        case 4: return launch_mix<4>(role_b, sink, clocks, workgroups, iters_m, iters_v, st);
+        case 5: return launch_mix<5>(role_b, sink, clocks, workgroups, iters_m, iters_v, st);
+        case 6: return launch_mix<6>(role_b, sink, clocks, workgroups, iters_m, iters_v, st);
+        case 7: return launch_mix<7>(role_b, sink, clocks, workgroups, iters_m, iters_v, st);
+        default: return launch_mix<8>(role_b, sink, clocks, workgroups, iters_m, iters_v, st);
     }
 }
 

@@ -292,7 +292,9 @@ def _ldsmfma(args):
             print(f"| {wps} | {pf} | {flops / t / 1e12:.0f} | {ghz:.3f} | {frac:.3f} |", flush=True)
 
 
-_ROLE = {0: "idle", 1: "MFMA (registers)", 2: "MFMA (1 KiB LDS read each)", 3: "FMA chains", 4: "exp2 chains"}
+_ROLE = {0: "idle", 1: "MFMA (registers)", 2: "MFMA (1 KiB LDS read each)", 3: "FMA chains", 4: "exp2 chains",
+         5: "MFMA + 4 FMAs each, one stream", 6: "MFMA + 4 exp2 each, one stream",
+         7: "LDS-fed MFMA + 4 FMAs each, one stream", 8: "LDS-fed MFMA + 4 exp2 each, one stream"}
 
 
 def _mix(args):
@@ -319,14 +321,18 @@ def _mix(args):
     print("| waves 0-3 (one per SIMD) | waves 4-7 (one per SIMD) | time (ms) | clock (GHz) | MFMA fraction of peak "
           "| vector instructions per SIMD-cycle | sum of the halves alone (ms) |")
     print("|---|---|---|---|---|---|---|")
-    for ra, rb in ((1, 0), (2, 0), (3, 0), (4, 0), (3, 3), (4, 4), (1, 3), (1, 4), (2, 3), (2, 4)):
+    for ra, rb in ((1, 0), (2, 0), (3, 0), (4, 0), (3, 3), (4, 4), (1, 3), (1, 4), (2, 3), (2, 4),
+                   (5, 0), (6, 0), (5, 5), (6, 6), (7, 0), (8, 0), (7, 7), (8, 8)):
         t, ghz = run(ra, rb) if (ra, rb) not in ((r, 0) for r in alone) else alone[ra]
         cyc = t * ghz * 1e9
-        mf = sum(4 for r in (ra, rb) if r in (1, 2)) * args.workgroups * it_m * 16 * 32768.0
-        vw = sum(4 for r in (ra, rb) if r in (3, 4)) * args.workgroups * it_v * 16.0
+        mf = sum(4 for r in (ra, rb) if r in (1, 2, 5, 6, 7, 8)) * args.workgroups * it_m * 16 * 32768.0
+        vw = sum(4 for r in (ra, rb) if r in (3, 4, 5, 6, 7, 8)) * args.workgroups * it_v * 16.0
         mfrac = mf / (_SIMDS * _MFMA_FLOP_PER_SIMD_CYCLE * cyc) if mf else 0.0
         vrate = vw / (_SIMDS * cyc) if vw else 0.0
-        parts = [alone[r][0] for r in (ra, rb) if r]
+        # a mixed role's halves are its MFMA part (role 1) and its vector part (3 or 4)
+        parts = [x for r in (ra, rb) if r
+                 for x in (((alone[2][0] if r >= 7 else alone[1][0]), alone[3 if r % 2 else 4][0])
+                           if r >= 5 else (alone[r][0],))]
         print(f"| {_ROLE[ra]} | {_ROLE[rb]} | {1e3 * t:.3f} | {ghz:.3f} | {mfrac:.3f} | {vrate:.3f} | "
               f"{1e3 * sum(parts):.3f} |", flush=True)
 
