@@ -709,6 +709,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
 // (their vmcnt waits count direct loads only); only consumers issue atomics.
 // ---------------------------------------------------------------------------
 constexpr int kPcBM = 64;  // query rows per streamed tile (two blocks)
+#ifndef FA_PC_DET
+#define FA_PC_DET 0
+#endif
 #ifndef FA_PC_PF
 #define FA_PC_PF 1
 #endif
@@ -1149,6 +1152,11 @@ int launch_bwd_t(const BwdArgs& a, int stage, hipStream_t stream) {
             if constexpr (D <= 128) {
                 if (a.dq_acc) {
                     auto kern = a.drop_t < 256 ? bwd_pc_kernel<BF16, D, true, true> : bwd_pc_kernel<BF16, D, false, true>;
+                    hipLaunchKernelGGL(kern, dim3(a.batch * a.kv_heads, ntiles), dim3(512), 0, stream, a);
+                    return hipGetLastError() == hipSuccess ? 0 : 1;
+                }
+                if (FA_PC_DET) {  // build-time switch for measurement: the separate-dQ path on the same kernel
+                    auto kern = a.drop_t < 256 ? bwd_pc_kernel<BF16, D, true, false> : bwd_pc_kernel<BF16, D, false, false>;
                     hipLaunchKernelGGL(kern, dim3(a.batch * a.kv_heads, ntiles), dim3(512), 0, stream, a);
                     return hipGetLastError() == hipSuccess ? 0 : 1;
                 }
