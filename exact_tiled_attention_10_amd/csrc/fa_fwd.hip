@@ -357,10 +357,12 @@ int launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
-// Launch shapes (measured on MI355X, bf16 causal): 8 waves of 32 query rows
-// (two waves per SIMD, all state in arch VGPRs) beat 4 waves of 64 rows, whose
-// accumulators spill into AGPR traffic; 64-key tiles suit d = 128, 128-key
-// tiles d = 64.  Overridable at build time for tuning.
+// Launch shapes (measured on MI355X, bf16 causal).  d = 128: 8 waves of 32
+// query rows (two waves per SIMD, all state in arch VGPRs) beat 4 waves of 64
+// rows, whose accumulators spill into AGPR traffic; 64-key tiles.  d = 64:
+// fewer registers per wave, so 4 waves of 32 rows with three workgroups per
+// CU (three waves per SIMD) and 64-key tiles.  Overridable at build time for
+// tuning.
 #ifndef FA_FWD_NW
 #define FA_FWD_NW 8
 #endif
@@ -370,18 +372,24 @@ int launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
 #ifndef FA_FWD_BN128
 #define FA_FWD_BN128 64
 #endif
-#ifndef FA_FWD_BN64
-#define FA_FWD_BN64 128
-#endif
 #ifndef FA_FWD_WPE
 #define FA_FWD_WPE 2
+#endif
+#ifndef FA_FWD64_NW
+#define FA_FWD64_NW 4
+#endif
+#ifndef FA_FWD_BN64
+#define FA_FWD_BN64 64
+#endif
+#ifndef FA_FWD64_WPE
+#define FA_FWD64_WPE 3
 #endif
 
 }  // namespace
 
 int launch_fwd(const FwdArgs& a, hipStream_t stream) {
-    constexpr int NW = FA_FWD_NW, QB = FA_FWD_QB, W = FA_FWD_WPE;
-    constexpr int B1 = FA_FWD_BN128, B2 = FA_FWD_BN64;
+    constexpr int NW = FA_FWD_NW, QB = FA_FWD_QB, W = FA_FWD_WPE, B1 = FA_FWD_BN128;
+    constexpr int NW2 = FA_FWD64_NW, W2 = FA_FWD64_WPE, B2 = FA_FWD_BN64;
     // tile width: the smallest of 64, 128, 256 holding head_dim.  At 256 the
     // O accumulators (128 per lane) and the resident Q^T (64) need more than
     // half the register file: 4 waves at one per SIMD, 32-key tiles (K and V
@@ -391,9 +399,9 @@ int launch_fwd(const FwdArgs& a, hipStream_t stream) {
                       : launch_fwd_t<false, 256, 4, 1, 32, 1>(a, stream);
     if (a.bf16)
         return a.head_dim > 64 ? launch_fwd_t<true, 128, NW, QB, B1, W>(a, stream)
-                               : launch_fwd_t<true, 64, NW, QB, B2, W>(a, stream);
+                               : launch_fwd_t<true, 64, NW2, QB, B2, W2>(a, stream);
     return a.head_dim > 64 ? launch_fwd_t<false, 128, NW, QB, B1, W>(a, stream)
-                           : launch_fwd_t<false, 64, NW, QB, B2, W>(a, stream);
+                           : launch_fwd_t<false, 64, NW2, QB, B2, W2>(a, stream);
 }
 
 }  // namespace fa
