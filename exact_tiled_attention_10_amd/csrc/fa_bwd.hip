@@ -381,6 +381,15 @@ constexpr int kKvBN = 32 * kKvWaves;  // keys per workgroup
 constexpr int kKvBM = 128;            // query rows per streamed tile
 constexpr int kKvQB = kKvBM / 32;     // 32-row blocks per tile
 
+// dK/dV waves per SIMD at width 64: two (with one k-step of operand reads
+// ahead, 256 registers), measured faster than one at 128 + 126 AGPRs.
+#ifndef FA_DKDV64_WPE
+#define FA_DKDV64_WPE 2
+#endif
+#ifndef FA_DKDV_PF_2W
+#define FA_DKDV_PF_2W 1
+#endif
+
 template <int D, int BMR>
 struct DkdvCfg {
     static constexpr int tileElems = BMR * D;
@@ -394,8 +403,8 @@ struct DkdvCfg {
 // the resident K^T / V^T do not fit the register file together: two
 // workgroups per key tile, each recomputing S and dP); BMR: query rows per
 // streamed tile (64 at width 256, so that two stages fit in LDS).
-template <bool BF16, int D, bool DROP, int DO, int BMR>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+template <bool BF16, int D, bool DROP, int DO, int BMR, int WPE>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(WPE, WPE)))
 void bwd_dkdv_kernel(BwdArgs a) {
     using C = DkdvCfg<D, BMR>;
     using Dma = TileDma<D, BMR, kKvWaves>;
@@ -503,7 +512,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
     // without any visible key give inf or NaN before the AND, never after.
     auto compute = [&](int n, int buf, bool full) {
         constexpr int QBS = (BMR / 32);
-        constexpr int kPf = 2;          // k-steps of operand reads ahead of their MFMAs
+        // k-steps of operand reads ahead of their MFMAs (one when a second
+        // wave per SIMD hides the LDS latency and the registers are short)
+        constexpr int kPf = WPE > 1 ? FA_DKDV_PF_2W : 2;
         constexpr int NJ = 4 * DB;      // dV, dK products per block
         constexpr int JPS = NJ / KS;    // dV, dK products per k-step
         constexpr int KPM = KS > 8 ? KS / 8 : 1;  // k-steps per softmax slot
@@ -1127,9 +1138,44 @@ void bwd_pc_kernel(BwdArgs a) {
     }
 }
 
+// dQ launch shapes (measured on MI355X, bf16 causal): NW waves of 32 query
+// rows, BN-key tiles, WPE waves per SIMD.  Width 128: 8 waves at two per SIMD,
+// 64-key tiles.  Width 64 without dropout: 4 waves at three per SIMD (168
+// registers), 64-key tiles; with dropout that shape spills, so it keeps 8
+// waves at two per SIMD with 128-key tiles.  Width 256: 4 waves at one per
+// SIMD, 32-key tiles (the resident Q, dO and the dQ accumulators take 256
+// registers per lane).  Overridable at build time for tuning.
 #ifndef FA_DQ_NW
 #define FA_DQ_NW 8
 #endif
+#ifndef FA_DQ64_NW
+#define FA_DQ64_NW 4
+#endif
+#ifndef FA_DQ64_BN
+#define FA_DQ64_BN 64
+#endif
+#ifndef FA_DQ64_WPE
+#define FA_DQ64_WPE 3
+#endif
+
+template <int D, bool DROP>
+struct DqShape {
+    static constexpr bool kNarrow = D == 64 && !DROP;
+    static constexpr int NW = D > 128 ? 4 : (kNarrow ? FA_DQ64_NW : FA_DQ_NW);
+    static constexpr int BN = D > 128 ? 32 : (kNarrow ? FA_DQ64_BN : (D == 128 ? 64 : 128));
+    static constexpr int WPE = D > 128 ? 1 : (kNarrow ? FA_DQ64_WPE : 2);
+};
+
+template <bool BF16, int D, bool DROP>
+int launch_dq(const BwdArgs& a, hipStream_t stream) {
+    using S = DqShape<D, DROP>;
+    constexpr int BM = 32 * S::NW;
+    const int ntiles = (a.seqlen_q + BM - 1) / BM;
+    if (ntiles == 0 || a.batch == 0) return 0;
+    hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, S::NW, S::BN, DROP, S::WPE>), dim3(a.batch * a.heads, ntiles),
+                       dim3(64 * S::NW), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? 0 : 1;
+}
 
 template <bool BF16, int D>
 int launch_bwd_t(const BwdArgs& a, int stage, hipStream_t stream) {
@@ -1162,8 +1208,9 @@ int launch_bwd_t(const BwdArgs& a, int stage, hipStream_t stream) {
                 }
             }
             constexpr int DO = D > 128 ? 128 : D, BMR = D > 128 ? 64 : kKvBM;
-            auto kern = a.drop_t < 256 ? bwd_dkdv_kernel<BF16, D, true, DO, BMR>
-                                       : bwd_dkdv_kernel<BF16, D, false, DO, BMR>;
+            constexpr int WPE = D == 64 ? FA_DKDV64_WPE : 1;
+            auto kern = a.drop_t < 256 ? bwd_dkdv_kernel<BF16, D, true, DO, BMR, WPE>
+                                       : bwd_dkdv_kernel<BF16, D, false, DO, BMR, WPE>;
             hipLaunchKernelGGL(kern, dim3(a.batch * a.kv_heads, ntiles, D / DO), dim3(256), 0, stream, a);
             if (hipGetLastError() != hipSuccess) return 1;
         }
@@ -1179,19 +1226,8 @@ int launch_bwd_t(const BwdArgs& a, int stage, hipStream_t stream) {
         }
         return 0;
     }
-    // stage 2: dQ (at width 256: 4 waves at one per SIMD, 32-key tiles; the
-    // resident Q, dO and the dQ accumulators take 256 registers per lane)
-    constexpr int NW = D > 128 ? 4 : FA_DQ_NW, BN = D > 128 ? 32 : (D == 128 ? 64 : 128);
-    constexpr int WPE = D > 128 ? 1 : 2;
-    constexpr int BM = 32 * NW;
-    const int ntiles = (a.seqlen_q + BM - 1) / BM;
-    if (ntiles > 0 && a.batch > 0) {
-        auto kern = a.drop_t < 256 ? bwd_dq_kernel<BF16, D, NW, BN, true, WPE>
-                                   : bwd_dq_kernel<BF16, D, NW, BN, false, WPE>;
-        hipLaunchKernelGGL(kern, dim3(a.batch * a.heads, ntiles), dim3(64 * NW), 0, stream, a);
-        if (hipGetLastError() != hipSuccess) return 1;
-    }
-    return 0;
+    // stage 2: dQ
+    return a.drop_t < 256 ? launch_dq<BF16, D, true>(a, stream) : launch_dq<BF16, D, false>(a, stream);
 }
 
 }  // namespace
