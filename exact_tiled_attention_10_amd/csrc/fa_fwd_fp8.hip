@@ -4,7 +4,7 @@
 // bf16 or fp16, LSE in fp32.
 //
 // The structure is the 16-bit forward's (fa_fwd.hip): one workgroup per
-// (batch, query head) and 256 query rows, 8 waves of 32 rows, the visible
+// (batch, query head) and 128 query rows, 4 waves of 32 rows, the visible
 // K/V tiles streamed through two LDS stages by direct global -> LDS loads,
 // S^T = K Q^T and O^T += V^T P^T on the matrix cores, the online softmax in
 // fp32 in between.  What changes with 8-bit operands:
@@ -30,8 +30,8 @@
 // * Scales.  The descales of Q and K fold into the softmax scale (the host
 //   passes scale = softmax_scale * dq * dk), the descale of V into the
 //   epilogue (O = dv * acc / l).
-// * Tiles.  128 keys per tile (two 64-key steps of P.V), 1 byte per element:
-//   two stages of K and V take 64 KiB at d = 128.  K and V have their own
+// * Tiles.  64 keys per tile (one 64-key step of P.V), 1 byte per element:
+//   two stages of K and V take 32 KiB at d = 128.  K and V have their own
 //   XOR swizzles of 16-byte chunks: the K operand reads (16 B per lane) and
 //   the transposing V reads (8 B per lane, 8 rows per 16 lanes) each spread
 //   over distinct bank groups.
@@ -95,8 +95,8 @@ struct F8Cfg {
     static_assert(kDmaBlocks % NW == 0, "tiles must split evenly into 1 KiB blocks per wave");
 };
 
-template <bool BF16, int D, int NW, int BN>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
+template <bool BF16, int D, int NW, int BN, int WPE>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(WPE, WPE)))
 void fwd_fp8_kernel(Fp8Args a8) {
     using C = F8Cfg<D, NW, BN>;
     constexpr int KS = D / 64;   // k-steps of S over d
@@ -359,14 +359,28 @@ void fwd_fp8_kernel(Fp8Args a8) {
     }
 }
 
+// Launch shape (measured on MI355X, causal, 8K, d = 128): 4 waves of 32 query
+// rows with 64-key tiles, three workgroups per CU (three waves per SIMD, 168
+// registers), against 8 waves at two per SIMD with 128-key tiles.
+// Overridable at build time for tuning.
+#ifndef FA_F8_NW
+#define FA_F8_NW 4
+#endif
+#ifndef FA_F8_BN
+#define FA_F8_BN 64
+#endif
+#ifndef FA_F8_WPE
+#define FA_F8_WPE 3
+#endif
+
 template <bool BF16, int D>
 int launch_fp8_t(const Fp8Args& a8, hipStream_t stream) {
-    constexpr int NW = 8, BN = 128, BM = 32 * NW;
+    constexpr int NW = FA_F8_NW, BN = FA_F8_BN, WPE = FA_F8_WPE, BM = 32 * NW;
     const FwdArgs& a = a8.f;
     const int ntiles = (a.seqlen_q + BM - 1) / BM;
     if (ntiles == 0 || a.batch == 0) return 0;
     dim3 grid(a.batch * a.heads, ntiles);
-    hipLaunchKernelGGL((fwd_fp8_kernel<BF16, D, NW, BN>), grid, dim3(64 * NW), 0, stream, a8);
+    hipLaunchKernelGGL((fwd_fp8_kernel<BF16, D, NW, BN, WPE>), grid, dim3(64 * NW), 0, stream, a8);
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
