@@ -19,6 +19,7 @@ namespace {
 constexpr int kVersion = 10000;  // 1.0.0
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+std::atomic<int> g_cus[kMaxDevices];         // compute units, valid once the state is known
 
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
@@ -56,15 +57,20 @@ int check_common(int batch, int heads, int kv_heads, int seqlen_q, int seqlen_k,
     return FA_OK;
 }
 
-int check_arch() {
+// The current device must be a gfx950; *cus (if given) receives its compute
+// unit count.  Both are looked up once per device.
+int check_arch(int* cus = nullptr) {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
         (void)hipGetLastError();
         return FA_ERR_ARCH;
     }
     if (dev < kMaxDevices) {
-        const int st = g_arch_state[dev].load(std::memory_order_relaxed);
-        if (st == 1) return FA_OK;
+        const int st = g_arch_state[dev].load(std::memory_order_acquire);
+        if (st == 1) {
+            if (cus) *cus = g_cus[dev].load(std::memory_order_relaxed);
+            return FA_OK;
+        }
         if (st == 2) return FA_ERR_ARCH;
     }
     hipDeviceProp_t prop;
@@ -74,7 +80,11 @@ int check_arch() {
     }
     const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 &&
                     (prop.gcnArchName[6] == '\0' || prop.gcnArchName[6] == ':');
-    if (dev < kMaxDevices) g_arch_state[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    if (dev < kMaxDevices) {
+        g_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+        g_arch_state[dev].store(ok ? 1 : 2, std::memory_order_release);
+    }
+    if (cus) *cus = prop.multiProcessorCount;
     return ok ? FA_OK : FA_ERR_ARCH;
 }
 
@@ -126,7 +136,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
     if ((has_q && (!q || !o || !lse)) || (has_k && (!k || !v))) return FA_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
         return FA_ERR_INVALID_ARG;
-    rc = check_arch();
+    int cus = 0;
+    rc = check_arch(&cus);
     if (rc != FA_OK) return rc;
     fa::FwdArgs a;
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
@@ -139,6 +150,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
     a.bf16 = dtype == FA_DTYPE_BF16;
     a.drop_t = drop_t; a.drop_scale = drop_scale;
     a.seed_lo = (uint32_t)dropout_seed; a.seed_hi = (uint32_t)(dropout_seed >> 32);
+    a.cus = cus;
     if (fa::launch_fwd(a, (hipStream_t)stream) != 0) return FA_ERR_LAUNCH;
     if (seqused_q && fa::launch_pad_fill(o, lse, seqused_q, batch, seqlen_q, heads, head_dim,
                                          (hipStream_t)stream) != 0)
@@ -165,7 +177,8 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
     if ((has_q && (!q || !o || !lse)) || (has_k && (!k || !v))) return FA_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
         return FA_ERR_INVALID_ARG;
-    rc = check_arch();
+    int cus = 0;
+    rc = check_arch(&cus);
     if (rc != FA_OK) return rc;
     fa::Fp8Args a8;
     fa::FwdArgs& a = a8.f;
@@ -178,6 +191,7 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
     a.scale = sc; a.scale_log2 = log2e_scaled(sc);
     a.bf16 = out_dtype == FA_DTYPE_BF16;
     a.drop_t = 256; a.drop_scale = 1.f; a.seed_lo = 0; a.seed_hi = 0;
+    a.cus = cus;
     a8.v_scale = descale_v;
     if (fa::launch_fwd_fp8(a8, (hipStream_t)stream) != 0) return FA_ERR_LAUNCH;
     if (seqused_q && fa::launch_pad_fill(o, lse, seqused_q, batch, seqlen_q, heads, head_dim,

@@ -1139,14 +1139,16 @@ void bwd_pc_kernel(BwdArgs a) {
 }
 
 // dQ launch shapes (measured on MI355X, bf16 causal): NW waves of 32 query
-// rows, BN-key tiles, WPE waves per SIMD.  Width 128: 8 waves at two per SIMD,
-// 64-key tiles.  Width 64 without dropout: 4 waves at three per SIMD (168
+// rows, BN-key tiles, WPE waves per SIMD.  Width 128: 4 waves at two per SIMD
+// (two workgroups per CU), 64-key tiles: as fast as 8 waves on large grids and
+// faster on small ones, which 8-wave workgroups (one per CU) fill unevenly.
+// Width 64 without dropout: 4 waves at three per SIMD (168
 // registers), 64-key tiles; with dropout that shape spills, so it keeps 8
 // waves at two per SIMD with 128-key tiles.  Width 256: 4 waves at one per
 // SIMD, 32-key tiles (the resident Q, dO and the dQ accumulators take 256
 // registers per lane).  Overridable at build time for tuning.
 #ifndef FA_DQ_NW
-#define FA_DQ_NW 8
+#define FA_DQ_NW 4
 #endif
 #ifndef FA_DQ64_NW
 #define FA_DQ64_NW 4
@@ -1161,7 +1163,7 @@ void bwd_pc_kernel(BwdArgs a) {
 template <int D, bool DROP>
 struct DqShape {
     static constexpr bool kNarrow = D == 64 && !DROP;
-    static constexpr int NW = D > 128 ? 4 : (kNarrow ? FA_DQ64_NW : FA_DQ_NW);
+    static constexpr int NW = D > 128 ? 4 : (kNarrow ? FA_DQ64_NW : (D == 64 ? 8 : FA_DQ_NW));
     static constexpr int BN = D > 128 ? 32 : (kNarrow ? FA_DQ64_BN : (D == 128 ? 64 : 128));
     static constexpr int WPE = D > 128 ? 1 : (kNarrow ? FA_DQ64_WPE : 2);
 };

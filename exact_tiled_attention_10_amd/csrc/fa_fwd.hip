@@ -359,7 +359,10 @@ int launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
 
 // Launch shapes (measured on MI355X, bf16 causal).  d = 128: 8 waves of 32
 // query rows (two waves per SIMD, all state in arch VGPRs) beat 4 waves of 64
-// rows, whose accumulators spill into AGPR traffic; 64-key tiles.  d = 64:
+// rows, whose accumulators spill into AGPR traffic; 64-key tiles.  An 8-wave
+// workgroup fills a CU, so a grid of fewer than four of them per CU ends in
+// a long tail: such grids run 4-wave workgroups of the same kind, two per CU
+// (same results: every query row is computed alike).  d = 64:
 // fewer registers per wave, so 4 waves of 32 rows with three workgroups per
 // CU (three waves per SIMD) and 64-key tiles.  Overridable at build time for
 // tuning.
@@ -397,11 +400,16 @@ int launch_fwd(const FwdArgs& a, hipStream_t stream) {
     if (a.head_dim > 128)
         return a.bf16 ? launch_fwd_t<true, 256, 4, 1, 32, 1>(a, stream)
                       : launch_fwd_t<false, 256, 4, 1, 32, 1>(a, stream);
-    if (a.bf16)
-        return a.head_dim > 64 ? launch_fwd_t<true, 128, NW, QB, B1, W>(a, stream)
-                               : launch_fwd_t<true, 64, NW2, QB, B2, W2>(a, stream);
-    return a.head_dim > 64 ? launch_fwd_t<false, 128, NW, QB, B1, W>(a, stream)
-                           : launch_fwd_t<false, 64, NW2, QB, B2, W2>(a, stream);
+    if (a.head_dim > 64) {
+        const long long wgs = (long long)a.batch * a.heads * ((a.seqlen_q + 32 * NW * QB - 1) / (32 * NW * QB));
+        if (NW == 8 && wgs < 4LL * a.cus)
+            return a.bf16 ? launch_fwd_t<true, 128, 4, QB, B1, W>(a, stream)
+                          : launch_fwd_t<false, 128, 4, QB, B1, W>(a, stream);
+        return a.bf16 ? launch_fwd_t<true, 128, NW, QB, B1, W>(a, stream)
+                      : launch_fwd_t<false, 128, NW, QB, B1, W>(a, stream);
+    }
+    return a.bf16 ? launch_fwd_t<true, 64, NW2, QB, B2, W2>(a, stream)
+                  : launch_fwd_t<false, 64, NW2, QB, B2, W2>(a, stream);
 }
 
 }  // namespace fa

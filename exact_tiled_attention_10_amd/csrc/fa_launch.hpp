@@ -27,6 +27,7 @@ struct FwdArgs {
     uint32_t drop_t;
     float drop_scale;
     uint32_t seed_lo, seed_hi;
+    int cus;  // compute units of the device (launch-shape choice on the host; 0: unknown)
 };
 
 struct Fp8Args {

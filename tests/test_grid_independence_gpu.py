@@ -126,3 +126,27 @@ def test_concurrent_stream(fa):
         torch.cuda.synchronize()
         for n in ("o", "lse", "dq", "dk", "dv"):
             same_bytes(got[n], ref[n], f"concurrent {n}")
+
+
+def test_forward_launch_shape(fa):
+    """At head_dim 128 the forward runs 4-wave workgroups on grids of fewer than
+    four 8-wave workgroups per CU and 8-wave ones otherwise: a sequence alone
+    (32 heads x 4 query tiles of 256 rows: 128 workgroups) and the same
+    sequence inside a batch of 8 (1024 workgroups) take the two shapes, and
+    their bytes must agree."""
+    say("[grid] forward launch shape")
+    cfg = dict(dtype="bf16", heads=32, kv_heads=8, seqlen=1024, head_dim=128, causal=True)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert 32 * 4 < 4 * cus <= 8 * 32 * 4, "the two grids must fall on both sides of the switch"
+    mask = dict(causal=True, window_size=(-1, -1))
+    p1, q1, k1, v1, do1 = dev_problem(11, batch=1, **cfg)
+    p8, q8, k8, v8, do8 = dev_problem(12, batch=8, **cfg)
+    for t8, t1 in ((q8, q1), (k8, k1), (v8, v1), (do8, do1)):
+        t8[5].copy_(t1[0])
+    mask["softmax_scale"] = p1.scale
+    a = run(fa, q1, k1, v1, do1, **mask)
+    b = run(fa, q8, k8, v8, do8, **mask)
+    torch.cuda.synchronize()
+    for n in ("o", "dq", "dk", "dv"):
+        same_bytes(b[n][5], a[n][0], f"launch shape {n}")
+    same_bytes(b["lse"][5], a["lse"][0], "launch shape lse")
