@@ -161,7 +161,7 @@ struct TileDma {
 
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per (batch, query head, BM-row tile); NW waves x 32 rows,
-// two waves per SIMD.  Per key tile and wave:
+// WPE waves per SIMD (launch shapes at launch_dq).  Per key tile and wave:
 //   S^T = K Q^T, dP^T = V dO^T     (A from the K / V tiles, B resident)
 //   P^T = exp2(c S^T - lse2), dS^T = P^T o (dP^T - D)   (one query per lane)
 //   dQ^T += K^T dS^T              (K^T from transposing reads of the K tile)
