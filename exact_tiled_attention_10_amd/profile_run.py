@@ -72,10 +72,8 @@ KERNEL_SOURCES = {
     "decode": ["fa_decode.hip", "fa_device.hpp"],
     "fwd_fp8": ["fa_fwd_fp8.hip", "fa_device.hpp"],
 }
-# Patterns (re.search) for the kernel names in rocprofv3 output.  The forward
-# is either of two kernels (two wave groups alternating matrix and vector
-# phases for head_dim <= 128, the single-group kernel above that).
-KERNEL_NAMES = {"fwd": r"fwd_(pp_)?kernel<", "rowdot": "bwd_rowdot_kernel", "dkdv": "bwd_dkdv_kernel",
+# Patterns (re.search) for the kernel names in rocprofv3 output.
+KERNEL_NAMES = {"fwd": "fwd_kernel<", "rowdot": "bwd_rowdot_kernel", "dkdv": "bwd_dkdv_kernel",
                 "dq": "bwd_dq_kernel", "decode": "decode_split_kernel", "fwd_fp8": "fwd_fp8_kernel"}
 COPY_NAME = "calib_copy_kernel"
 CALIB_LIB = os.path.join(HERE, "libfacalib.so")
