@@ -28,6 +28,7 @@
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Wave w copies 16-byte units [w * per_wave, (w + 1) * per_wave), 16 loads
 // of 1 KiB in flight per step.
@@ -193,6 +194,43 @@ void calib_lds_mfma_kernel(float* __restrict__ sink, uint64_t* __restrict__ cloc
 #pragma unroll
         for (int j = 0; j < 16; ++j) sum += acc[i][j];
     sink[(int64_t)blockIdx.x * 512 + t] = sum;
+    ck.stop(clocks);
+}
+
+// The same with the 16x16x32 MFMA: 4 WPE waves, each `iters` x 32 MFMAs
+// (16384 FLOP each, the FLOP of 16 of the 32x32x16 form) over 8 accumulator
+// chains; MFMA k takes A from LDS read k, issued 4 MFMAs earlier.  A 1 KiB
+// operand then feeds half the work it feeds in the 32x32x16 form.
+template <int WPE>
+__global__ __attribute__((amdgpu_flat_work_group_size(256 * WPE, 256 * WPE), amdgpu_waves_per_eu(WPE, WPE)))
+void calib_lds_mfma16_kernel(float* __restrict__ sink, uint64_t* __restrict__ clocks, int iters) {
+    constexpr int PF = 4;
+    __shared__ __attribute__((aligned(16))) uint32_t lds[16384];
+    ClockPair ck;
+    ck.start();
+    fill_lds(lds);
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    f32x4 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bf16x8 b = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F81u, 0x3F803F80u, 0x3F803F80u});
+    u32x4 ring[PF + 1];
+#pragma unroll
+    for (int p = 0; p < PF; ++p) ring[p] = lds_operand(lds, p, w, lane);
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int s = 0; s < 32; ++s) {
+            ring[(s + PF) % (PF + 1)] = lds_operand(lds, it * 32 + s + PF, w, lane);
+            acc[s % 8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ring[s % (PF + 1)]), b,
+                                                                 acc[s % 8], 0, 0, 0);
+        }
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sum += acc[i][j];
+    sink[(int64_t)blockIdx.x * 1024 + t] = sum;
     ck.stop(clocks);
 }
 
@@ -366,6 +404,22 @@ int fa_calib_lds_mfma(float* sink, uint64_t* clocks, int workgroups, int iters, 
                             : (prefetch == 1 ? calib_lds_mfma_kernel<2, 1>
                                : prefetch == 2 ? calib_lds_mfma_kernel<2, 2>
                                                : calib_lds_mfma_kernel<2, 4>);
+    hipLaunchKernelGGL(k, dim3(workgroups), dim3(256 * waves_per_simd), 0, (hipStream_t)stream, sink, clocks, iters);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// LDS-fed 16x16x32 MFMA calibration: `workgroups` workgroups of 4 x
+// waves_per_simd waves (1..4 per SIMD), each iters x 32 MFMAs with a 1 KiB LDS
+// read per MFMA, 4 ahead.  sink (device) receives workgroups * 1024 floats,
+// clocks as for fa_calib_mfma.  Returns 0 when the launch was accepted, 1 for
+// bad arguments, 2 for a failed launch.
+int fa_calib_lds_mfma16(float* sink, uint64_t* clocks, int workgroups, int iters, int waves_per_simd,
+                        void* stream) {
+    if (!sink || !clocks || workgroups < 1 || iters < 1 || waves_per_simd < 1 || waves_per_simd > 4) return 1;
+    void (*k)(float*, uint64_t*, int) = waves_per_simd == 1   ? calib_lds_mfma16_kernel<1>
+                                        : waves_per_simd == 2 ? calib_lds_mfma16_kernel<2>
+                                        : waves_per_simd == 3 ? calib_lds_mfma16_kernel<3>
+                                                              : calib_lds_mfma16_kernel<4>;
     hipLaunchKernelGGL(k, dim3(workgroups), dim3(256 * waves_per_simd), 0, (hipStream_t)stream, sink, clocks, iters);
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }

@@ -32,7 +32,8 @@ Subcommands (run from anywhere; the repository root is found from this file):
           rate it sustains and the shader clock under that load.
   ldsmfma [--workgroups G] [--iters N]
           Run the LDS-fed matrix-core calibration (every MFMA with a 1 KiB LDS
-          read of its own; 1 and 2 waves per SIMD; reads 1, 2, 4 MFMAs ahead)
+          read of its own; 32x32x16 at 1 and 2 waves per SIMD, reads 1, 2, 4
+          MFMAs ahead; 16x16x32 at 1 to 4 waves per SIMD, reads 4 ahead)
           and print the rate each sustains, as a fraction of the matrix-core
           peak at the clock measured during the run.
   mix     [--workgroups G]
@@ -258,6 +259,8 @@ def _calib_lib():
     P, I = ctypes.c_void_p, ctypes.c_int
     L.fa_calib_lds_mfma.argtypes = [P, P, I, I, I, I, P]
     L.fa_calib_lds_mfma.restype = I
+    L.fa_calib_lds_mfma16.argtypes = [P, P, I, I, I, P]
+    L.fa_calib_lds_mfma16.restype = I
     L.fa_calib_mix.argtypes = [P, P, I, I, I, I, I, P]
     L.fa_calib_mix.restype = I
     return L
@@ -288,6 +291,23 @@ def _ldsmfma(args):
             flops = args.workgroups * 4.0 * wps * args.iters * 16 * 32768
             frac = flops / t / (_SIMDS * _MFMA_FLOP_PER_SIMD_CYCLE * ghz * 1e9)
             print(f"| {wps} | {pf} | {flops / t / 1e12:.0f} | {ghz:.3f} | {frac:.3f} |", flush=True)
+    # the 16x16x32 form: a 1 KiB operand per 16384 FLOP (half the 32x32x16 reuse)
+    sink16 = torch.empty(args.workgroups * 1024, dtype=torch.float32, device=dev)
+    print()
+    print("16x16x32 MFMA, one 1 KiB LDS read each, 4 ahead:")
+    print()
+    print("| waves per SIMD | TFLOP/s | clock (GHz) | fraction of the matrix-core peak at that clock |")
+    print("|---|---|---|---|")
+    for wps in (1, 2, 3, 4):
+        def fn16():
+            rc = L.fa_calib_lds_mfma16(ctypes.c_void_p(sink16.data_ptr()), ctypes.c_void_p(clocks.data_ptr()),
+                                       args.workgroups, args.iters, wps, sp)
+            if rc != 0:
+                raise RuntimeError(f"fa_calib_lds_mfma16 returned {rc}")
+        t, ghz = _calib_timed(fn16, sink16, clocks)
+        flops = args.workgroups * 4.0 * wps * args.iters * 32 * 16384
+        frac = flops / t / (_SIMDS * _MFMA_FLOP_PER_SIMD_CYCLE * ghz * 1e9)
+        print(f"| {wps} | {flops / t / 1e12:.0f} | {ghz:.3f} | {frac:.3f} |", flush=True)
 
 
 _ROLE = {0: "idle", 1: "MFMA (registers)", 2: "MFMA (1 KiB LDS read each)", 3: "FMA chains", 4: "exp2 chains",
