@@ -188,7 +188,7 @@ void bwd_dq_kernel(BwdArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r32 = lane & 31, half = lane >> 5;
     int b, h;
-    xcd_head(blockIdx.x, a.batch, a.heads, a.kv_heads, b, h);
+    xcd_head(rotated_column(), a.batch, a.heads, a.kv_heads, b, h);
     const int ntiles = gridDim.y;
     const int qt = a.causal ? (ntiles - 1 - (int)blockIdx.y) : (int)blockIdx.y;
     const Seq s = seq_of(b, a.cu_q, a.cu_k, a.used_q, a.used_k, a.seqlen_q, a.seqlen_k);
@@ -418,7 +418,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r32 = lane & 31, half = lane >> 5;
     const int g = a.heads / a.kv_heads;
-    const int b = blockIdx.x / a.kv_heads, hk = blockIdx.x % a.kv_heads;
+    const int col = rotated_column();
+    const int b = col / a.kv_heads, hk = col % a.kv_heads;
     const Seq s = seq_of(b, a.cu_q, a.cu_k, a.used_q, a.used_k, a.seqlen_q, a.seqlen_k);
     const int j0 = blockIdx.y * kKvBN;
     if (j0 >= s.len_k) return;
@@ -765,7 +766,8 @@ void bwd_pc_kernel(BwdArgs a) {
     const int kw = wave & 3;  // key block of this wave
     const int r32 = lane & 31, half = lane >> 5;
     const int g = a.heads / a.kv_heads;
-    const int b = blockIdx.x / a.kv_heads, hk = blockIdx.x % a.kv_heads;
+    const int col = rotated_column();
+    const int b = col / a.kv_heads, hk = col % a.kv_heads;
     const Seq s = seq_of(b, a.cu_q, a.cu_k, a.used_q, a.used_k, a.seqlen_q, a.seqlen_k);
     const int j0 = blockIdx.y * kKvBN;
     if (j0 >= s.len_k) return;

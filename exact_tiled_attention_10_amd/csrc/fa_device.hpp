@@ -312,6 +312,23 @@ __device__ __forceinline__ bool keep_byte(uint32_t w, int e, uint32_t thresh) {
 #ifndef FA_XCD_GROUPS
 #define FA_XCD_GROUPS 1
 #endif
+// Column of this workgroup in a grid (columns, rows[, z]) dispatched row after
+// row.  The GPU hands workgroup i to XCD i % 8 and, inside the XCD, to its four
+// shader engines in a fixed rotation by i / 8 (read back from the hardware id
+// register).  When 8 divides the column count n and n / 8 is even, a column's
+// engine slot repeats every row or every other row: with 32 columns, columns
+// 8 s .. 8 s + 7 land in slot s on every row, and when some columns have no
+// work (the shorter sequences of a packed batch, past their end) the same
+// engines idle row after row while the others queue the real workgroups.
+// Shifting the columns by 8 per row then moves each column one slot further
+// per row and keeps it on its XCD (its L2 keeps serving it).  For other n the
+// slot already advances with the row, and the columns are left in place.
+__device__ __forceinline__ int rotated_column() {
+    const unsigned n = gridDim.x;
+    const unsigned shift = (n % 8u == 0u && (n / 8u) % 2u == 0u) ? 8u : 0u;
+    return (int)((blockIdx.x + shift * blockIdx.y) % n);
+}
+
 // (batch, query head) of workgroup column x in a grid over batch * heads.
 // The GPU hands workgroups to its 8 XCDs (each with its own L2) in turn, so
 // columns x and x + 8 run on the same XCD.  When the g = heads / kv_heads

@@ -87,7 +87,7 @@ void fwd_kernel(FwdArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches below
     const int r32 = lane & 31, half = lane >> 5;
     int b, h;
-    xcd_head(blockIdx.x, a.batch, a.heads, a.kv_heads, b, h);
+    xcd_head(rotated_column(), a.batch, a.heads, a.kv_heads, b, h);
     const int ntiles = gridDim.y;
     const int qt = a.causal ? (ntiles - 1 - (int)blockIdx.y) : (int)blockIdx.y;
     const Seq s = seq_of(b, a.cu_q, a.cu_k, a.used_q, a.used_k, a.seqlen_q, a.seqlen_k);
